@@ -1,0 +1,340 @@
+"""Pins of the CPU oracle against facts other than itself (no GPU needed).
+
+Each test fixes the oracle to something independent: exact brute force in
+rational arithmetic, closed forms (all-ones scales, rank one, Hadamard
+factors), symmetries, format facts, and numbers the pages print.  Shapes are
+non-square with distinct rank so that a transposed operand or a scale on the
+wrong side changes the shape or the result.
+"""
+import itertools
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+# dyadic values exactly representable in fp16 and bf16
+DYADIC = [0.25, 0.5, 0.75, 1.0, 1.25, 1.5, 2.0, 3.0, -0.5, -1.0, -2.0, 0.375]
+
+
+def f16bits(vals):
+    return np.asarray(vals, dtype=np.float16).view(np.uint16)
+
+
+def bf16bits(vals):
+    v = np.asarray(vals, dtype=np.float32).view(np.uint32)
+    assert np.all((v & 0xFFFF) == 0), "test values must be exact in bf16"
+    return (v >> 16).astype(np.uint16)
+
+
+def random_path(rng, m, n, r, scale_pool=DYADIC):
+    U = rng.choice([-1, 1], size=(m, r)).astype(np.int8)
+    V = rng.choice([-1, 1], size=(n, r)).astype(np.int8)
+    return dict(rank=r, u_words=oracle.pack_signs(U), v_words=oracle.pack_signs(V),
+                h=f16bits(rng.choice(scale_pool, m)), g=f16bits(rng.choice(scale_pool, n)),
+                l=f16bits(rng.choice(scale_pool, r)), _U=U, _V=V)
+
+
+# ----------------------------------------------------------------------------
+# storage formats
+# ----------------------------------------------------------------------------
+
+def test_decode_formats_known_values():
+    # IEEE binary16 and bfloat16 encodings of textbook values
+    assert oracle.decode_fp16(np.array([0x3C00, 0xC000, 0x0001, 0x7BFF, 0x3555], np.uint16)).tolist() == \
+        [1.0, -2.0, 2.0 ** -24, 65504.0, 0.333251953125]
+    assert oracle.decode_bf16(np.array([0x3F80, 0xC000, 0x3F81, 0x0080, 0x4049], np.uint16)).tolist() == \
+        [1.0, -2.0, 1.0078125, 2.0 ** -126, 3.140625]
+
+
+def test_pack_golden_words():
+    """Words derived by hand from the format: bit j%32 of word j//32 set iff -1."""
+    cases = [
+        ([[-1, 1, 1]], [[0x00000001]]),
+        ([[(-1 if j % 2 == 0 else 1) for j in range(32)]], [[0x55555555]]),
+        ([[-1] * 40], [[0xFFFFFFFF, 0x000000FF]]),
+        ([[1] * 33], [[0, 0]]),
+        ([[1] * 31 + [-1]], [[0x80000000]]),
+        ([[1] * 32 + [-1]], [[0, 1]]),
+        ([[-1], [1], [-1]], [[1], [0], [1]]),
+    ]
+    for signs, words in cases:
+        got = oracle.pack_signs(np.array(signs, np.int8))
+        assert got.dtype == np.uint32
+        assert got.tolist() == words, (signs, got)
+        back = oracle.unpack_signs(np.array(words, np.uint32), len(signs), len(signs[0]))
+        assert back.tolist() == signs
+
+
+@pytest.mark.parametrize("rows,rank", [(1, 1), (7, 31), (5, 32), (9, 33), (3, 64), (4, 65), (6, 319)])
+def test_pack_unpack_roundtrip(rows, rank):
+    s = synth.int8_signs((77, rows, rank), rows, rank)
+    w = oracle.pack_signs(s)
+    assert w.shape == (rows, (rank + 31) // 32)
+    assert np.array_equal(oracle.unpack_signs(w, rows, rank), s)
+    # generator words (padding zero) unpack to +-1 and repack identically
+    words = synth.sign_words((78, rows, rank), rows, rank)
+    u = oracle.unpack_signs(words, rows, rank)
+    oracle.check_sign_factor(u)
+    assert np.array_equal(oracle.pack_signs(u), words)
+
+
+def test_pack_rejects_non_sign_and_unpack_rejects_padding():
+    with pytest.raises(ValueError):
+        oracle.pack_signs(np.array([[1, 0, -1]], np.int8))
+    with pytest.raises(ValueError):
+        oracle.pack_signs(np.array([[2]], np.int8))
+    with pytest.raises(ValueError):
+        oracle.unpack_signs(np.array([[1 << 5]], np.uint32), 1, 5)   # bit 5 is padding for rank 5
+    with pytest.raises(AssertionError):
+        oracle.check_sign_factor(np.array([[1, 0]]))
+
+
+# ----------------------------------------------------------------------------
+# the forward pass
+# ----------------------------------------------------------------------------
+
+def brute_force(x, paths, m, n):
+    """y[t][i] = sum_p sum_k sum_j x[t][j] g[j] V[j][k] l[k] U[i][k] h[i], in Fractions."""
+    T = len(x)
+    y = [[Fraction(0)] * m for _ in range(T)]
+    for p in paths:
+        U, V = p["_U"], p["_V"]
+        h = [Fraction(float(v)) for v in p["h"].view(np.float16)]
+        g = [Fraction(float(v)) for v in p["g"].view(np.float16)]
+        l = [Fraction(float(v)) for v in p["l"].view(np.float16)]
+        for t in range(T):
+            for i in range(m):
+                acc = Fraction(0)
+                for k in range(p["rank"]):
+                    for j in range(n):
+                        acc += Fraction(float(x[t][j])) * g[j] * int(V[j][k]) * l[k] * int(U[i][k]) * h[i]
+                y[t][i] += acc
+    return y
+
+
+def test_brute_force_exact_tiny():
+    rng = np.random.default_rng(1234)
+    checked = 0
+    for m, n in itertools.product(range(1, 7), range(1, 7)):
+        for npaths in (1, 2):
+            r = int(rng.integers(1, 4))
+            T = int(rng.integers(1, 3))
+            paths = [random_path(rng, m, n, r) for _ in range(npaths)]
+            xv = rng.choice(DYADIC, size=(T, n))
+            x = oracle.decode_bf16(bf16bits(xv))
+            y = oracle.forward(x, paths, m, n)
+            yb = brute_force(xv, paths, m, n)
+            assert y.shape == (T, m)
+            for t in range(T):
+                for i in range(m):
+                    assert Fraction(float(y[t, i])) == yb[t][i], (m, n, r, T)
+            checked += 1
+    assert checked == 72
+
+
+def test_associativity_factored_equals_explicit():
+    rng = np.random.default_rng(7)
+    for (m, n, r, T) in [(96, 160, 13, 3), (257, 130, 40, 5), (64, 512, 33, 1)]:
+        paths = []
+        for p in range(2):
+            paths.append(dict(rank=r, u_words=synth.sign_words((5, m, n, p, 0), m, r),
+                              v_words=synth.sign_words((5, m, n, p, 1), n, r),
+                              h=synth.scales_fp16_bits((5, m, p, 2), m),
+                              g=synth.scales_fp16_bits((5, n, p, 3), n),
+                              l=synth.scales_fp16_bits((5, r, p, 4), r)))
+        x = oracle.decode_bf16(synth.activations((5, T, n), T, n))
+        y1 = oracle.forward(x, paths, m, n)
+        y2 = oracle.forward_factored(x, paths, m, n)
+        rms = np.sqrt(np.mean(y1 ** 2))
+        assert np.max(np.abs(y1 - y2)) <= 1e-12 * rms
+
+
+def test_all_ones_scales_reduce_to_sign_product():
+    """h = g = l = 1: W = sum_p U_p V_p^T, an integer matrix; integer x gives integer y."""
+    rng = np.random.default_rng(3)
+    m, n, r = 37, 53, 11
+    ones = lambda k: f16bits(np.ones(k))
+    paths, S = [], np.zeros((m, n), np.int64)
+    for _ in range(2):
+        U = rng.choice([-1, 1], size=(m, r)).astype(np.int8)
+        V = rng.choice([-1, 1], size=(n, r)).astype(np.int8)
+        S += U.astype(np.int64) @ V.astype(np.int64).T
+        paths.append(dict(rank=r, u_words=oracle.pack_signs(U), v_words=oracle.pack_signs(V),
+                          h=ones(m), g=ones(n), l=ones(r)))
+    W = oracle.reconstruct_w(paths, m, n)
+    assert np.array_equal(W, S.astype(np.float64))
+    xi = rng.integers(-3, 4, size=(4, n))
+    y = oracle.forward(xi.astype(np.float64), paths, m, n)
+    assert np.array_equal(y, (xi @ S.T).astype(np.float64))
+
+
+def test_rank_one_all_plus_closed_form():
+    """U = V = +1, r = 1: y_t = sum_p h_p * l_p * (x_t . g_p)."""
+    rng = np.random.default_rng(4)
+    m, n, T = 7, 19, 3
+    paths, expect = [], np.zeros((T, m))
+    x = oracle.decode_bf16(bf16bits(rng.choice(DYADIC, size=(T, n))))
+    for _ in range(2):
+        h, g, l = rng.choice(DYADIC, m), rng.choice(DYADIC, n), rng.choice(DYADIC, 1)
+        paths.append(dict(rank=1, u_words=np.zeros((m, 1), np.uint32),
+                          v_words=np.zeros((n, 1), np.uint32), h=f16bits(h), g=f16bits(g), l=f16bits(l)))
+        expect += np.outer(x @ g, h) * l[0]
+    assert np.array_equal(oracle.forward(x, paths, m, n), expect)
+
+
+def sylvester(k):
+    H = np.array([[1]], np.int64)
+    for _ in range(k):
+        H = np.block([[H, H], [H, -H]])
+    return H
+
+
+def test_hadamard_closed_form():
+    """V = first r columns of a Sylvester Hadamard H_n, g = 1, x = column j of H_n:
+    z = x V = n e_j (H^T H = n I), so y = n * l_j * (U[:, j] o h)."""
+    rng = np.random.default_rng(5)
+    n, r, m = 32, 12, 9
+    H = sylvester(5)
+    assert np.array_equal(H.T @ H, n * np.eye(n, dtype=np.int64))
+    U = rng.choice([-1, 1], size=(m, r)).astype(np.int8)
+    h, l = rng.choice(DYADIC, m), rng.choice(DYADIC, r)
+    path = dict(rank=r, u_words=oracle.pack_signs(U), v_words=oracle.pack_signs(H[:, :r].astype(np.int8)),
+                h=f16bits(h), g=f16bits(np.ones(n)), l=f16bits(l))
+    # second path with zero row scale must not change anything
+    dead = dict(path, h=f16bits(np.zeros(m)), l=f16bits(rng.choice(DYADIC, r)))
+    js = [0, 3, 11]
+    x = H[:, js].T.astype(np.float64)
+    y = oracle.forward(x, [path, dead], m, n)
+    for row, j in enumerate(js):
+        assert np.array_equal(y[row], n * l[j] * U[:, j] * h)
+
+
+def test_latent_symmetries_are_exact():
+    rng = np.random.default_rng(6)
+    m, n, r = 11, 23, 7
+    p = random_path(rng, m, n, r)
+    x = oracle.decode_bf16(bf16bits(rng.choice(DYADIC, size=(3, n))))
+    y = oracle.forward(x, [p], m, n)
+    # negate latent column k in both U and V
+    U, V = p["_U"].copy(), p["_V"].copy()
+    U[:, 2] *= -1
+    V[:, 2] *= -1
+    q = dict(p, u_words=oracle.pack_signs(U), v_words=oracle.pack_signs(V))
+    assert np.array_equal(oracle.forward(x, [q], m, n), y)
+    # permute latent indices consistently in U, V and l
+    perm = rng.permutation(r)
+    q = dict(p, u_words=oracle.pack_signs(p["_U"][:, perm]), v_words=oracle.pack_signs(p["_V"][:, perm]),
+             l=p["l"][perm])
+    assert np.array_equal(oracle.forward(x, [q], m, n), y)
+    # flipping only U's column changes the result (the pin is not vacuous)
+    q = dict(p, u_words=oracle.pack_signs(U))
+    assert not np.array_equal(oracle.forward(x, [q], m, n), y)
+
+
+def test_path_additivity_and_linearity():
+    rng = np.random.default_rng(8)
+    m, n, r = 13, 29, 5
+    p1, p2 = random_path(rng, m, n, r), random_path(rng, m, n, 3)
+    x1 = oracle.decode_bf16(bf16bits(rng.choice(DYADIC, size=(2, n))))
+    x2 = oracle.decode_bf16(bf16bits(rng.choice(DYADIC, size=(2, n))))
+    y12 = oracle.forward(x1, [p1, p2], m, n)
+    assert np.array_equal(y12, oracle.forward(x1, [p1], m, n) + oracle.forward(x1, [p2], m, n))
+    ylin = oracle.forward(2 * x1 - 0.5 * x2, [p1, p2], m, n)
+    assert np.array_equal(ylin, 2 * y12 - 0.5 * oracle.forward(x2, [p1, p2], m, n))
+
+
+def test_input_channel_scale_is_g_and_output_scale_is_h():
+    """One-hot input channel j picks column j of W: y = W[:, j] (g on inputs, h on outputs)."""
+    rng = np.random.default_rng(9)
+    m, n, r = 5, 8, 3
+    p = random_path(rng, m, n, r)
+    W = oracle.reconstruct_w([p], m, n)
+    h = oracle.decode_fp16(p["h"])
+    g = oracle.decode_fp16(p["g"])
+    l = oracle.decode_fp16(p["l"])
+    for j in range(n):
+        x = np.zeros((1, n))
+        x[0, j] = 1.0
+        y = oracle.forward(x, [p], m, n)[0]
+        col = np.array([h[i] * sum(int(p["_U"][i, k]) * l[k] * int(p["_V"][j, k]) for k in range(r)) * g[j]
+                        for i in range(m)])
+        assert np.array_equal(y, col)
+        assert np.array_equal(W[:, j], col)
+
+
+def test_forward_rejects_bad_shapes_and_scales():
+    rng = np.random.default_rng(10)
+    p = random_path(rng, 4, 6, 2)
+    with pytest.raises(ValueError):
+        oracle.forward(np.zeros((1, 5)), [p], 4, 6)
+    with pytest.raises(ValueError):
+        oracle.forward(np.zeros((1, 6)), [dict(p, l=f16bits([1.0]))], 4, 6)
+    with pytest.raises(ValueError):
+        oracle.forward(np.zeros((1, 6)), [dict(p, h=f16bits([np.inf, 1, 1, 1]))], 4, 6)
+
+
+# ----------------------------------------------------------------------------
+# bit budget and the pages' storage numbers
+# ----------------------------------------------------------------------------
+
+def rank_brute(m, n, bpw):
+    q = Fraction(bpw) * m * n / (2 * (m + n))
+    best = None
+    for r in range(0, int(q) + 3):
+        d = abs(Fraction(r) - q)
+        if best is None or d < best[0] or (d == best[0] and r > best[1]):
+            best = (d, r)
+    return best[1]
+
+
+def test_rank_rule_matches_nearest_integer_search():
+    for wl in synth.WORKLOADS.values():
+        if wl.bpw is None:
+            continue
+        for s in wl.mats:
+            r = oracle.rank_for_bpw(s.m, s.n, wl.bpw, s.rank_mult)
+            assert r == rank_brute(s.m, s.n, wl.bpw) * s.rank_mult
+            assert r >= 1
+    # exact tie rounds up: m = n = 10, BPW = 1 gives 100 / 40 = 2.5 -> 3
+    assert oracle.rank_for_bpw(10, 10, Fraction(1)) == 3
+    assert rank_brute(10, 10, Fraction(1)) == 3
+    assert oracle.rank_for_bpw(4096, 4096, Fraction(1, 10)) == 102
+
+
+def test_sign_bits_per_weight_spends_the_budget():
+    for wl in synth.WORKLOADS.values():
+        if wl.bpw is None:
+            continue
+        for s in wl.mats:
+            r = oracle.rank_for_bpw(s.m, s.n, wl.bpw, 1)
+            got = oracle.sign_bits_per_weight(s.m, s.n, [r, r])
+            # within one rank step of the budget
+            assert abs(got - wl.bpw) <= Fraction(s.m + s.n, s.m * s.n)
+
+
+def _llama_total_bytes(d, ffn, kv, layers, bpw, vocab=32000):
+    """Linears at ``bpw`` (two paths, sign bits + fp16 scales) + fp16 embeddings, head and norms."""
+    mats = [(d, d), (kv, d), (kv, d), (d, d), (ffn, d), (ffn, d), (d, ffn)]
+    lin = sum(oracle.linear_storage_bytes(m, n, [oracle.rank_for_bpw(m, n, bpw)] * 2) for m, n in mats)
+    fp16_rest = 2 * (2 * vocab * d + (2 * layers + 1) * d)
+    params = layers * (sum(m * n for m, n in mats) + 2 * d) + 2 * vocab * d + d
+    return float(lin * layers + fp16_rest), params
+
+
+def test_pages_storage_numbers():
+    gold = {k: v["value"] for k, v in json.load(open(os.path.join(GOLDEN, "pages_storage.json"))).items()
+            if not k.startswith("_")}
+    b13, p13 = _llama_total_bytes(5120, 13824, 5120, 40, Fraction(1, 10))
+    assert b13 / 1e9 < gold["llama2_13b_0p1bpw_max_gb"]
+    assert round(2 * p13 / b13) == gold["llama2_13b_reduction_x"]
+    b70, p70 = _llama_total_bytes(8192, 28672, 1024, 80, Fraction(1, 10))
+    assert abs(2 * p70 / 1e9 - gold["llama2_70b_fp16_gb"]) / gold["llama2_70b_fp16_gb"] < 2e-3
+    assert b70 / 1e9 < gold["llama2_70b_0p1bpw_max_gb"]
+    assert Fraction(16) / Fraction(1, 10) == gold["bpw_0p1_vs_fp16_x"]
