@@ -1,0 +1,677 @@
+// Host side of the C ABI declared in include/littlebit.h: validation, device
+// memory ownership, layer build, regime dispatch, stacks and HIP graphs.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "lb_internal.h"
+#include "lb_prefill.h"
+
+using namespace lb;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+lb_status fail(lb_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+lb_status hip_fail(hipError_t e, const char* what) {
+  return fail(e == hipErrorOutOfMemory ? LB_ERR_OUT_OF_MEMORY : LB_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIP_TRY(expr)                                     \
+  do {                                                    \
+    hipError_t e_ = (expr);                               \
+    if (e_ != hipSuccess) return hip_fail(e_, #expr);     \
+  } while (0)
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline int64_t words_per_row(int64_t r) { return r <= 0 ? 0 : (r + 31) / 32; }
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// One device allocation carved into 256-byte aligned pieces.
+struct Arena {
+  char* base = nullptr;
+  size_t size = 0;
+  size_t used = 0;
+  void* take(size_t bytes) {
+    void* p = base + used;
+    used += align256(bytes);
+    return p;
+  }
+};
+
+// Device scratch that grows on demand (callers synchronise before reuse).
+struct Scratch {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+  hipError_t ensure(size_t want) {
+    if (want <= bytes) return hipSuccess;
+    if (ptr) {
+      hipError_t e = hipFree(ptr);
+      if (e != hipSuccess) return e;
+      ptr = nullptr;
+      bytes = 0;
+    }
+    hipError_t e = hipMalloc(&ptr, want);
+    if (e == hipSuccess) bytes = want;
+    return e;
+  }
+  void release() {
+    if (ptr) (void)hipFree(ptr);
+    ptr = nullptr;
+    bytes = 0;
+  }
+};
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// objects
+// ---------------------------------------------------------------------------
+
+// Decode launch plan: entries, work items and control words for a given token
+// count.  Owned by a linear (single forwards) or a stack.
+struct DecodePlan {
+  int T = -1;             // tokens per launch this plan was built for
+  int tb = 0;
+  std::vector<DecEntry> entries_h;
+  std::vector<WorkItem> items_h;
+  DecEntry* entries_d = nullptr;
+  WorkItem* items_d = nullptr;
+  unsigned int* counters_d = nullptr;  // [count]
+  unsigned int* ready_d = nullptr;     // [count]
+  Control* ctl_d = nullptr;
+  Scratch zbuf;
+  size_t cap_entries = 0, cap_items = 0;
+  void release() {
+    if (entries_d) (void)hipFree(entries_d);
+    if (items_d) (void)hipFree(items_d);
+    if (counters_d) (void)hipFree(counters_d);
+    if (ready_d) (void)hipFree(ready_d);
+    if (ctl_d) (void)hipFree(ctl_d);
+    entries_d = nullptr; items_d = nullptr; counters_d = nullptr; ready_d = nullptr; ctl_d = nullptr;
+    zbuf.release();
+    cap_entries = cap_items = 0;
+    T = -1;
+  }
+};
+
+struct lb_linear_s {
+  int device = 0;
+  int64_t m = 0, n = 0;
+  int np = 0;
+  int64_t r[2] = {0, 0};
+  Arena arena;
+  PathDev paths[2] = {};
+  uint32_t* udec = nullptr;
+  int uw = 0;
+  PrefillLayer pre = {};
+  // single-forward state
+  Scratch zexact;
+  DecodePlan plan;
+  PrefillPlan pplan;
+  hipStream_t last_stream = nullptr;
+};
+
+struct lb_stack_s {
+  int device = 0;
+  std::vector<lb_linear> linears;
+  std::vector<const PrefillLayer*> pre;
+  DecodePlan plan;
+  PrefillPlan pplan;
+  Scratch zexact;
+  // device copies of the caller's pointer arrays
+  const void** xs_d = nullptr;
+  void** ys_d = nullptr;
+  std::vector<const void*> xs_h;
+  std::vector<void*> ys_h;
+  // captured graph and what it was captured for
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  hipStream_t cap_stream = nullptr;
+  int64_t g_tokens = -1;
+  int g_io = -1, g_regime = -1;
+  hipStream_t last_stream = nullptr;
+};
+
+namespace {
+
+void linear_free(lb_linear L) {
+  if (!L) return;
+  if (L->arena.base) (void)hipFree(L->arena.base);
+  L->zexact.release();
+  L->plan.release();
+  prefill_plan_release(L->pplan);
+  delete L;
+}
+
+// ---------------------------------------------------------------------------
+// decode plans
+// ---------------------------------------------------------------------------
+
+// Builds (or reuses) the work list for `count` linears at `T` tokens per launch.
+lb_status build_decode_plan(DecodePlan& P, const lb_linear* L, int count, int T) {
+  if (P.T == T && (int)P.entries_h.size() == count) return LB_OK;
+  const int tb = (T + 7) / 8;
+  const int ctm = decode_ct_max(tb);
+  P.entries_h.assign(count, DecEntry{});
+  std::vector<std::pair<int64_t, WorkItem>> vitems;
+  std::vector<int64_t> entry_weight(count, 0);
+  size_t zoff = 0;
+  std::vector<size_t> zoffs(count);
+  for (int e = 0; e < count; ++e) {
+    const lb_linear l = L[e];
+    DecEntry& E = P.entries_h[e];
+    E.m = (int)l->m;
+    E.n = (int)l->n;
+    E.np = l->np;
+    E.nkc = (int)((l->n + kChunk - 1) / kChunk);
+    E.nrt = (int)((l->m + kTile - 1) / kTile);
+    E.udec = l->udec;
+    E.uw = l->uw;
+    int rmax = 0, woff = 0, nv = 0;
+    for (int p = 0; p < l->np; ++p) {
+      E.p[p] = l->paths[p];
+      E.woff[p] = woff;
+      woff += l->paths[p].W;
+      rmax = std::max(rmax, l->paths[p].r);
+      const int nct = l->paths[p].nct;
+      const int groups = (nct + ctm - 1) / ctm;
+      const int per = (nct + groups - 1) / groups;
+      E.vct[p] = per;
+      for (int g = 0; g < groups; ++g) {
+        const int cnt = std::min(per, nct - g * per);
+        WorkItem w{(uint32_t)e, (uint16_t)p, (uint16_t)g};
+        const int64_t bytes = (int64_t)E.nkc * cnt;
+        vitems.push_back({bytes, w});
+        entry_weight[e] = std::max(entry_weight[e], bytes);
+        ++nv;
+      }
+    }
+    E.nv = nv;
+    E.rpad = ((rmax + 15) / 16) * 16;
+    zoffs[e] = zoff;
+    zoff += (size_t)E.np * T * E.rpad;
+  }
+  // V items first, longest first; then U items grouped by entry in the same order
+  std::stable_sort(vitems.begin(), vitems.end(),
+                   [](const std::pair<int64_t, WorkItem>& a, const std::pair<int64_t, WorkItem>& b) { return a.first > b.first; });
+  std::vector<int> order(count);
+  for (int e = 0; e < count; ++e) order[e] = e;
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return entry_weight[a] > entry_weight[b]; });
+  P.items_h.clear();
+  for (auto& v : vitems) P.items_h.push_back(v.second);
+  for (int e : order) {
+    const int nrg = (P.entries_h[e].nrt + kDecodeRowTilesPerItem - 1) / kDecodeRowTilesPerItem;
+    for (int g = 0; g < nrg; ++g) P.items_h.push_back(WorkItem{(uint32_t)e, (uint16_t)0x8000u, (uint16_t)g});
+  }
+  // device buffers
+  HIP_TRY(P.zbuf.ensure(std::max<size_t>(zoff, 1) * sizeof(float)));
+  for (int e = 0; e < count; ++e) P.entries_h[e].zbuf = reinterpret_cast<float*>(P.zbuf.ptr) + zoffs[e];
+  if ((size_t)count > P.cap_entries) {
+    if (P.entries_d) HIP_TRY(hipFree(P.entries_d));
+    if (P.counters_d) HIP_TRY(hipFree(P.counters_d));
+    if (P.ready_d) HIP_TRY(hipFree(P.ready_d));
+    P.entries_d = nullptr; P.counters_d = nullptr; P.ready_d = nullptr;
+    HIP_TRY(hipMalloc(&P.entries_d, count * sizeof(DecEntry)));
+    HIP_TRY(hipMalloc(&P.counters_d, count * sizeof(unsigned int)));
+    HIP_TRY(hipMalloc(&P.ready_d, count * sizeof(unsigned int)));
+    P.cap_entries = count;
+  }
+  if (P.items_h.size() > P.cap_items) {
+    if (P.items_d) HIP_TRY(hipFree(P.items_d));
+    P.items_d = nullptr;
+    HIP_TRY(hipMalloc(&P.items_d, P.items_h.size() * sizeof(WorkItem)));
+    P.cap_items = P.items_h.size();
+  }
+  if (!P.ctl_d) HIP_TRY(hipMalloc(&P.ctl_d, sizeof(Control)));
+  // fresh control state: counters, flags and queue start at zero
+  HIP_TRY(hipMemset(P.counters_d, 0, count * sizeof(unsigned int)));
+  HIP_TRY(hipMemset(P.ready_d, 0, count * sizeof(unsigned int)));
+  HIP_TRY(hipMemset(P.ctl_d, 0, sizeof(Control)));
+  HIP_TRY(hipMemcpy(P.entries_d, P.entries_h.data(), count * sizeof(DecEntry), hipMemcpyHostToDevice));
+  HIP_TRY(hipMemcpy(P.items_d, P.items_h.data(), P.items_h.size() * sizeof(WorkItem), hipMemcpyHostToDevice));
+  P.T = T;
+  P.tb = tb;
+  return LB_OK;
+}
+
+// Launches the decode kernel over token slices of at most kDecodeMaxTokens.
+lb_status run_decode(DecodePlan& P, const lb_linear* L, int count, const void* const* xs_d, void* const* ys_d,
+                     const void* x0, void* y0, int64_t tokens, hipStream_t st) {
+  const int64_t full = std::min<int64_t>(tokens, kDecodeMaxTokens);
+  for (int64_t t0 = 0; t0 < tokens; t0 += kDecodeMaxTokens) {
+    const int T = (int)std::min<int64_t>(kDecodeMaxTokens, tokens - t0);
+    (void)full;
+    if (P.T != T && P.T != -1) HIP_TRY(hipStreamSynchronize(st));  // the plan is rewritten below
+    lb_status s = build_decode_plan(P, L, count, T);
+    if (s != LB_OK) return s;
+    DecArgs a{};
+    a.entries = P.entries_d;
+    a.xs = xs_d;
+    a.ys = ys_d;
+    a.x0 = x0;
+    a.y0 = y0;
+    a.items = P.items_d;
+    a.counters = P.counters_d;
+    a.ready = P.ready_d;
+    a.ctl = P.ctl_d;
+    a.nitems = (int)P.items_h.size();
+    a.T = T;
+    a.t0 = (int)t0;
+    a.spin_limit = 1 << 21;
+    HIP_TRY(launch_decode(a, P.tb, st));
+  }
+  return LB_OK;
+}
+
+lb_status check_io(int64_t tokens, lb_dtype io, lb_regime regime) {
+  if (tokens <= 0) return fail(LB_ERR_INVALID_ARGUMENT, "tokens must be positive (got %lld)", (long long)tokens);
+  if (tokens > LB_MAX_TOKENS) return fail(LB_ERR_UNSUPPORTED, "tokens %lld exceeds %d", (long long)tokens, LB_MAX_TOKENS);
+  if (io != LB_BF16 && io != LB_FP32) return fail(LB_ERR_INVALID_ARGUMENT, "io must be LB_BF16 or LB_FP32");
+  if (regime < LB_REGIME_AUTO || regime > LB_REGIME_PREFILL) return fail(LB_ERR_INVALID_ARGUMENT, "unknown regime");
+  if (io == LB_FP32 && (regime == LB_REGIME_DECODE || regime == LB_REGIME_PREFILL))
+    return fail(LB_ERR_UNSUPPORTED, "the decode and prefill kernels take bf16 I/O; fp32 I/O runs the exact kernels");
+  return LB_OK;
+}
+
+lb_regime pick_regime(int64_t tokens, lb_dtype io, lb_regime regime) {
+  if (regime != LB_REGIME_AUTO) return regime;
+  if (io == LB_FP32) return LB_REGIME_EXACT;
+  return tokens < LB_PREFILL_MIN_TOKENS ? LB_REGIME_DECODE : LB_REGIME_PREFILL;
+}
+
+int current_device() {
+  int d = 0;
+  (void)hipGetDevice(&d);
+  return d;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// ABI
+// ---------------------------------------------------------------------------
+extern "C" {
+
+const char* lb_status_string(lb_status s) {
+  switch (s) {
+    case LB_OK: return "ok";
+    case LB_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case LB_ERR_INVALID_SIGN: return "sign value outside {-1, +1}";
+    case LB_ERR_ALIGNMENT: return "pointer not 16-byte aligned";
+    case LB_ERR_UNSUPPORTED: return "unsupported size";
+    case LB_ERR_OUT_OF_MEMORY: return "out of device memory";
+    case LB_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* lb_last_error(void) { return g_last_error.c_str(); }
+
+int64_t lb_packed_words_per_row(int64_t rank) { return words_per_row(rank); }
+
+int64_t lb_rank_for_bpw(int64_t d_out, int64_t d_in, int64_t bpw_num, int64_t bpw_den) {
+  if (d_out <= 0 || d_in <= 0 || bpw_num <= 0 || bpw_den <= 0) return -1;
+  // round(num * m * n / (2 den (m + n))), ties up: floor((2 A + B) / (2 B))
+  const __int128 A = (__int128)bpw_num * d_out * d_in;
+  const __int128 B = (__int128)2 * bpw_den * (d_out + d_in);
+  return (int64_t)((2 * A + B) / (2 * B));
+}
+
+lb_status lb_pack_signs_host(const int8_t* signs, int64_t rows, int64_t rank, uint32_t* packed) {
+  if (!signs || !packed) return fail(LB_ERR_INVALID_ARGUMENT, "null pointer");
+  if (rows <= 0 || rank <= 0) return fail(LB_ERR_INVALID_ARGUMENT, "rows and rank must be positive");
+  const int64_t W = words_per_row(rank);
+  for (int64_t i = 0; i < rows * rank; ++i)
+    if (signs[i] != 1 && signs[i] != -1)
+      return fail(LB_ERR_INVALID_SIGN, "value %d at row %lld, column %lld", (int)signs[i], (long long)(i / rank),
+                  (long long)(i % rank));
+  for (int64_t i = 0; i < rows; ++i)
+    for (int64_t w = 0; w < W; ++w) {
+      uint32_t word = 0;
+      for (int b = 0; b < 32; ++b) {
+        const int64_t j = 32 * w + b;
+        if (j < rank && signs[i * rank + j] == -1) word |= 1u << b;
+      }
+      packed[i * W + w] = word;
+    }
+  return LB_OK;
+}
+
+lb_status lb_pack_signs(const int8_t* signs, int64_t rows, int64_t rank, uint32_t* packed, void* stream) {
+  if (!signs || !packed) return fail(LB_ERR_INVALID_ARGUMENT, "null pointer");
+  if (rows <= 0 || rank <= 0) return fail(LB_ERR_INVALID_ARGUMENT, "rows and rank must be positive");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  int* flag = nullptr;
+  HIP_TRY(hipMalloc(&flag, sizeof(int)));
+  int bad = 0;
+  hipError_t e = hipMemsetAsync(flag, 0, sizeof(int), st);
+  if (e == hipSuccess) e = launch_validate_signs(signs, rows * rank, flag, st);
+  if (e == hipSuccess) e = hipMemcpyAsync(&bad, flag, sizeof(int), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e == hipSuccess && !bad) e = launch_pack_signs(signs, rows, rank, packed, st);
+  (void)hipFree(flag);
+  if (e != hipSuccess) return hip_fail(e, "lb_pack_signs");
+  if (bad) return fail(LB_ERR_INVALID_SIGN, "a sign value is not -1 or +1");
+  return LB_OK;
+}
+
+lb_status lb_unpack_signs(const uint32_t* packed, int64_t rows, int64_t rank, int8_t* signs, void* stream) {
+  if (!signs || !packed) return fail(LB_ERR_INVALID_ARGUMENT, "null pointer");
+  if (rows <= 0 || rank <= 0) return fail(LB_ERR_INVALID_ARGUMENT, "rows and rank must be positive");
+  HIP_TRY(launch_unpack_signs(packed, rows, rank, signs, reinterpret_cast<hipStream_t>(stream)));
+  return LB_OK;
+}
+
+lb_status lb_linear_create(int64_t d_out, int64_t d_in, const lb_path* paths, int32_t n_paths, void* stream,
+                           lb_linear* out) {
+  if (!out) return fail(LB_ERR_INVALID_ARGUMENT, "out is null");
+  if (!paths) return fail(LB_ERR_INVALID_ARGUMENT, "paths is null");
+  if (n_paths != 1 && n_paths != 2) return fail(LB_ERR_INVALID_ARGUMENT, "n_paths must be 1 or 2 (got %d)", n_paths);
+  if (d_out <= 0 || d_in <= 0) return fail(LB_ERR_INVALID_ARGUMENT, "d_out and d_in must be positive");
+  if (d_out > LB_MAX_DIM || d_in > LB_MAX_DIM) return fail(LB_ERR_UNSUPPORTED, "dimension exceeds %d", LB_MAX_DIM);
+  for (int p = 0; p < n_paths; ++p) {
+    const lb_path& P = paths[p];
+    if (P.rank <= 0) return fail(LB_ERR_INVALID_ARGUMENT, "path %d: rank must be positive", p);
+    if (P.rank > LB_MAX_RANK) return fail(LB_ERR_UNSUPPORTED, "path %d: rank exceeds %d", p, LB_MAX_RANK);
+    if (!P.u_packed || !P.v_packed || !P.h || !P.g || !P.l)
+      return fail(LB_ERR_INVALID_ARGUMENT, "path %d: null pointer", p);
+  }
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  lb_linear L = new (std::nothrow) lb_linear_s();
+  if (!L) return fail(LB_ERR_OUT_OF_MEMORY, "host allocation failed");
+  L->device = current_device();
+  L->m = d_out;
+  L->n = d_in;
+  L->np = n_paths;
+  // sizes of every piece
+  const int nkc = (int)((d_in + kChunk - 1) / kChunk);
+  const int nrt = (int)((d_out + kTile - 1) / kTile);
+  size_t total = 0;
+  int uw = 0;
+  size_t pre_bytes = prefill_layer_bytes(d_out, d_in, paths, n_paths);
+  for (int p = 0; p < n_paths; ++p) {
+    const int64_t r = paths[p].rank, W = words_per_row(r), nct = (r + kTile - 1) / kTile;
+    L->r[p] = r;
+    uw += (int)W;
+    total += align256(d_out * W * 4) + align256(d_in * W * 4);                  // canonical
+    total += align256((d_out + d_in + r) * 2);                                   // fp16 scales
+    total += align256((size_t)nkc * nct * 64 * 4);                              // decode V
+  }
+  total += align256((size_t)nrt * uw * 16 * 4);                                  // decode U
+  total += pre_bytes;
+  L->uw = uw;
+  hipError_t e = hipMalloc(&L->arena.base, total);
+  if (e != hipSuccess) {
+    delete L;
+    return hip_fail(e, "hipMalloc(layer)");
+  }
+  L->arena.size = total;
+  auto bail = [&](hipError_t err, const char* what) {
+    linear_free(L);
+    return hip_fail(err, what);
+  };
+  L->udec = reinterpret_cast<uint32_t*>(L->arena.take((size_t)nrt * uw * 16 * 4));
+  int woff = 0;
+  for (int p = 0; p < n_paths; ++p) {
+    const lb_path& S = paths[p];
+    const int64_t r = S.rank, W = words_per_row(r);
+    PathDev& D = L->paths[p];
+    D.r = (int)r;
+    D.W = (int)W;
+    D.nct = (int)((r + kTile - 1) / kTile);
+    uint32_t* ucan = reinterpret_cast<uint32_t*>(L->arena.take(d_out * W * 4));
+    uint32_t* vcan = reinterpret_cast<uint32_t*>(L->arena.take(d_in * W * 4));
+    uint16_t* sc = reinterpret_cast<uint16_t*>(L->arena.take((d_out + d_in + r) * 2));
+    uint32_t* vdec = reinterpret_cast<uint32_t*>(L->arena.take((size_t)nkc * D.nct * 64 * 4));
+    D.u_can = ucan;
+    D.v_can = vcan;
+    D.h = sc;
+    D.g = sc + d_out;
+    D.l = sc + d_out + d_in;
+    D.vdec = vdec;
+    if ((e = hipMemcpyAsync(ucan, S.u_packed, d_out * W * 4, hipMemcpyDefault, st)) != hipSuccess) return bail(e, "copy U");
+    if ((e = hipMemcpyAsync(vcan, S.v_packed, d_in * W * 4, hipMemcpyDefault, st)) != hipSuccess) return bail(e, "copy V");
+    if ((e = hipMemcpyAsync(sc, S.h, d_out * 2, hipMemcpyDefault, st)) != hipSuccess) return bail(e, "copy h");
+    if ((e = hipMemcpyAsync(sc + d_out, S.g, d_in * 2, hipMemcpyDefault, st)) != hipSuccess) return bail(e, "copy g");
+    if ((e = hipMemcpyAsync(sc + d_out + d_in, S.l, r * 2, hipMemcpyDefault, st)) != hipSuccess) return bail(e, "copy l");
+    if ((e = launch_retile_v_decode(vcan, (int)d_in, (int)r, vdec, st)) != hipSuccess) return bail(e, "retile V");
+    if ((e = launch_retile_u_decode(ucan, (int)d_out, (int)r, (int)W, uw, woff, L->udec, st)) != hipSuccess)
+      return bail(e, "retile U");
+    woff += (int)W;
+  }
+  if ((e = prefill_layer_build(L->pre, L->arena.take(pre_bytes), pre_bytes, d_out, d_in, L->paths, n_paths, st)) !=
+      hipSuccess)
+    return bail(e, "prefill layout");
+  *out = L;
+  return LB_OK;
+}
+
+lb_status lb_linear_info(lb_linear L, int64_t* d_out, int64_t* d_in, int32_t* n_paths, int64_t* ranks,
+                         int64_t* device_bytes) {
+  if (!L) return fail(LB_ERR_INVALID_ARGUMENT, "null linear");
+  if (d_out) *d_out = L->m;
+  if (d_in) *d_in = L->n;
+  if (n_paths) *n_paths = L->np;
+  if (ranks)
+    for (int p = 0; p < L->np; ++p) ranks[p] = L->r[p];
+  if (device_bytes) *device_bytes = (int64_t)L->arena.size;
+  return LB_OK;
+}
+
+lb_status lb_linear_forward_ex(lb_linear L, const void* x, void* y, int64_t tokens, lb_dtype io, lb_regime regime,
+                               void* stream) {
+  if (!L) return fail(LB_ERR_INVALID_ARGUMENT, "null linear");
+  if (!x || !y) return fail(LB_ERR_INVALID_ARGUMENT, "null x or y");
+  lb_status s = check_io(tokens, io, regime);
+  if (s != LB_OK) return s;
+  if (!aligned16(x) || !aligned16(y)) return fail(LB_ERR_ALIGNMENT, "x and y must be 16-byte aligned");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const lb_regime rg = pick_regime(tokens, io, regime);
+  // scratch and plans are rebuilt on the host: order them after the previous call's work
+  if (L->last_stream != st && L->last_stream) HIP_TRY(hipStreamSynchronize(L->last_stream));
+  L->last_stream = st;
+  if (rg == LB_REGIME_EXACT) {
+    int rpad = 0;
+    for (int p = 0; p < L->np; ++p) rpad = std::max(rpad, L->paths[p].r);
+    rpad = (rpad + 15) / 16 * 16;
+    const size_t want = (size_t)L->np * tokens * rpad * sizeof(float);
+    if (want > L->zexact.bytes) {
+      HIP_TRY(hipStreamSynchronize(st));
+      HIP_TRY(L->zexact.ensure(want));
+    }
+    HIP_TRY(launch_exact(L->paths, L->np, (int)L->m, (int)L->n, x, y, (int)tokens, io == LB_FP32,
+                         reinterpret_cast<float*>(L->zexact.ptr), rpad, st));
+    return LB_OK;
+  }
+  if (rg == LB_REGIME_DECODE) {
+    const int T = (int)std::min<int64_t>(tokens, kDecodeMaxTokens);
+    if (L->plan.T != T) HIP_TRY(hipStreamSynchronize(st));
+    lb_linear one[1] = {L};
+    return run_decode(L->plan, one, 1, nullptr, nullptr, x, y, tokens, st);
+  }
+  if (!prefill_available()) return fail(LB_ERR_UNSUPPORTED, "the prefill kernels are not available in this build");
+  const PrefillLayer* one[1] = {&L->pre};
+  const void* xs[1] = {x};
+  void* ys[1] = {y};
+  HIP_TRY(prefill_run(L->pplan, one, 1, xs, ys, (int)tokens, st, /*sync_on_rebuild=*/true));
+  return LB_OK;
+}
+
+lb_status lb_linear_forward(lb_linear L, const void* x, void* y, int64_t tokens, lb_dtype io, void* stream) {
+  return lb_linear_forward_ex(L, x, y, tokens, io, LB_REGIME_AUTO, stream);
+}
+
+lb_status lb_linear_destroy(lb_linear L) {
+  linear_free(L);
+  return LB_OK;
+}
+
+lb_status lb_stack_create(const lb_linear* linears, int32_t count, lb_stack* out) {
+  if (!out || !linears) return fail(LB_ERR_INVALID_ARGUMENT, "null pointer");
+  if (count <= 0) return fail(LB_ERR_INVALID_ARGUMENT, "count must be positive");
+  if (count > LB_MAX_STACK) return fail(LB_ERR_UNSUPPORTED, "count exceeds %d", LB_MAX_STACK);
+  for (int i = 0; i < count; ++i) {
+    if (!linears[i]) return fail(LB_ERR_INVALID_ARGUMENT, "linear %d is null", i);
+    if (linears[i]->device != linears[0]->device) return fail(LB_ERR_INVALID_ARGUMENT, "linears on different devices");
+  }
+  lb_stack S = new (std::nothrow) lb_stack_s();
+  if (!S) return fail(LB_ERR_OUT_OF_MEMORY, "host allocation failed");
+  S->device = linears[0]->device;
+  S->linears.assign(linears, linears + count);
+  for (int i = 0; i < count; ++i) S->pre.push_back(&linears[i]->pre);
+  hipError_t e = hipMalloc(&S->xs_d, count * sizeof(void*));
+  if (e == hipSuccess) e = hipMalloc(&S->ys_d, count * sizeof(void*));
+  if (e == hipSuccess) e = hipStreamCreateWithFlags(&S->cap_stream, hipStreamNonBlocking);
+  if (e != hipSuccess) {
+    lb_stack_destroy(S);
+    return hip_fail(e, "lb_stack_create");
+  }
+  *out = S;
+  return LB_OK;
+}
+
+namespace {
+
+// Enqueues the stack's kernels on `st` (no graph).
+lb_status stack_launch(lb_stack S, lb_regime rg, int64_t tokens, lb_dtype io, hipStream_t st) {
+  const int count = (int)S->linears.size();
+  if (rg == LB_REGIME_DECODE)
+    return run_decode(S->plan, S->linears.data(), count, S->xs_d, S->ys_d, nullptr, nullptr, tokens, st);
+  if (rg == LB_REGIME_PREFILL) {
+    HIP_TRY(prefill_run(S->pplan, S->pre.data(), count, S->xs_h.data(), S->ys_h.data(), (int)tokens, st, false));
+    return LB_OK;
+  }
+  // exact: one pair of kernels per linear, sharing one z' scratch laid out per entry
+  size_t off = 0;
+  for (int i = 0; i < count; ++i) {
+    lb_linear L = S->linears[i];
+    int rpad = 0;
+    for (int p = 0; p < L->np; ++p) rpad = std::max(rpad, L->paths[p].r);
+    rpad = (rpad + 15) / 16 * 16;
+    HIP_TRY(launch_exact(L->paths, L->np, (int)L->m, (int)L->n, S->xs_h[i], S->ys_h[i], (int)tokens, io == LB_FP32,
+                         reinterpret_cast<float*>(S->zexact.ptr) + off, rpad, st));
+    off += (size_t)L->np * tokens * rpad;
+  }
+  return LB_OK;
+}
+
+// Prepares everything a launch sequence needs outside of any graph capture.
+lb_status stack_prepare(lb_stack S, lb_regime rg, int64_t tokens) {
+  const int count = (int)S->linears.size();
+  if (rg == LB_REGIME_DECODE) {
+    const int T = (int)std::min<int64_t>(tokens, kDecodeMaxTokens);
+    lb_status s = build_decode_plan(S->plan, S->linears.data(), count, T);
+    if (s != LB_OK) return s;
+    (void)decode_grid_size(S->plan.tb);  // occupancy query before any capture
+    if (tokens > kDecodeMaxTokens && tokens % kDecodeMaxTokens) {
+      // a ragged last slice uses another plan shape: keep direct launches for it
+      return LB_OK;
+    }
+  } else if (rg == LB_REGIME_PREFILL) {
+    if (!prefill_available()) return fail(LB_ERR_UNSUPPORTED, "the prefill kernels are not available in this build");
+    HIP_TRY(prefill_prepare(S->pplan, S->pre.data(), count, (int)tokens));
+  } else {
+    size_t want = 0;
+    for (lb_linear L : S->linears) {
+      int rpad = 0;
+      for (int p = 0; p < L->np; ++p) rpad = std::max(rpad, L->paths[p].r);
+      want += (size_t)L->np * tokens * ((rpad + 15) / 16 * 16);
+    }
+    HIP_TRY(S->zexact.ensure(std::max<size_t>(want, 1) * sizeof(float)));
+  }
+  return LB_OK;
+}
+
+}  // namespace
+
+lb_status lb_stack_forward_ex(lb_stack S, const void* const* xs, void* const* ys, int64_t tokens, lb_dtype io,
+                              lb_regime regime, int32_t use_graph, void* stream) {
+  if (!S) return fail(LB_ERR_INVALID_ARGUMENT, "null stack");
+  if (!xs || !ys) return fail(LB_ERR_INVALID_ARGUMENT, "null pointer array");
+  lb_status s = check_io(tokens, io, regime);
+  if (s != LB_OK) return s;
+  const int count = (int)S->linears.size();
+  for (int i = 0; i < count; ++i) {
+    if (!xs[i] || !ys[i]) return fail(LB_ERR_INVALID_ARGUMENT, "entry %d: null x or y", i);
+    if (!aligned16(xs[i]) || !aligned16(ys[i])) return fail(LB_ERR_ALIGNMENT, "entry %d: pointer not 16-byte aligned", i);
+  }
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const lb_regime rg = pick_regime(tokens, io, regime);
+  const bool same_ptrs = S->xs_h.size() == (size_t)count && std::equal(xs, xs + count, S->xs_h.begin()) &&
+                         std::equal(ys, ys + count, S->ys_h.begin());
+  const bool same = same_ptrs && S->g_tokens == tokens && S->g_io == (int)io && S->g_regime == (int)rg;
+  if (!same) {
+    // everything below rewrites memory earlier launches read: wait for them
+    if (S->last_stream) HIP_TRY(hipStreamSynchronize(S->last_stream));
+    HIP_TRY(hipStreamSynchronize(st));
+    S->xs_h.assign(xs, xs + count);
+    S->ys_h.assign(ys, ys + count);
+    HIP_TRY(hipMemcpy(S->xs_d, S->xs_h.data(), count * sizeof(void*), hipMemcpyHostToDevice));
+    HIP_TRY(hipMemcpy(S->ys_d, S->ys_h.data(), count * sizeof(void*), hipMemcpyHostToDevice));
+    s = stack_prepare(S, rg, tokens);
+    if (s != LB_OK) return s;
+    if (S->exec) HIP_TRY(hipGraphExecDestroy(S->exec));
+    if (S->graph) HIP_TRY(hipGraphDestroy(S->graph));
+    S->exec = nullptr;
+    S->graph = nullptr;
+    S->g_tokens = tokens;
+    S->g_io = (int)io;
+    S->g_regime = (int)rg;
+  }
+  S->last_stream = st;
+  const bool ragged_decode = rg == LB_REGIME_DECODE && tokens > kDecodeMaxTokens && tokens % kDecodeMaxTokens;
+  if (!use_graph || ragged_decode) return stack_launch(S, rg, tokens, io, st);
+  if (!S->exec) {
+    HIP_TRY(hipStreamBeginCapture(S->cap_stream, hipStreamCaptureModeThreadLocal));
+    lb_status ls = stack_launch(S, rg, tokens, io, S->cap_stream);
+    hipGraph_t g = nullptr;
+    hipError_t ce = hipStreamEndCapture(S->cap_stream, &g);
+    if (ls != LB_OK) {
+      if (g) (void)hipGraphDestroy(g);
+      return ls;
+    }
+    if (ce != hipSuccess) return hip_fail(ce, "hipStreamEndCapture");
+    S->graph = g;
+    HIP_TRY(hipGraphInstantiate(&S->exec, S->graph, nullptr, nullptr, 0));
+  }
+  HIP_TRY(hipGraphLaunch(S->exec, st));
+  return LB_OK;
+}
+
+lb_status lb_stack_forward(lb_stack S, const void* const* xs, void* const* ys, int64_t tokens, lb_dtype io,
+                           void* stream) {
+  return lb_stack_forward_ex(S, xs, ys, tokens, io, LB_REGIME_AUTO, 1, stream);
+}
+
+lb_status lb_stack_destroy(lb_stack S) {
+  if (!S) return LB_OK;
+  if (S->exec) (void)hipGraphExecDestroy(S->exec);
+  if (S->graph) (void)hipGraphDestroy(S->graph);
+  if (S->cap_stream) (void)hipStreamDestroy(S->cap_stream);
+  if (S->xs_d) (void)hipFree(S->xs_d);
+  if (S->ys_d) (void)hipFree(S->ys_d);
+  S->plan.release();
+  prefill_plan_release(S->pplan);
+  S->zexact.release();
+  delete S;
+  return LB_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,178 @@
+/*
+ * littlebit.h -- C ABI of the MI355X (gfx950) LittleBit factorised-linear library.
+ *
+ * The layer (paper notes "LittleBit: Ultra Low-Bit Quantization via Latent
+ * Factorization", section "Key design / multi-scale compensation" for one path
+ * and section "Residual compensation" for the sum of two paths):
+ *
+ *     W = sum_{p < n_paths} diag(h_p) * U_p * diag(l_p) * V_p^T * diag(g_p)
+ *     y = x * W^T
+ *
+ * U_p in {-1,+1}^{d_out x r_p} and V_p in {-1,+1}^{d_in x r_p} are the sign
+ * factors, h_p (length d_out), g_p (length d_in) and l_p (length r_p) the row,
+ * column and latent scales, stored as IEEE fp16.  The same section says the
+ * inference forward is a sequence of element-wise products and binary matrix
+ * products that never forms W; every forward entry point here follows that
+ * order (x o g -> V -> o l -> U -> o h) and never materialises W.
+ *
+ * Conventions common to every call
+ * --------------------------------
+ * - Shapes: d_out = m rows of W (length of h), d_in = n columns (length of g).
+ *   x is [tokens][d_in], y is [tokens][d_out], both row-major and contiguous.
+ *   y is overwritten, never accumulated into.
+ * - Canonical packed signs (the interchange format of this ABI): a factor
+ *   S in {-1,+1}^{rows x r} packs row by row into W = ceil(r/32) uint32 words
+ *   per row; bit (j mod 32) of word i*W + j/32 is 1 iff S[i][j] == -1.  Bits
+ *   at positions j >= r are zero.
+ * - Pointers marked "device" are HIP device pointers on the device that is
+ *   current when the call is made; "host" pointers are ordinary CPU memory.
+ *   Every pointer passed to a forward call must be 16-byte aligned.
+ * - stream is a hipStream_t passed as void* (NULL = the null stream).  Calls
+ *   that take a stream are asynchronous on it unless stated otherwise.
+ * - Errors: every call returns lb_status.  No C++ exception crosses the ABI.
+ *   On any error the call's outputs are left untouched and lb_last_error()
+ *   returns a description (thread-local).  HIP failures return LB_ERR_HIP
+ *   with the HIP error text.  Faults inside kernels surface at the caller's
+ *   next synchronisation, as with any asynchronous stream API.
+ */
+#ifndef LITTLEBIT_H
+#define LITTLEBIT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LB_OK = 0,
+  LB_ERR_INVALID_ARGUMENT = 1, /* null pointer, non-positive size, bad enum  */
+  LB_ERR_INVALID_SIGN = 2,     /* an unpacked sign value outside {-1, +1}     */
+  LB_ERR_ALIGNMENT = 3,        /* a forward pointer is not 16-byte aligned    */
+  LB_ERR_UNSUPPORTED = 4,      /* a size beyond the documented limits         */
+  LB_ERR_OUT_OF_MEMORY = 5,    /* device allocation failed                    */
+  LB_ERR_HIP = 6               /* a HIP runtime call failed                   */
+} lb_status;
+
+typedef enum { LB_BF16 = 0, LB_FP32 = 1 } lb_dtype; /* element type of x and y */
+
+/* Which kernels run a forward.  AUTO picks by tokens and dtype:
+ *   fp32 I/O            -> EXACT  (fp32 vector arithmetic end to end);
+ *   bf16, tokens <  LB_PREFILL_MIN_TOKENS -> DECODE (fused fp8 x fp4 MFMA pass);
+ *   bf16, tokens >= LB_PREFILL_MIN_TOKENS -> PREFILL (bf16 MFMA GEMMs).
+ * Forcing a regime is for tests and measurements; every regime accepts every
+ * token count.  DECODE and PREFILL require bf16 I/O. */
+typedef enum { LB_REGIME_AUTO = 0, LB_REGIME_EXACT = 1, LB_REGIME_DECODE = 2,
+               LB_REGIME_PREFILL = 3 } lb_regime;
+
+#define LB_PREFILL_MIN_TOKENS 128
+
+/* Limits (LB_ERR_UNSUPPORTED beyond them). */
+#define LB_MAX_DIM    (1 << 20)   /* d_in, d_out                */
+#define LB_MAX_RANK   4096        /* r_p                        */
+#define LB_MAX_TOKENS (1 << 20)   /* tokens per forward         */
+#define LB_MAX_STACK  65536       /* linears in one stack       */
+
+typedef struct lb_linear_s* lb_linear; /* opaque, immutable after create */
+typedef struct lb_stack_s* lb_stack;   /* opaque                         */
+
+/* One path: diag(h) * U * diag(l) * V^T * diag(g).  All pointers are device
+ * pointers; they are only read during lb_linear_create. */
+typedef struct {
+  int64_t rank;              /* r_p >= 1                                     */
+  const uint32_t* u_packed;  /* [d_out][ceil(r/32)] canonical packed U signs */
+  const uint32_t* v_packed;  /* [d_in ][ceil(r/32)] canonical packed V signs */
+  const uint16_t* h;         /* [d_out] fp16 bit patterns, row scale         */
+  const uint16_t* g;         /* [d_in ] fp16 bit patterns, column scale      */
+  const uint16_t* l;         /* [rank ] fp16 bit patterns, latent scale      */
+} lb_path;
+
+/* ceil(rank / 32): uint32 words per row of a canonical packed factor
+ * (0 for rank <= 0). */
+int64_t lb_packed_words_per_row(int64_t rank);
+
+/* Per-path rank for a sign-bit budget of bpw_num/bpw_den bits per weight:
+ * round(BPW * d_out * d_in / (2 * (d_out + d_in))) in exact integer
+ * arithmetic, ties rounded up.  Two paths of this rank store 2 r (m + n) sign
+ * bits for m n weights (bits-per-weight accounting: paper notes "LittleBit",
+ * sections "Overall framework" and "Residual compensation"; the aibk.xyz
+ * article's advice on how bpp is counted).  Scale bits are not counted.
+ * Returns -1 for non-positive arguments. */
+int64_t lb_rank_for_bpw(int64_t d_out, int64_t d_in, int64_t bpw_num, int64_t bpw_den);
+
+/* Pack an int8 sign matrix [rows][rank] (values -1 / +1, host memory) into
+ * canonical words [rows][ceil(rank/32)] (host memory).  Synchronous.
+ * LB_ERR_INVALID_SIGN if any value is not -1 or +1 (packed untouched). */
+lb_status lb_pack_signs_host(const int8_t* signs, int64_t rows, int64_t rank, uint32_t* packed);
+
+/* Device version of lb_pack_signs_host: signs and packed are device
+ * pointers.  Validates every value first and returns LB_ERR_INVALID_SIGN
+ * without writing packed if any is not +-1.  Synchronises `stream` (it reads
+ * the validation result back). */
+lb_status lb_pack_signs(const int8_t* signs, int64_t rows, int64_t rank, uint32_t* packed, void* stream);
+
+/* Inverse of lb_pack_signs (test aid): device packed -> device int8 +-1.
+ * Padding bits are ignored.  Asynchronous on stream. */
+lb_status lb_unpack_signs(const uint32_t* packed, int64_t rows, int64_t rank, int8_t* signs, void* stream);
+
+/* Build a linear from n_paths (1 or 2) paths.  The library COPIES the packed
+ * signs and scales into memory it owns (re-laid out for its kernels) using
+ * `stream`; the caller's buffers may be freed once `stream` has synchronised.
+ * The linear is bound to the current device.  Returns LB_ERR_INVALID_ARGUMENT
+ * for null pointers, d_out/d_in/rank <= 0 or n_paths not in {1, 2}. */
+lb_status lb_linear_create(int64_t d_out, int64_t d_in, const lb_path* paths, int32_t n_paths,
+                           void* stream, lb_linear* out);
+
+/* y = x W^T for `tokens` rows.  x and y are device pointers (bf16 or fp32 per
+ * `io`), borrowed until the stream work completes.  Runs the kernels of
+ * LB_REGIME_AUTO.  Concurrent forwards of the same linear must be ordered on
+ * one stream (they share the linear's scratch memory). */
+lb_status lb_linear_forward(lb_linear L, const void* x, void* y, int64_t tokens, lb_dtype io, void* stream);
+
+/* As lb_linear_forward with an explicit regime. */
+lb_status lb_linear_forward_ex(lb_linear L, const void* x, void* y, int64_t tokens, lb_dtype io,
+                               lb_regime regime, void* stream);
+
+/* Shape of a linear; any output pointer may be NULL.  ranks receives n_paths
+ * values; device_bytes is the library-owned device memory of the linear. */
+lb_status lb_linear_info(lb_linear L, int64_t* d_out, int64_t* d_in, int32_t* n_paths,
+                         int64_t* ranks, int64_t* device_bytes);
+
+/* Frees the linear's device memory.  Does not synchronise: the caller must
+ * make sure no queued work still uses it.  NULL is accepted. */
+lb_status lb_linear_destroy(lb_linear L);
+
+/* A stack is an ordered list of linears run together by lb_stack_forward.
+ * It borrows the linears, which must outlive it.  All linears must live on
+ * the same device. */
+lb_status lb_stack_create(const lb_linear* linears, int32_t count, lb_stack* out);
+
+/* Runs every linear i of the stack: ys[i] = xs[i] W_i^T, `tokens` rows each
+ * (xs and ys are host arrays of `count` device pointers).  Entries are
+ * independent: the library runs them concurrently, so no ys[i] may alias any
+ * xs[j] or another ys[k].  The launch sequence is captured once into a HIP
+ * graph and replayed on `stream`; it is re-captured when the pointers,
+ * tokens, io or regime change.  Calls on one stack must be ordered on one
+ * stream (they share the stack's scratch memory and graph). */
+lb_status lb_stack_forward(lb_stack S, const void* const* xs, void* const* ys, int64_t tokens,
+                           lb_dtype io, void* stream);
+
+/* As lb_stack_forward with an explicit regime and graph use (use_graph = 0
+ * launches the same kernels directly, without a graph). */
+lb_status lb_stack_forward_ex(lb_stack S, const void* const* xs, void* const* ys, int64_t tokens,
+                              lb_dtype io, lb_regime regime, int32_t use_graph, void* stream);
+
+/* Frees the stack (not its linears).  Does not synchronise.  NULL accepted. */
+lb_status lb_stack_destroy(lb_stack S);
+
+/* Static text for a status code. */
+const char* lb_status_string(lb_status s);
+
+/* Thread-local description of this thread's last failure ("" if none). */
+const char* lb_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LITTLEBIT_H */

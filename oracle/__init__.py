@@ -6,6 +6,7 @@ from .littlebit_oracle import (  # noqa: F401
     decode_path,
     forward,
     forward_factored,
+    forward_rows,
     linear_storage_bytes,
     pack_signs,
     rank_for_bpw,

@@ -209,3 +209,19 @@ def linear_storage_bytes(m: int, n: int, ranks: Iterable[int]) -> Fraction:
     """Bytes of one factorised linear: sign bits / 8 plus fp16 scales."""
     ranks = list(ranks)
     return Fraction(sum(int(r) * (m + n) for r in ranks), 8) + 2 * sum(m + n + int(r) for r in ranks)
+
+
+def forward_rows(x: np.ndarray, paths: Sequence[Dict], m: int, n: int, rows: Sequence[int]) -> np.ndarray:
+    """y[:, rows] from the explicit rows W[rows, :] of the same weight definition.
+
+    Lets full-size layers be checked on a sample of outputs: only the selected
+    rows of W = sum_p diag(h_p) U_p diag(l_p) V_p^T diag(g_p) are formed.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    x = np.asarray(x, dtype=np.float64)
+    Wr = np.zeros((rows.size, n), dtype=np.float64)
+    for path in paths:
+        f = decode_path(path, m, n)
+        left = f["h"][rows, None] * f["U"][rows] * f["l"][None, :]
+        Wr += left @ (f["V"] * f["g"][:, None]).T
+    return x @ Wr.T

@@ -1,0 +1,269 @@
+"""Parity of the HIP library (through its C ABI) with the CPU oracle.
+
+Exact probes use inputs for which every intermediate is exactly representable
+(small integers, one-hot activations, unit or power-of-two scales), so the GPU
+must match the oracle bit for bit; float parity uses seeded synthetic layers
+and the acceptance criteria in lbtest.py.
+"""
+import numpy as np
+import pytest
+
+import binary_rank_gemm_amd as lb
+import oracle
+import synth
+from lbtest import assert_bf16_close, assert_fp32_close, log, to_f64, x_f64, x_tensor
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _needs_gpu(gpu):
+    return gpu
+
+
+def f16bits(v):
+    return np.asarray(v, np.float16).view(np.uint16)
+
+
+def build(m, n, paths):
+    return lb.Linear.from_numpy(m, n, paths)
+
+
+def seeded_paths(key, m, n, ranks):
+    return synth.layer_tensors(key[0], key[1], key[2], m, n, ranks)
+
+
+# ----------------------------------------------------------------------------
+# packing
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("rows,rank", [(1, 1), (17, 31), (100, 32), (33, 33), (1000, 319), (64, 1027)])
+def test_pack_signs_device_bit_exact(rows, rank):
+    log(f"pack rows={rows} rank={rank}")
+    s = synth.int8_signs((11, rows, rank), rows, rank)
+    d = torch.from_numpy(s).cuda()
+    w = lb.pack_signs(d)
+    torch.cuda.synchronize()
+    got = w.cpu().numpy().view(np.uint32)
+    assert np.array_equal(got, oracle.pack_signs(s))
+    assert np.array_equal(got, lb.pack_signs_host(s))
+    back = lb.unpack_signs(w, rank)
+    torch.cuda.synchronize()
+    assert np.array_equal(back.cpu().numpy(), s)
+
+
+def test_pack_signs_device_rejects_bad_values_untouched():
+    s = np.ones((4, 40), np.int8)
+    s[2, 17] = 0
+    d = torch.from_numpy(s).cuda()
+    out = torch.full((4, 2), 12345, dtype=torch.int32, device="cuda")
+    with pytest.raises(lb.LittleBitError) as ei:
+        lb.lib()
+        st = lb._binding._check(lb.lib().lb_pack_signs(d.data_ptr(), 4, 40, out.data_ptr(),
+                                                         torch.cuda.current_stream().cuda_stream))
+    assert ei.value.status == lb._binding.INVALID_SIGN
+    torch.cuda.synchronize()
+    assert torch.all(out == 12345)
+
+
+# ----------------------------------------------------------------------------
+# fp32 exact path
+# ----------------------------------------------------------------------------
+
+def test_exact_fp32_single_512_workload():
+    wl = synth.WORKLOADS["single-512"]
+    m, n, r, T = 512, 512, wl.fixed_rank, wl.tokens[0]
+    log(f"exact fp32 single-512 T={T}")
+    paths = seeded_paths((wl.wid, 0, 0), m, n, [r, r])
+    x = synth.layer_activations(wl, 0, 0, n, T)
+    lin = build(m, n, paths)
+    y = lin.forward(x_tensor(x))
+    torch.cuda.synchronize()
+    s = assert_fp32_close(to_f64(y), oracle.forward(x_f64(x), paths, m, n), "single-512 fp32")
+    log(f"  E_max/rms = {s['emax_rel_rms']:.2e}")
+
+
+def test_exact_fp32_integer_probe_bit_exact():
+    """x in {-2..2}, scales in {1, 2}: every partial sum is an integer < 2^22, exact in fp32."""
+    rng = np.random.default_rng(21)
+    m, n, ranks, T = 300, 2048, [64, 40], 3
+    paths = []
+    for p, r in enumerate(ranks):
+        paths.append(dict(rank=r, u_words=synth.sign_words((21, p, 0), m, r), v_words=synth.sign_words((21, p, 1), n, r),
+                          h=f16bits(rng.choice([1.0, 2.0], m)), g=f16bits(rng.choice([1.0, 2.0], n)),
+                          l=f16bits(rng.choice([1.0, 2.0], r))))
+    x = rng.integers(-2, 3, size=(T, n)).astype(np.float32)
+    y_ref = oracle.forward(x.astype(np.float64), paths, m, n)
+    assert np.max(np.abs(y_ref)) < 2 ** 22
+    lin = build(m, n, paths)
+    y = lin.forward(torch.from_numpy(x).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(to_f64(y), y_ref)
+
+
+@pytest.mark.parametrize("m,n,ranks,T", [(300, 700, [37, 45], 5), (1000, 64, [1], 1), (33, 4100, [130, 7], 2)])
+def test_exact_fp32_ragged(m, n, ranks, T):
+    log(f"exact fp32 m={m} n={n} ranks={ranks} T={T}")
+    paths = seeded_paths((22, m, n), m, n, ranks)
+    x = synth.activations((22, T, n), T, n, io="fp32")
+    y = build(m, n, paths).forward(x_tensor(x))
+    torch.cuda.synchronize()
+    assert_fp32_close(to_f64(y), oracle.forward(x_f64(x), paths, m, n), "ragged fp32")
+
+
+# ----------------------------------------------------------------------------
+# decode path (bf16)
+# ----------------------------------------------------------------------------
+
+def onehot_x(n, ks, vals=None):
+    x = np.zeros((len(ks), n), np.float32)
+    for t, k in enumerate(ks):
+        x[t, k] = 1.0 if vals is None else vals[t]
+    return synth.bf16_bits_from_f32(x)
+
+
+@pytest.mark.parametrize("regime", [lb.REGIME_DECODE, lb.REGIME_EXACT])
+def test_identity_probe_bit_exact(regime):
+    """Unit scales, x = e_k: y = row k of V_p contracted with U_p, summed over
+    paths -- integers of magnitude <= r1 + r2 <= 256, exact in bf16."""
+    m, n, ranks = 333, 1000, [100, 80]
+    ones = lambda k: f16bits(np.ones(k))
+    paths = [dict(rank=r, u_words=synth.sign_words((23, p, 0), m, r), v_words=synth.sign_words((23, p, 1), n, r),
+                  h=ones(m), g=ones(n), l=ones(r)) for p, r in enumerate(ranks)]
+    ks = [0, 1, 127, 128, 500, 998, 999, 640]
+    x = onehot_x(n, ks)
+    log(f"identity probe regime={regime}")
+    y = build(m, n, paths).forward(x_tensor(x), regime=regime)
+    torch.cuda.synchronize()
+    y_ref = oracle.forward(x_f64(x), paths, m, n)
+    assert np.array_equal(to_f64(y), y_ref)
+
+
+def test_decode_power_of_two_scales_bit_exact():
+    """Scales in {1, 2} and x in {+-1, +-2} one-hot: |y| <= 256, every step exact."""
+    rng = np.random.default_rng(24)
+    m, n, ranks = 70, 4000, [10, 6]
+    paths = []
+    for p, r in enumerate(ranks):
+        paths.append(dict(rank=r, u_words=synth.sign_words((24, p, 0), m, r), v_words=synth.sign_words((24, p, 1), n, r),
+                          h=f16bits(rng.choice([1.0, 2.0], m)), g=f16bits(rng.choice([1.0, 2.0], n)),
+                          l=f16bits(rng.choice([1.0, 2.0], r))))
+    ks = [5, 3999, 2048, 77, 1000, 129, 130, 3000, 12, 13, 14]
+    x = onehot_x(n, ks, vals=[1, -1, 2, -2, 1, 1, -1, 2, -2, 1, 2])
+    y_ref = oracle.forward(x_f64(x), paths, m, n)
+    assert np.max(np.abs(y_ref)) <= 256
+    y = build(m, n, paths).forward(x_tensor(x), regime=lb.REGIME_DECODE)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_f64(y), y_ref)
+
+
+DECODE_SHAPES = [
+    # m, n, ranks, T, outliers
+    (512, 512, [16, 16], 4, 0.0),        # the single-512 shape in bf16
+    (300, 700, [37, 45], 1, 0.0),        # ragged everything
+    (1000, 1200, [149, 102], 3, 0.0),
+    (4096, 4096, [102, 102], 1, 0.01),   # Llama-2-7B q/k/v/o at 0.1 BPW with outlier channels
+    (1024, 8192, [46, 46], 8, 0.0),      # Llama-2-70B k/v at 0.1 BPW
+    (777, 2100, [319, 5], 9, 0.0),       # two token blocks, unequal ranks
+    (640, 384, [1, 1], 16, 0.0),
+    (513, 257, [33, 31], 17, 0.0),       # 17 tokens: two launches of the decode kernel
+    (2000, 300, [600], 2, 0.0),          # single path, rank above one column group
+]
+
+
+@pytest.mark.parametrize("m,n,ranks,T,outl", DECODE_SHAPES)
+def test_decode_parity(m, n, ranks, T, outl):
+    log(f"decode m={m} n={n} ranks={ranks} T={T}")
+    paths = seeded_paths((25, m, n), m, n, ranks)
+    x = synth.activations((25, T, n), T, n, outlier_frac=outl)
+    lin = build(m, n, paths)
+    y = lin.forward(x_tensor(x), regime=lb.REGIME_DECODE)
+    torch.cuda.synchronize()
+    s = assert_bf16_close(to_f64(y), oracle.forward(x_f64(x), paths, m, n), f"decode {m}x{n}")
+    log(f"  E_rms={s['erms']:.2e} E_max/rms={s['emax_rel_rms']:.2e}")
+    # deterministic: a second run is bit-identical
+    y2 = lin.forward(x_tensor(x), regime=lb.REGIME_DECODE)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+
+
+def test_forward_errors():
+    m, n = 64, 128
+    lin = build(m, n, seeded_paths((26, 0, 0), m, n, [8, 8]))
+    x = torch.zeros((4, n), dtype=torch.bfloat16, device="cuda")
+    y = torch.zeros((4, m), dtype=torch.bfloat16, device="cuda")
+    L = lb.lib()
+    st = torch.cuda.current_stream().cuda_stream
+    assert L.lb_linear_forward(lin.handle, x.data_ptr() + 2, y.data_ptr(), 3, lb.BF16, st) == lb._binding.ALIGNMENT
+    assert L.lb_linear_forward(lin.handle, x.data_ptr(), y.data_ptr(), 0, lb.BF16, st) == lb._binding.INVALID_ARGUMENT
+    assert L.lb_linear_forward_ex(lin.handle, x.data_ptr(), y.data_ptr(), 4, lb.FP32, lb.REGIME_DECODE, st) == \
+        lb._binding.UNSUPPORTED
+    assert L.lb_linear_forward_ex(lin.handle, x.data_ptr(), y.data_ptr(), 4, lb.BF16, 9, st) == \
+        lb._binding.INVALID_ARGUMENT
+    info = lin.info()
+    assert info["d_out"] == m and info["d_in"] == n and info["ranks"] == [8, 8] and info["device_bytes"] > 0
+
+
+# ----------------------------------------------------------------------------
+# stacks
+# ----------------------------------------------------------------------------
+
+STACK_SHAPES = [(256, 512, [16, 16]), (1024, 300, [33, 20]), (200, 2000, [102, 90]), (4096, 1024, [46, 46]),
+                (96, 96, [5]), (700, 700, [149, 149])]
+
+
+def make_stack(key, shapes, T, io="bf16"):
+    lins, paths, xs = [], [], []
+    for i, (m, n, ranks) in enumerate(shapes):
+        p = seeded_paths((key, i, 0), m, n, ranks)
+        paths.append(p)
+        lins.append(build(m, n, p))
+        xs.append(synth.activations((key, i, T), T, n, io=io))
+    return lins, paths, xs
+
+
+@pytest.mark.parametrize("T", [1, 8, 16])
+def test_stack_decode_graph_eager_single_agree(T):
+    log(f"stack decode T={T}")
+    lins, paths, xs = make_stack(27, STACK_SHAPES, T)
+    S = lb.Stack(lins)
+    xd = [x_tensor(x) for x in xs]
+    ys_g = [torch.empty((T, m), dtype=torch.bfloat16, device="cuda") for m, _, _ in STACK_SHAPES]
+    ys_e = [torch.empty_like(y) for y in ys_g]
+    S.forward(xd, ys_e, regime=lb.REGIME_DECODE, use_graph=False)
+    S.forward(xd, ys_g, regime=lb.REGIME_DECODE, use_graph=True)
+    torch.cuda.synchronize()
+    for i, (m, n, _) in enumerate(STACK_SHAPES):
+        single = lins[i].forward(xd[i], regime=lb.REGIME_DECODE)
+        torch.cuda.synchronize()
+        assert torch.equal(ys_g[i].view(torch.int16), ys_e[i].view(torch.int16)), f"graph != eager, entry {i}"
+        assert torch.equal(ys_g[i].view(torch.int16), single.view(torch.int16)), f"stack != single, entry {i}"
+        assert_bf16_close(to_f64(ys_g[i]), oracle.forward(x_f64(xs[i]), paths[i], m, n), f"stack entry {i}")
+    # replay the captured graph several times with eager work in between
+    ref = [y.clone() for y in ys_g]
+    for rep in range(3):
+        for y in ys_g:
+            y.zero_()
+        junk = torch.randn(1000, 1000, device="cuda") @ torch.randn(1000, 1000, device="cuda")
+        S.forward(xd, ys_g, regime=lb.REGIME_DECODE, use_graph=True)
+        torch.cuda.synchronize()
+        del junk
+        for i in range(len(ys_g)):
+            assert torch.equal(ys_g[i].view(torch.int16), ref[i].view(torch.int16)), f"replay {rep} entry {i}"
+
+
+def test_stack_exact_fp32_matches_single():
+    T = 3
+    lins, paths, xs = make_stack(28, STACK_SHAPES[:4], T, io="fp32")
+    S = lb.Stack(lins)
+    xd = [x_tensor(x) for x in xs]
+    ys = [torch.empty((T, m), dtype=torch.float32, device="cuda") for m, _, _ in STACK_SHAPES[:4]]
+    S.forward(xd, ys)
+    torch.cuda.synchronize()
+    for i, (m, n, _) in enumerate(STACK_SHAPES[:4]):
+        single = lins[i].forward(xd[i])
+        torch.cuda.synchronize()
+        assert torch.equal(ys[i], single)
+        assert_fp32_close(to_f64(ys[i]), oracle.forward(x_f64(xs[i]), paths[i], m, n), f"fp32 stack {i}")

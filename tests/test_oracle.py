@@ -338,3 +338,12 @@ def test_pages_storage_numbers():
     assert abs(2 * p70 / 1e9 - gold["llama2_70b_fp16_gb"]) / gold["llama2_70b_fp16_gb"] < 2e-3
     assert b70 / 1e9 < gold["llama2_70b_0p1bpw_max_gb"]
     assert Fraction(16) / Fraction(1, 10) == gold["bpw_0p1_vs_fp16_x"]
+
+
+def test_forward_rows_is_the_same_definition():
+    rng = np.random.default_rng(11)
+    m, n, r = 41, 23, 6
+    paths = [random_path(rng, m, n, r), random_path(rng, m, n, 4)]
+    x = oracle.decode_bf16(bf16bits(rng.choice(DYADIC, size=(3, n))))
+    rows = [0, 7, 40, 13]
+    assert np.array_equal(oracle.forward_rows(x, paths, m, n, rows), oracle.forward(x, paths, m, n)[:, rows])
