@@ -84,30 +84,24 @@ struct Scratch {
 // objects
 // ---------------------------------------------------------------------------
 
-// Decode launch plan: entries, work items and control words for a given token
-// count.  Owned by a linear (single forwards) or a stack.
+// Decode launch plan: entries and the two kernels' per-workgroup item lists for
+// a given token count.  Owned by a linear (single forwards) or a stack.
 struct DecodePlan {
   int T = -1;             // tokens per launch this plan was built for
   int tb = 0;
+  int count = 0;
   std::vector<DecEntry> entries_h;
-  std::vector<WorkItem> items_h;
   DecEntry* entries_d = nullptr;
-  WorkItem* items_d = nullptr;
-  unsigned int* counters_d = nullptr;  // [count]
-  unsigned int* ready_d = nullptr;     // [count]
-  Control* ctl_d = nullptr;
-  Scratch zbuf;
-  size_t cap_entries = 0, cap_items = 0;
+  WorkItem* items_d = nullptr;    // V items then U items, each longest first
+  int nv_items = 0, nu_items = 0;
+  Scratch work;                   // U-stage A images and correction sums of every entry
   void release() {
     if (entries_d) (void)hipFree(entries_d);
     if (items_d) (void)hipFree(items_d);
-    if (counters_d) (void)hipFree(counters_d);
-    if (ready_d) (void)hipFree(ready_d);
-    if (ctl_d) (void)hipFree(ctl_d);
-    entries_d = nullptr; items_d = nullptr; counters_d = nullptr; ready_d = nullptr; ctl_d = nullptr;
-    zbuf.release();
-    cap_entries = cap_items = 0;
+    entries_d = nullptr; items_d = nullptr;
+    work.release();
     T = -1;
+    count = 0;
   }
 };
 
@@ -164,16 +158,25 @@ void linear_free(lb_linear L) {
 // decode plans
 // ---------------------------------------------------------------------------
 
-// Builds (or reuses) the work list for `count` linears at `T` tokens per launch.
+// Items sorted longest first (stable): the order the hardware dispatches them.
+std::vector<WorkItem> longest_first(const std::vector<std::pair<double, WorkItem>>& items) {
+  std::vector<int> order(items.size());
+  for (size_t i = 0; i < items.size(); ++i) order[i] = (int)i;
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return items[a].first > items[b].first; });
+  std::vector<WorkItem> out;
+  for (int i : order) out.push_back(items[i].second);
+  return out;
+}
+
+// Builds (or reuses) the decode plan for `count` linears at `T` tokens per launch.
 lb_status build_decode_plan(DecodePlan& P, const lb_linear* L, int count, int T) {
-  if (P.T == T && (int)P.entries_h.size() == count) return LB_OK;
+  if (P.T == T && P.count == count) return LB_OK;
   const int tb = (T + 7) / 8;
-  const int ctm = decode_ct_max(tb);
+  const int ctm = decode_ct_max(T);
   P.entries_h.assign(count, DecEntry{});
-  std::vector<std::pair<int64_t, WorkItem>> vitems;
-  std::vector<int64_t> entry_weight(count, 0);
-  size_t zoff = 0;
-  std::vector<size_t> zoffs(count);
+  std::vector<std::pair<double, WorkItem>> vitems, uitems;
+  size_t work_bytes = 0;
+  std::vector<size_t> img_off(count), cp_off(count);
   for (int e = 0; e < count; ++e) {
     const lb_linear l = L[e];
     DecEntry& E = P.entries_h[e];
@@ -184,80 +187,68 @@ lb_status build_decode_plan(DecodePlan& P, const lb_linear* L, int count, int T)
     E.nrt = (int)((l->m + kTile - 1) / kTile);
     E.udec = l->udec;
     E.uw = l->uw;
-    int rmax = 0, woff = 0, nv = 0;
+    int woff = 0, pc = 0;
     for (int p = 0; p < l->np; ++p) {
       E.p[p] = l->paths[p];
       E.woff[p] = woff;
       woff += l->paths[p].W;
-      rmax = std::max(rmax, l->paths[p].r);
+      E.pcoff[p] = pc;
+      pc += (l->paths[p].r + kChunk - 1) / kChunk;
+      // column groups: balanced, even-sized (32-latent blocks never straddle two groups)
       const int nct = l->paths[p].nct;
-      const int groups = (nct + ctm - 1) / ctm;
-      const int per = (nct + groups - 1) / groups;
+      int groups = (nct + ctm - 1) / ctm;
+      int per = (nct + groups - 1) / groups;
+      per = std::min(ctm, per + (per & 1));
+      groups = (nct + per - 1) / per;
       E.vct[p] = per;
+      E.nvg[p] = groups;
       for (int g = 0; g < groups; ++g) {
         const int cnt = std::min(per, nct - g * per);
-        WorkItem w{(uint32_t)e, (uint16_t)p, (uint16_t)g};
-        const int64_t bytes = (int64_t)E.nkc * cnt;
-        vitems.push_back({bytes, w});
-        entry_weight[e] = std::max(entry_weight[e], bytes);
-        ++nv;
+        const double cost = (double)E.nkc * (cnt + 1.0 + T / 4.0) + 8.0;
+        vitems.push_back({cost, WorkItem{(uint32_t)e, (uint16_t)p, (uint16_t)g}});
       }
     }
-    E.nv = nv;
-    E.rpad = ((rmax + 15) / 16) * 16;
-    zoffs[e] = zoff;
-    zoff += (size_t)E.np * T * E.rpad;
+    E.npc = pc;
+    img_off[e] = work_bytes;
+    work_bytes += align256((size_t)E.npc * tb * kABytes);
+    cp_off[e] = work_bytes;
+    work_bytes += align256((size_t)E.np * kMaxGroups * 16 * sizeof(float));
+    const int nrg = (E.nrt + kDecodeRowTilesPerItem - 1) / kDecodeRowTilesPerItem;
+    for (int g = 0; g < nrg; ++g) {
+      const int rts = std::min(kDecodeRowTilesPerItem, E.nrt - g * kDecodeRowTilesPerItem);
+      const double cost = (double)rts * E.uw / 4.0 + 4.0;
+      uitems.push_back({cost, WorkItem{(uint32_t)e, (uint16_t)0, (uint16_t)g}});
+    }
   }
-  // V items first, longest first; then U items grouped by entry in the same order
-  std::stable_sort(vitems.begin(), vitems.end(),
-                   [](const std::pair<int64_t, WorkItem>& a, const std::pair<int64_t, WorkItem>& b) { return a.first > b.first; });
-  std::vector<int> order(count);
-  for (int e = 0; e < count; ++e) order[e] = e;
-  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return entry_weight[a] > entry_weight[b]; });
-  P.items_h.clear();
-  for (auto& v : vitems) P.items_h.push_back(v.second);
-  for (int e : order) {
-    const int nrg = (P.entries_h[e].nrt + kDecodeRowTilesPerItem - 1) / kDecodeRowTilesPerItem;
-    for (int g = 0; g < nrg; ++g) P.items_h.push_back(WorkItem{(uint32_t)e, (uint16_t)0x8000u, (uint16_t)g});
+  const std::vector<WorkItem> vlist = longest_first(vitems), ulist = longest_first(uitems);
+  std::vector<WorkItem> all(vlist);  // U items follow V items in one array
+  all.insert(all.end(), ulist.begin(), ulist.end());
+  // device buffers (callers synchronised with earlier launches before a rebuild)
+  HIP_TRY(P.work.ensure(std::max<size_t>(work_bytes, 256)));
+  for (int e = 0; e < count; ++e) {
+    P.entries_h[e].aimg = reinterpret_cast<uint8_t*>(P.work.ptr) + img_off[e];
+    P.entries_h[e].cpart = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(P.work.ptr) + cp_off[e]);
   }
-  // device buffers
-  HIP_TRY(P.zbuf.ensure(std::max<size_t>(zoff, 1) * sizeof(float)));
-  for (int e = 0; e < count; ++e) P.entries_h[e].zbuf = reinterpret_cast<float*>(P.zbuf.ptr) + zoffs[e];
-  if ((size_t)count > P.cap_entries) {
-    if (P.entries_d) HIP_TRY(hipFree(P.entries_d));
-    if (P.counters_d) HIP_TRY(hipFree(P.counters_d));
-    if (P.ready_d) HIP_TRY(hipFree(P.ready_d));
-    P.entries_d = nullptr; P.counters_d = nullptr; P.ready_d = nullptr;
-    HIP_TRY(hipMalloc(&P.entries_d, count * sizeof(DecEntry)));
-    HIP_TRY(hipMalloc(&P.counters_d, count * sizeof(unsigned int)));
-    HIP_TRY(hipMalloc(&P.ready_d, count * sizeof(unsigned int)));
-    P.cap_entries = count;
-  }
-  if (P.items_h.size() > P.cap_items) {
-    if (P.items_d) HIP_TRY(hipFree(P.items_d));
-    P.items_d = nullptr;
-    HIP_TRY(hipMalloc(&P.items_d, P.items_h.size() * sizeof(WorkItem)));
-    P.cap_items = P.items_h.size();
-  }
-  if (!P.ctl_d) HIP_TRY(hipMalloc(&P.ctl_d, sizeof(Control)));
-  // fresh control state: counters, flags and queue start at zero
-  HIP_TRY(hipMemset(P.counters_d, 0, count * sizeof(unsigned int)));
-  HIP_TRY(hipMemset(P.ready_d, 0, count * sizeof(unsigned int)));
-  HIP_TRY(hipMemset(P.ctl_d, 0, sizeof(Control)));
+  if (P.entries_d) HIP_TRY(hipFree(P.entries_d));
+  if (P.items_d) HIP_TRY(hipFree(P.items_d));
+  P.entries_d = nullptr; P.items_d = nullptr;
+  HIP_TRY(hipMalloc(&P.entries_d, count * sizeof(DecEntry)));
+  HIP_TRY(hipMalloc(&P.items_d, std::max<size_t>(all.size(), 1) * sizeof(WorkItem)));
   HIP_TRY(hipMemcpy(P.entries_d, P.entries_h.data(), count * sizeof(DecEntry), hipMemcpyHostToDevice));
-  HIP_TRY(hipMemcpy(P.items_d, P.items_h.data(), P.items_h.size() * sizeof(WorkItem), hipMemcpyHostToDevice));
+  if (!all.empty()) HIP_TRY(hipMemcpy(P.items_d, all.data(), all.size() * sizeof(WorkItem), hipMemcpyHostToDevice));
+  P.nv_items = (int)vlist.size();
+  P.nu_items = (int)ulist.size();
   P.T = T;
   P.tb = tb;
+  P.count = count;
   return LB_OK;
 }
 
-// Launches the decode kernel over token slices of at most kDecodeMaxTokens.
+// Launches the two decode kernels over token slices of at most kDecodeMaxTokens.
 lb_status run_decode(DecodePlan& P, const lb_linear* L, int count, const void* const* xs_d, void* const* ys_d,
                      const void* x0, void* y0, int64_t tokens, hipStream_t st) {
-  const int64_t full = std::min<int64_t>(tokens, kDecodeMaxTokens);
   for (int64_t t0 = 0; t0 < tokens; t0 += kDecodeMaxTokens) {
     const int T = (int)std::min<int64_t>(kDecodeMaxTokens, tokens - t0);
-    (void)full;
     if (P.T != T && P.T != -1) HIP_TRY(hipStreamSynchronize(st));  // the plan is rewritten below
     lb_status s = build_decode_plan(P, L, count, T);
     if (s != LB_OK) return s;
@@ -267,15 +258,12 @@ lb_status run_decode(DecodePlan& P, const lb_linear* L, int count, const void* c
     a.ys = ys_d;
     a.x0 = x0;
     a.y0 = y0;
-    a.items = P.items_d;
-    a.counters = P.counters_d;
-    a.ready = P.ready_d;
-    a.ctl = P.ctl_d;
-    a.nitems = (int)P.items_h.size();
     a.T = T;
     a.t0 = (int)t0;
-    a.spin_limit = 1 << 21;
-    HIP_TRY(launch_decode(a, P.tb, st));
+    a.items = P.items_d;
+    HIP_TRY(launch_decode_v(a, P.nv_items, st));
+    a.items = P.items_d + P.nv_items;
+    HIP_TRY(launch_decode_u(a, P.nu_items, st));
   }
   return LB_OK;
 }
@@ -579,7 +567,6 @@ lb_status stack_prepare(lb_stack S, lb_regime rg, int64_t tokens) {
     const int T = (int)std::min<int64_t>(tokens, kDecodeMaxTokens);
     lb_status s = build_decode_plan(S->plan, S->linears.data(), count, T);
     if (s != LB_OK) return s;
-    (void)decode_grid_size(S->plan.tb);  // occupancy query before any capture
     if (tokens > kDecodeMaxTokens && tokens % kDecodeMaxTokens) {
       // a ragged last slice uses another plan shape: keep direct launches for it
       return LB_OK;

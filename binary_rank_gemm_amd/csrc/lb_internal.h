@@ -36,52 +36,48 @@ struct PathDev {
   int r, W, nct;
 };
 
-// One entry of a decode / exact launch: a linear plus its activations.
+// One entry of a decode launch: a linear plus its activations.
 struct DecEntry {
   PathDev p[2];
   const uint32_t* udec;    // decode U layout, both paths
-  float* zbuf;             // scratch [np][T][rpad] of z' = (x o g) V o l
-  int m, n, np, nkc, nrt, rpad, uw;   // uw = sum_p W_p (words per row, U layout)
-  int nv;                  // number of V work items of this entry
+  uint8_t* aimg;           // U-stage fp8 A operand images [npc][tb][kABytes], written by the V stage
+  float* cpart;            // U-stage C partial sums [np][kMaxGroups][16], written by the V stage
+  int m, n, np, nkc, nrt, uw;   // uw = sum_p W_p (words per row, U layout)
   int vct[2];              // column tiles per V work item, per path
+  int nvg[2];              // V work items (column groups) per path
   int woff[2];             // word offset of each path inside a U-layout row
+  int pcoff[2];            // first 128-latent chunk of each path in aimg
+  int npc;                 // chunks over both paths
 };
 
-// Work item of the decode kernel: kind 0 = V stage (entry, path, column group),
-// kind 1 = U stage (entry, row group).
+constexpr int kMaxGroups = 32;          // column groups per path (rank <= 4096, >= 8 tiles per group)
+constexpr int kABytes = 2048 + 64;      // one fp8 A operand image: 16 rows x 4 groups x 32 B + scales
+
+// Work item: V stage (entry, path, column group) or U stage (entry, 16 row tiles).
 struct WorkItem {
   uint32_t entry;
-  uint16_t kind_path;      // bit 15: kind, bits 0..14: path
+  uint16_t path;
   uint16_t group;
 };
 
-// Control words of one persistent launch (zero-initialised once, self-resetting).
-struct Control {
-  unsigned int ticket;     // next work item
-  unsigned int done;       // workgroups finished
-  unsigned int gen;        // launches completed
-  unsigned int err;        // nonzero if a bounded wait gave up (never expected)
-};
-
-// Launch-wide arguments of the decode kernel.
+// Launch-wide arguments of the two decode kernels.
 struct DecArgs {
   const DecEntry* entries;
   const void* const* xs;   // per entry input (device array), or null: use x0 / y0
   void* const* ys;         // per entry output
   const void* x0;          // single-entry input when xs is null
   void* y0;
-  const WorkItem* items;
-  unsigned int* counters;  // per entry V-completion counter
-  unsigned int* ready;     // per entry generation flag
-  Control* ctl;
-  int nitems, T, t0;       // tokens in this launch and the offset of its first token
-  int spin_limit;          // polls before a wait gives up (sets ctl->err)
+  const WorkItem* items;   // this kernel's items, one workgroup each
+  int T, t0;               // tokens in this launch and the offset of its first token
 };
 
 // Tokens one decode launch handles (token blocks of 8, at most 2 blocks).
 constexpr int kDecodeMaxTokens = 16;
-constexpr int kDecodeRowTilesPerItem = 16;   // U work item = 256 output rows
-__host__ __device__ inline int decode_ct_max(int tb) { return tb == 1 ? 16 : 8; }
+constexpr int kDecodeRowTilesPerItem = 64;   // U work item = 1024 output rows
+// Token-count bucket of a decode launch (per-token state is sized by it) and the
+// most column tiles one V work item holds at that bucket.
+__host__ __device__ inline int decode_bucket(int T) { return T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : T <= 8 ? 8 : 16; }
+__host__ __device__ inline int decode_ct_max(int T) { return decode_bucket(T) >= 8 ? 8 : 16; }
 
 // ---------------------------------------------------------------------------
 // kernel launchers (defined in the .hip files)
@@ -97,8 +93,8 @@ hipError_t launch_retile_u_decode(const uint32_t* ucan, int m, int r, int W, int
 hipError_t launch_exact(const PathDev* p, int np, int m, int n, const void* x, void* y, int T,
                         int io_fp32, float* zbuf, int rpad, hipStream_t st);
 
-// decode path: persistent fused kernel over a work list
-hipError_t launch_decode(const DecArgs& a, int tb, hipStream_t st);
-int decode_grid_size(int tb);
+// decode path: V-stage kernel then U-stage kernel, one workgroup per work item
+hipError_t launch_decode_v(const DecArgs& a, int nitems, hipStream_t st);
+hipError_t launch_decode_u(const DecArgs& a, int nitems, hipStream_t st);
 
 }  // namespace lb
