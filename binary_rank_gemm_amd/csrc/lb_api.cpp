@@ -498,7 +498,7 @@ lb_status lb_linear_forward_ex(lb_linear L, const void* x, void* y, int64_t toke
   const PrefillLayer* one[1] = {&L->pre};
   const void* xs[1] = {x};
   void* ys[1] = {y};
-  HIP_TRY(prefill_run(L->pplan, one, 1, xs, ys, (int)tokens, st, /*sync_on_rebuild=*/true));
+  HIP_TRY(prefill_run(L->pplan, one, 1, xs, ys, (int)tokens, st, /*single=*/true));
   return LB_OK;
 }
 
@@ -573,7 +573,7 @@ lb_status stack_prepare(lb_stack S, lb_regime rg, int64_t tokens) {
     }
   } else if (rg == LB_REGIME_PREFILL) {
     if (!prefill_available()) return fail(LB_ERR_UNSUPPORTED, "the prefill kernels are not available in this build");
-    HIP_TRY(prefill_prepare(S->pplan, S->pre.data(), count, (int)tokens));
+    HIP_TRY(prefill_prepare(S->pplan, S->pre.data(), count, (int)tokens, S->xs_h.data(), S->ys_h.data()));
   } else {
     size_t want = 0;
     for (lb_linear L : S->linears) {

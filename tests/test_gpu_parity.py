@@ -124,7 +124,7 @@ def onehot_x(n, ks, vals=None):
     return synth.bf16_bits_from_f32(x)
 
 
-@pytest.mark.parametrize("regime", [lb.REGIME_DECODE, lb.REGIME_EXACT])
+@pytest.mark.parametrize("regime", [lb.REGIME_DECODE, lb.REGIME_EXACT, lb.REGIME_PREFILL])
 def test_identity_probe_bit_exact(regime):
     """Unit scales, x = e_k: y = row k of V_p contracted with U_p, summed over
     paths -- integers of magnitude <= r1 + r2 <= 256, exact in bf16."""
@@ -141,7 +141,8 @@ def test_identity_probe_bit_exact(regime):
     assert np.array_equal(to_f64(y), y_ref)
 
 
-def test_decode_power_of_two_scales_bit_exact():
+@pytest.mark.parametrize("regime", [lb.REGIME_DECODE, lb.REGIME_PREFILL])
+def test_power_of_two_scales_bit_exact(regime):
     """Scales in {1, 2} and x in {+-1, +-2} one-hot: |y| <= 256, every step exact."""
     rng = np.random.default_rng(24)
     m, n, ranks = 70, 4000, [10, 6]
@@ -154,9 +155,21 @@ def test_decode_power_of_two_scales_bit_exact():
     x = onehot_x(n, ks, vals=[1, -1, 2, -2, 1, 1, -1, 2, -2, 1, 2])
     y_ref = oracle.forward(x_f64(x), paths, m, n)
     assert np.max(np.abs(y_ref)) <= 256
-    y = build(m, n, paths).forward(x_tensor(x), regime=lb.REGIME_DECODE)
+    y = build(m, n, paths).forward(x_tensor(x), regime=regime)
     torch.cuda.synchronize()
     assert np.array_equal(to_f64(y), y_ref)
+
+
+def test_prefill_identity_probe_many_tokens_bit_exact():
+    """x = I_n (T = n = 640 tokens, spans three 256-row tiles): y = sum_p U_p V_p^T, exact."""
+    m, n, ranks = 700, 640, [90, 70]
+    ones = lambda k: f16bits(np.ones(k))
+    paths = [dict(rank=r, u_words=synth.sign_words((29, p, 0), m, r), v_words=synth.sign_words((29, p, 1), n, r),
+                  h=ones(m), g=ones(n), l=ones(r)) for p, r in enumerate(ranks)]
+    x = synth.bf16_bits_from_f32(np.eye(n, dtype=np.float32))
+    y = build(m, n, paths).forward(x_tensor(x), regime=lb.REGIME_PREFILL)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_f64(y), oracle.forward(x_f64(x), paths, m, n))
 
 
 DECODE_SHAPES = [
@@ -267,3 +280,78 @@ def test_stack_exact_fp32_matches_single():
         torch.cuda.synchronize()
         assert torch.equal(ys[i], single)
         assert_fp32_close(to_f64(ys[i]), oracle.forward(x_f64(xs[i]), paths[i], m, n), f"fp32 stack {i}")
+
+
+# ----------------------------------------------------------------------------
+# prefill path (bf16 MFMA GEMMs)
+# ----------------------------------------------------------------------------
+
+PREFILL_SHAPES = [
+    # m, n, ranks, T
+    (300, 700, [37, 45], 130),           # ragged everything, one row tile
+    (1000, 1200, [149, 102], 300),       # two row tiles, ragged
+    (513, 257, [33, 31], 600),           # n not a multiple of 8: element-wise A loads
+    (4096, 1024, [46, 46], 256),
+    (2000, 300, [600], 129),             # single path
+    (1024, 2048, [704, 704], 512),       # Llama-2-13B-like rank at 0.55 BPW
+]
+
+
+@pytest.mark.parametrize("m,n,ranks,T", PREFILL_SHAPES)
+def test_prefill_parity(m, n, ranks, T):
+    log(f"prefill m={m} n={n} ranks={ranks} T={T}")
+    paths = seeded_paths((30, m, n), m, n, ranks)
+    x = synth.activations((30, T, n), T, n)
+    lin = build(m, n, paths)
+    y = lin.forward(x_tensor(x), regime=lb.REGIME_PREFILL)
+    torch.cuda.synchronize()
+    s = assert_bf16_close(to_f64(y), oracle.forward(x_f64(x), paths, m, n), f"prefill {m}x{n}")
+    log(f"  E_rms={s['erms']:.2e} E_max/rms={s['emax_rel_rms']:.2e}")
+    y2 = lin.forward(x_tensor(x), regime=lb.REGIME_PREFILL)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    # AUTO picks prefill at this token count
+    if T >= lb.PREFILL_MIN_TOKENS:
+        y3 = lin.forward(x_tensor(x))
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y3.view(torch.int16))
+
+
+def test_prefill_token_count_changes():
+    m, n = 400, 520
+    paths = seeded_paths((31, 0, 0), m, n, [40, 24])
+    lin = build(m, n, paths)
+    for T in (200, 513, 128, 1):
+        x = synth.activations((31, T, n), T, n)
+        y = lin.forward(x_tensor(x), regime=lb.REGIME_PREFILL)
+        torch.cuda.synchronize()
+        assert_bf16_close(to_f64(y), oracle.forward(x_f64(x), paths, m, n), f"prefill T={T}")
+
+
+def test_stack_prefill_graph_eager_single_agree():
+    T = 300
+    log(f"stack prefill T={T}")
+    lins, paths, xs = make_stack(32, STACK_SHAPES, T)
+    S = lb.Stack(lins)
+    xd = [x_tensor(x) for x in xs]
+    ys_g = [torch.empty((T, m), dtype=torch.bfloat16, device="cuda") for m, _, _ in STACK_SHAPES]
+    ys_e = [torch.empty_like(y) for y in ys_g]
+    S.forward(xd, ys_e, regime=lb.REGIME_PREFILL, use_graph=False)
+    S.forward(xd, ys_g, regime=lb.REGIME_PREFILL, use_graph=True)
+    torch.cuda.synchronize()
+    for i, (m, n, _) in enumerate(STACK_SHAPES):
+        single = lins[i].forward(xd[i], regime=lb.REGIME_PREFILL)
+        torch.cuda.synchronize()
+        assert torch.equal(ys_g[i].view(torch.int16), ys_e[i].view(torch.int16)), f"graph != eager, entry {i}"
+        assert torch.equal(ys_g[i].view(torch.int16), single.view(torch.int16)), f"stack != single, entry {i}"
+        assert_bf16_close(to_f64(ys_g[i]), oracle.forward(x_f64(xs[i]), paths[i], m, n), f"prefill stack {i}")
+    ref = [y.clone() for y in ys_g]
+    for rep in range(3):
+        for y in ys_g:
+            y.zero_()
+        junk = torch.randn(1000, 1000, device="cuda") @ torch.randn(1000, 1000, device="cuda")
+        S.forward(xd, ys_g, regime=lb.REGIME_PREFILL, use_graph=True)
+        torch.cuda.synchronize()
+        del junk
+        for i in range(len(ys_g)):
+            assert torch.equal(ys_g[i].view(torch.int16), ref[i].view(torch.int16)), f"replay {rep} entry {i}"
