@@ -194,6 +194,7 @@ def main():
     ap.add_argument("--workload", default="cfg5-decode", choices=sorted(WORKLOADS))
     ap.add_argument("--layers", type=int, default=None, help="limit the stack to this many layers (not for reports)")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true", help="time only the prefill stack (for profiling)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="before timing, run one device-to-device copy of this many MiB (a known-size "
@@ -219,6 +220,11 @@ def main():
         del src, dst
         log(f"copy probe: {nb} bytes read + {nb} bytes written")
 
+    if args.prefill_only:
+        p = run_prefill(args, lb, torch, "cfg3-prefill")
+        log(f"prefill: {p['ms_per_step']:.2f} ms/step, {p['tflops']:.0f} TFLOP/s")
+        print(json.dumps({"prefill": p}), flush=True)
+        return
     r = run_decode(args, lb, torch)
     wl, T = r["wl"], r["T"]
     log(f"decode: {r['kern_ms'] * 1e3:.1f} us/step (events), {r['ms'] * 1e3:.1f} us/step (wall), {r['gbps']:.0f} GB/s")

@@ -12,13 +12,15 @@
 // B operand pair is one shift and one bit-field insert of the sign bits into
 // a bf16 pair of magnitudes.
 //
-// Workgroup tile 256 x 256 (4 waves of 128 x 128, 32x32x16 MFMA), K blocks of
-// 64.  A goes global -> registers -> LDS (double buffered, rows padded to 72
-// elements against bank conflicts); B goes from packed bits straight into
-// registers.  Each GEMM is one launch over every tile of every entry, tiles
+// Workgroup tile 256 x 256 (4 waves of 128 x 128, 32x32x16 MFMA, fp32
+// accumulators in AGPRs), K blocks of 64.  A goes global -> registers (two
+// blocks ahead) -> LDS (three buffers, rows padded to 72 elements against bank
+// conflicts), so the next block's first A fragments are read before the
+// barrier that ends a block; B goes from packed bits straight into registers.  Each GEMM is one launch over every tile of every entry, tiles
 // of one (entry, row stripe) placed on one XCD so the stripe is read into one
 // L2.
 #include <algorithm>
+#include <type_traits>
 
 #include "lb_prefill.h"
 #include <hip/hip_fp16.h>
@@ -37,11 +39,6 @@ __device__ inline LB_GLOBAL T* gp(T* p) { return (LB_GLOBAL T*)p; }
 template <class T>
 __device__ inline const LB_GLOBAL T* gp(const T* p) { return (const LB_GLOBAL T*)p; }
 
-constexpr int kThreads = 256;
-constexpr int kLdsRow = kPreBK + 8;                      // padded A row (elements)
-constexpr int kLdsA = kPreBM * kLdsRow * 2;              // bytes per A buffer
-constexpr int kLdsG = 2 * kPreBK * 2;                    // bytes per |g| stage (2 paths)
-constexpr size_t kPreLds = 2 * (size_t)kLdsA + 2 * kLdsG;
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 inline int rup(int v, int m) { return (v + m - 1) / m * m; }
@@ -171,8 +168,44 @@ __device__ inline u32x4 expand_b(uint32_t d, int b, const u32x4& s2) {
   return r;
 }
 
-template <int MODE>
-__global__ void __launch_bounds__(kThreads, 1) k_prefill(PreArgs a) {
+template <int N>
+using Int = std::integral_constant<int, N>;
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(1))) void gbl_void;
+
+// s_waitcnt on the vector-memory counter only (other counters at their maximum),
+// then the workgroup barrier.  The memory clobber keeps the compiler from
+// moving LDS accesses across it.
+template <int VM>
+__device__ inline void vm_wait_barrier() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  constexpr int imm = (VM & 15) | (7 << 4) | (15 << 8) | ((VM >> 4) << 14);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(imm);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// A tile in LDS: 256 rows x 64 bf16, 16-byte chunk c of row r at slot
+// 8 r + (c ^ (r & 7)) (rows unpadded, the XOR spreads the 8 rows read together
+// over all banks).  Slots are filled in order by the direct-to-LDS loads: wave
+// w, instruction i, lane l writes slot 64 (W i + w) + l, W = waves.
+__device__ inline int a_slot_row(int s) { return s >> 3; }
+__device__ inline int a_slot_chunk(int s) { return (s & 7) ^ ((s >> 3) & 7); }
+
+// Wave layout of the 256 x 256 workgroup tile: WM x WN waves, each owning
+// (256 / WM) x (256 / WN) outputs as MB x NB blocks of 32 x 32.  STR (GEMM1
+// only): some wave's columns cross from the primary path into the residual
+// one, so |g| is chosen per column block.
+template <int MODE, int WM, int WN, bool STR>
+__global__ void __launch_bounds__(64 * WM * WN, 1) k_prefill(PreArgs a) {
+  constexpr int kWaves = WM * WN, kNT = 64 * kWaves;
+  constexpr int MB = kPreBM / WM / 32, NB = kPreBN / WN / 32;
+  constexpr int kAI = kPreBM * 8 / kNT;                 // A loads (16 B per lane) per wave per block
+  static_assert(NB == 2 || NB == 4, "a wave covers half or all of a 128-column B tile");
+  static_assert(kWaves >= 3, "waves 0, 1, 2 carry the B words and |g|");
+  static_assert(MODE == 1 || !STR, "only GEMM1 columns span paths");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const PreItem it = a.items[blockIdx.x];
   if (it.entry < 0) return;
@@ -181,159 +214,207 @@ __global__ void __launch_bounds__(kThreads, 1) k_prefill(PreArgs a) {
   const int T = a.T;
   const bool first = it.entry == 0 && a.x0 != nullptr;
   const uint16_t* A;
-  int lda, K, N, kbn;
+  int lda, K, N, kbn, ntiles;
   const uint32_t* Bw;
   uint16_t* C;
   int ldc;
   if (MODE == 1) {
     A = reinterpret_cast<const uint16_t*>(first ? a.x0 : Eg.x);
-    lda = L.n; K = L.n; N = L.Rp; kbn = L.kb1; Bw = L.b1;
+    lda = L.n; K = L.n; N = L.Rp; kbn = L.kb1; Bw = L.b1; ntiles = L.nt1;
     C = Eg.z; ldc = L.Rp;
   } else {
     A = Eg.z;
-    lda = L.Rp; K = L.Rp; N = L.m; kbn = L.kb2; Bw = L.b2;
+    lda = L.Rp; K = L.Rp; N = L.m; kbn = L.kb2; Bw = L.b2; ntiles = L.nt2;
     C = reinterpret_cast<uint16_t*>(first ? a.y0 : Eg.y); ldc = L.m;
   }
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
+  const int wm = wave / WN, wn = wave % WN;
   const int m0 = it.mt * kPreBM, n0 = it.nt * kPreBN;
-  // this wave's B tile; past the last tile (N not a multiple of 256) the loads
-  // are clamped and every column of the wave is discarded in the epilogue
-  const int ntile = min((n0 + wn * kPreWN) / kPreWN, (MODE == 1 ? L.nt1 : L.nt2) - 1);
   const int l32 = lane & 31, kg = lane >> 5;
+  const int wcol = wn * (NB * 32);                       // first column of this wave in the tile
+  const int bb0 = (wcol & (kPreWN - 1)) / 32;            // first 32-column block inside its B tile
   const bool vec_ok = (lda & 7) == 0;
   const int nkb = (K + kPreBK - 1) / kPreBK;
 
-  uint16_t* As = reinterpret_cast<uint16_t*>(lds);                 // [2][256][72]
-  uint16_t* Gs = reinterpret_cast<uint16_t*>(lds + 2 * kLdsA);     // [2][2 paths][64]
+  // LDS, three buffers of: A [256 x 64] bf16 (swizzled) | B words [2 tiles][64 lanes] u32x4 | |g| [2][64] bf16
+  constexpr int kBufA = kPreBM * kPreBK * 2, kBufB = 2 * 64 * 16, kBufG = 2 * kPreBK * 2;
+  constexpr int kBuf = kBufA + kBufB + kBufG;
 
-  // ---- global -> register staging of one A block (8 x 16 B per thread) and |g|
-  u32x4 areg[8];
-  uint32_t greg = 0;
-  auto load_a = [&](int kb) {
+  // ---- block loads: rows past T are clamped onto row T - 1 (a row of A only
+  // reaches the same output row, which is not stored)
+  const LB_GLOBAL uint16_t* asrc[kAI];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = tid + kThreads * i;
-      const int row = m0 + (c >> 3), k = kb * kPreBK + (c & 7) * 8;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (row < T) {
-        const LB_GLOBAL uint16_t* src = gp(A) + (int64_t)row * lda + k;
-        if (vec_ok && k + 8 <= K) {
-          v = *reinterpret_cast<const LB_GLOBAL u32x4*>(src);
-        } else {
-          uint32_t e[8];
-#pragma unroll
-          for (int q = 0; q < 8; ++q) e[q] = k + q < K ? src[q] : 0u;
-          v = u32x4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
-        }
-      }
-      areg[i] = v;
-    }
-    if (MODE == 1 && tid < 64) {   // |g| of both paths for this K block, as bf16 pairs
-      const int p = tid >> 5, k2 = (tid & 31) * 2;
-      greg = *reinterpret_cast<const LB_GLOBAL uint32_t*>(gp(L.gabs) + (int64_t)p * L.kb1 * kPreBK + kb * kPreBK + k2);
-    }
-  };
-  auto store_a = [&](int buf) {
-    uint16_t* dst = As + buf * (kPreBM * kLdsRow);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = tid + kThreads * i;
-      *reinterpret_cast<u32x4*>(dst + (c >> 3) * kLdsRow + (c & 7) * 8) = areg[i];
-    }
-    if (MODE == 1 && tid < 64) *reinterpret_cast<uint32_t*>(Gs + buf * 2 * kPreBK + tid * 2) = greg;
-  };
-  // ---- B words: one dword per K step, 4 steps per K block
-  const LB_GLOBAL u32x4* bsrc = reinterpret_cast<const LB_GLOBAL u32x4*>(gp(Bw)) + (int64_t)ntile * kbn * 64 + lane;
-  auto load_b = [&](int kb) { return bsrc[(int64_t)kb * 64]; };
-
-  // ---- scales that do not change along K (GEMM2: |h| of this lane's columns)
-  u32x4 h2[2];
-  int bpath[4];
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const int col = n0 + wn * kPreWN + 32 * b;   // first column of block b
-    bpath[b] = (MODE == 1 && L.np > 1 && col >= L.roff[1]) ? 1 : 0;
+  for (int i = 0; i < kAI; ++i) {
+    const int s = 64 * (kWaves * i + wave) + lane;
+    asrc[i] = gp(A) + (int64_t)min(m0 + a_slot_row(s), T - 1) * lda + a_slot_chunk(s) * 8;
   }
+  const int btile = min(2 * it.nt + (wave & 1), ntiles - 1);
+  const LB_GLOBAL u32x4* bsrc = reinterpret_cast<const LB_GLOBAL u32x4*>(gp(Bw)) + (int64_t)btile * kbn * 64 + lane;
+  const LB_GLOBAL uint32_t* gsrc =
+      reinterpret_cast<const LB_GLOBAL uint32_t*>(gp(L.gabs) + (int64_t)(lane >> 5) * L.kb1 * kPreBK + l32 * 2);
+  // Issues block kb into LDS buffer buf.  Full blocks of 16-byte aligned rows
+  // go straight to LDS (the B / |g| load first, so that a wait for "all but
+  // the last kAI" covers it); a ragged or unaligned block goes through
+  // registers with zero fill past K, synchronously.
+  auto issue = [&](int kb, int buf) {
+    uint8_t* base = lds + buf * kBuf;
+    const int k0 = kb * kPreBK;
+    if (wave < 2)
+      __builtin_amdgcn_global_load_lds((gbl_void*)(bsrc + (int64_t)kb * 64), (lds_void*)(base + kBufA + wave * 1024), 16, 0, 0);
+    else if (MODE == 1 && wave == 2)
+      __builtin_amdgcn_global_load_lds((gbl_void*)(gsrc + k0 / 2), (lds_void*)(base + kBufA + kBufB), 4, 0, 0);
+    if (vec_ok && k0 + kPreBK <= K) {
+#pragma unroll
+      for (int i = 0; i < kAI; ++i)
+        __builtin_amdgcn_global_load_lds((gbl_void*)(asrc[i] + k0), (lds_void*)(base + (kWaves * i + wave) * 1024), 16, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kAI; ++i) {
+        const int s = 64 * (kWaves * i + wave) + lane;
+        const int k = k0 + a_slot_chunk(s) * 8;
+        uint32_t e[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) e[q] = k + q < K ? asrc[i][k0 + q] : 0u;
+        *reinterpret_cast<u32x4*>(base + s * 16) =
+            u32x4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
+      }
+    }
+  };
+  // A fragment of row block mb, K step ks: row R = wm 128 + 32 mb + l32,
+  // chunk 2 ks + kg; R & 7 == l32 & 7
+  int aoff[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) aoff[ks] = (wm * MB * 32 + l32) * 128 + (((2 * ks + kg) ^ (l32 & 7)) * 16);
+  auto read_a = [&](int buf, int ks, u32x4* af) {
+    const uint8_t* Ab = lds + buf * kBuf + aoff[ks];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) af[mb] = *reinterpret_cast<const u32x4*>(Ab + mb * 32 * 128);
+  };
+  const int bsel = wcol / kPreWN;                        // which of the two B tiles
+  auto read_b = [&](int buf) { return reinterpret_cast<const u32x4*>(lds + buf * kBuf + kBufA)[bsel * 64 + lane]; };
+
+  // ---- B magnitudes.  GEMM1: |g| of the path of the wave's columns (per
+  // column block when STR), per K step from LDS.  GEMM2: |h| of each column,
+  // fixed along K, one set per path, chosen per K step.
+  bool bpath[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) bpath[b] = MODE == 1 && L.np > 1 && n0 + wcol + (STR ? 32 * b : 0) >= L.roff[1];
+  auto read_g = [&](int buf, int ks, bool path1) {
+    return *reinterpret_cast<const u32x4*>(lds + buf * kBuf + kBufA + kBufB + (path1 ? kPreBK * 2 : 0) + 16 * kg + 32 * ks);
+  };
+  uint32_t h0[NB], h1[NB];
   if (MODE == 2) {
+    const int tile = min((n0 + wcol) / kPreWN, ntiles - 1);
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const uint32_t h = gp(L.habs)[(int64_t)p * L.nt2 * kPreWN + ntile * kPreWN + 32 * b + l32];
-        h2[p][b] = h | (h << 16);
-      }
+    for (int b = 0; b < NB; ++b) {
+      const int64_t i = (int64_t)tile * kPreWN + 32 * (bb0 + b) + l32;
+      const uint32_t x0 = gp(L.habs)[i], x1 = gp(L.habs)[(int64_t)L.nt2 * kPreWN + i];
+      h0[b] = x0 | (x0 << 16);
+      h1[b] = x1 | (x1 << 16);
+    }
   }
+  // B operands of one K step: sign bits d (one word per step), magnitudes
+  // gc (GEMM1, path of block 0) / gs (GEMM1, the other path; STR only) / the
+  // GEMM2 path of the step
+  auto make_b = [&](uint32_t d, const u32x4& gc, const u32x4& gs, bool kp, u32x4* bf) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      u32x4 sc;
+      if (MODE == 1) {
+        sc = (STR && bpath[b] != bpath[0]) ? gs : gc;
+      } else {
+        const uint32_t h = kp ? h1[b] : h0[b];
+        sc = u32x4{h, h, h, h};
+      }
+      bf[b] = expand_b(d, bb0 + b, sc);
+    }
+  };
+  auto kpath = [&](int kb, int ks) { return MODE == 2 && L.np > 1 && kb * kPreBK + ks * 16 >= L.roff[1]; };
 
-  v16f acc[4][4];
+  v16f acc[MB][NB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-  load_a(0);
-  u32x4 bcur = load_b(0), bnxt = bcur;
-  store_a(0);
-  __syncthreads();
+  // Pipeline over three LDS buffers: block kb + 2 is issued at the start of
+  // block kb (into the buffer block kb - 1 used), and the barrier that ends
+  // block kb waits for this wave's loads of block kb + 1 first.  Inside a
+  // block, K step ks multiplies while the A fragments and B operands of step
+  // ks + 1 are read and expanded (for ks = 3: step 0 of the next block, whose
+  // buffer is complete since the previous barrier; past the last block the
+  // buffer is stale and the result unused).
+  issue(0, 0);
+  if (nkb > 1) issue(1, 1);
+  vm_wait_barrier<0>();
+  u32x4 af[2][MB], bf[2][NB];
+  read_a(0, 0, af[0]);
+  u32x4 bw = read_b(0);
+  {
+    const u32x4 g0 = MODE == 1 ? read_g(0, 0, bpath[0]) : u32x4{};
+    const u32x4 g1 = (MODE == 1 && STR) ? read_g(0, 0, !bpath[0]) : u32x4{};
+    make_b(bw[0], g0, g1, kpath(0, 0), bf[0]);
+  }
+
   for (int kb = 0; kb < nkb; ++kb) {
-    const int cur = kb & 1;
-    if (kb + 1 < nkb) {
-      load_a(kb + 1);
-      bnxt = load_b(kb + 1);
-    }
-    const uint16_t* Ab = As + cur * (kPreBM * kLdsRow) + (wm * 128 + l32) * kLdsRow + 8 * kg;
+    const int cur = kb % 3, nxt = (kb + 1) % 3;
+    const bool more = kb + 2 < nkb;
+    if (more) issue(kb + 2, (kb + 2) % 3);
+    const u32x4 bwn = read_b(nxt);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      u32x4 af[4];
+      const int rb = ks < 3 ? cur : nxt, rks = (ks + 1) & 3;
+      read_a(rb, rks, af[(ks + 1) & 1]);
+      const uint32_t dn = ks < 3 ? bw[ks + 1] : bwn[0];
+      const u32x4 g0 = MODE == 1 ? read_g(rb, rks, bpath[0]) : u32x4{};
+      const u32x4 g1 = (MODE == 1 && STR) ? read_g(rb, rks, !bpath[0]) : u32x4{};
+      make_b(dn, g0, g1, kpath(ks < 3 ? kb : kb + 1, rks), bf[(ks + 1) & 1]);
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) af[mb] = *reinterpret_cast<const u32x4*>(Ab + mb * 32 * kLdsRow + ks * 16);
-      const uint32_t d = bcur[ks];
-      u32x4 s2[2];
-      if (MODE == 1) {
+      for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int p = 0; p < 2; ++p)
-          s2[p] = *reinterpret_cast<const u32x4*>(Gs + cur * 2 * kPreBK + p * kPreBK + ks * 16 + 8 * kg);
-      }
-      const int kpath = (MODE == 2 && L.np > 1 && kb * kPreBK + ks * 16 >= L.roff[1]) ? 1 : 0;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        u32x4 sc;
-        if (MODE == 1) sc = bpath[b] ? s2[1] : s2[0];
-        else {
-          const uint32_t h = kpath ? h2[1][b] : h2[0][b];
-          sc = u32x4{h, h, h, h};
-        }
-        const u32x4 bf = expand_b(d, b, sc);
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) acc[mb][b] = mfma32(af[mb], bf, acc[mb][b]);
-      }
+        for (int mb = 0; mb < MB; ++mb) acc[mb][b] = mfma32(af[ks & 1][mb], bf[ks & 1][b], acc[mb][b]);
     }
-    if (kb + 1 < nkb) {
-      store_a(cur ^ 1);
-      bcur = bnxt;
-    }
-    __syncthreads();
+    bw = bwn;
+    if (more) vm_wait_barrier<kAI>();
+    else vm_wait_barrier<0>();
   }
 
   // ---- epilogue: lane holds D[8 (q/4) + 4 kg + q%4][l32] of each 32x32 block
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const int col = n0 + wn * kPreWN + 32 * b + l32;
+  for (int b = 0; b < NB; ++b) {
+    const int col = n0 + wcol + 32 * b + l32;
     if (col < N) {
       const float ls = MODE == 1 ? gp(L.lpad)[col] : 1.f;
       LB_GLOBAL uint16_t* cp = gp(C) + col;
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
-          const int row = m0 + wm * 128 + mb * 32 + 8 * (q >> 2) + 4 * kg + (q & 3);
+          const int row = m0 + wm * MB * 32 + mb * 32 + 8 * (q >> 2) + 4 * kg + (q & 3);
           if (row < T) cp[(int64_t)row * ldc] = f32_to_bf16_rne(acc[mb][b][q] * ls);
         }
     }
   }
 }
+
+// wave layout of the prefill GEMMs
+constexpr int kPreWM = 2, kPreWNv = 2;
+constexpr int kWaveCols = kPreBN / kPreWNv;
+
+// true when a wave of GEMM1 tile nt has columns of both paths
+bool tile_straddles(const PrefillLayer& L, int nt) {
+  if (L.np < 2) return false;
+  for (int w = 0; w < kPreWNv; ++w) {
+    const int c0 = nt * kPreBN + w * kWaveCols;
+    if (c0 < L.roff[1] && c0 + kWaveCols - 32 >= L.roff[1]) return true;
+  }
+  return false;
+}
+constexpr int kThreads = 64 * kPreWM * kPreWNv;
+constexpr size_t kPreLds = 3 * (size_t)(kPreBM * kPreBK * 2 + 2 * 64 * 16 + 2 * kPreBK * 2);
 
 }  // namespace
 
@@ -445,7 +526,7 @@ std::vector<PreItem> xcd_order(const std::vector<std::vector<PreItem>>& stripes)
 hipError_t prefill_prepare(PrefillPlan& P, const PrefillLayer* const* layers, int count, int T,
                            const void* const* xs, void* const* ys) {
   const int mts = (T + kPreBM - 1) / kPreBM;
-  std::vector<std::vector<PreItem>> s1, s2;
+  std::vector<std::vector<PreItem>> s1, s1s, s2;
   size_t zoff = 0;
   std::vector<size_t> zoffs(count);
   P.entries_h.assign(count, PreEntry{});
@@ -456,14 +537,15 @@ hipError_t prefill_prepare(PrefillPlan& P, const PrefillLayer* const* layers, in
     zoff += align256((size_t)T * L.Rp * 2);
     const int nt1 = (L.Rp + kPreBN - 1) / kPreBN, nt2 = (L.m + kPreBN - 1) / kPreBN;
     for (int mt = 0; mt < mts; ++mt) {
-      std::vector<PreItem> a, b;
-      for (int nt = 0; nt < nt1; ++nt) a.push_back(PreItem{e, mt, nt});
+      std::vector<PreItem> a, as, b;
+      for (int nt = 0; nt < nt1; ++nt) (tile_straddles(L, nt) ? as : a).push_back(PreItem{e, mt, nt});
       for (int nt = 0; nt < nt2; ++nt) b.push_back(PreItem{e, mt, nt});
       s1.push_back(a);
+      if (!as.empty()) s1s.push_back(as);
       s2.push_back(b);
     }
   }
-  std::vector<PreItem> i1 = xcd_order(s1), i2 = xcd_order(s2);
+  std::vector<PreItem> i1 = xcd_order(s1), i1s = xcd_order(s1s), i2 = xcd_order(s2);
   if (zoff > P.zbytes) {
     if (P.zbuf) {
       hipError_t e = hipFree(P.zbuf);
@@ -485,13 +567,15 @@ hipError_t prefill_prepare(PrefillPlan& P, const PrefillLayer* const* layers, in
   P.entries_d = nullptr;
   P.items_d = nullptr;
   hipError_t e = hipMalloc(&P.entries_d, count * sizeof(PreEntry));
-  if (e == hipSuccess) e = hipMalloc(&P.items_d, (i1.size() + i2.size()) * sizeof(PreItem));
+  if (e == hipSuccess) e = hipMalloc(&P.items_d, (i1.size() + i1s.size() + i2.size()) * sizeof(PreItem));
   if (e == hipSuccess) e = hipMemcpy(P.entries_d, P.entries_h.data(), count * sizeof(PreEntry), hipMemcpyHostToDevice);
   if (e != hipSuccess) return e;
   std::vector<PreItem> all(i1);
+  all.insert(all.end(), i1s.begin(), i1s.end());
   all.insert(all.end(), i2.begin(), i2.end());
   if ((e = hipMemcpy(P.items_d, all.data(), all.size() * sizeof(PreItem), hipMemcpyHostToDevice)) != hipSuccess) return e;
   P.n1 = (int)i1.size();
+  P.n1s = (int)i1s.size();
   P.n2 = (int)i2.size();
   P.T = T;
   P.count = count;
@@ -519,11 +603,14 @@ hipError_t prefill_run(PrefillPlan& P, const PrefillLayer* const* layers, int co
   a.entries = P.entries_d;
   a.T = T;
   a.items = P.items_d;
-  hipLaunchKernelGGL(k_prefill<1>, dim3(P.n1), dim3(kThreads), kPreLds, st, a);
+  if (P.n1 > 0) hipLaunchKernelGGL((k_prefill<1, kPreWM, kPreWNv, false>), dim3(P.n1), dim3(kThreads), kPreLds, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   a.items = P.items_d + P.n1;
-  hipLaunchKernelGGL(k_prefill<2>, dim3(P.n2), dim3(kThreads), kPreLds, st, a);
+  if (P.n1s > 0) hipLaunchKernelGGL((k_prefill<1, kPreWM, kPreWNv, true>), dim3(P.n1s), dim3(kThreads), kPreLds, st, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  a.items = P.items_d + P.n1 + P.n1s;
+  hipLaunchKernelGGL((k_prefill<2, kPreWM, kPreWNv, false>), dim3(P.n2), dim3(kThreads), kPreLds, st, a);
   return hipGetLastError();
 }
 
