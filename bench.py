@@ -4,8 +4,9 @@
 Default workload: the Llama-2-70B-shaped stack at 0.1 sign bits per weight
 (80 layers x {q, k, v, o, gate, up, down}, both paths, 560 linears, 0.91 GB
 of packed signs + fp16 scales), decode at batch 1, run as one lb_stack_forward
-per step (HIP graph replay of the persistent decode kernel).  Inputs are
-seeded synthetic data resident in HBM before timing starts.
+per step (HIP graph replay of the two decode kernels, V stage then U stage,
+each over every linear of the stack).  Inputs are seeded synthetic data
+resident in HBM before timing starts.
 
 Prints one JSON line: the decode step's microseconds per token and achieved
 HBM GB/s (algorithmic bytes), the roofline of the dominant kernel, the
@@ -246,8 +247,10 @@ def main():
                    "tokens": T, "linears": wl.count, "ranks": {s.name: r["ranks_of"][j][0] for j, s in enumerate(wl.mats)}},
         "hbm_gbps": round(r["gbps"], 1),
         "hbm_frac": round(r["gbps"] / HBM_PEAK_GBPS, 4),
+        "step_us_p10_p50_p90": [round(float(np.percentile(r["per"], q)) * 1e3, 2) for q in (10, 50, 90)],
         "roofline": {
-            "bound": "hbm", "kernel": "k_decode (persistent, whole stack per launch)",
+            "bound": "hbm",
+            "kernel": "decode step: k_decode_v then k_decode_u over all linears (one graph launch)",
             "achieved": round(r["gbps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(r["gbps"] / HBM_PEAK_GBPS, 4),
             "traffic": read_traffic("lb_decode.hip", args.workload),

@@ -13,12 +13,13 @@
 // a bf16 pair of magnitudes.
 //
 // Workgroup tile 256 x 256 (4 waves of 128 x 128, 32x32x16 MFMA, fp32
-// accumulators in AGPRs), K blocks of 64.  A goes global -> registers (two
-// blocks ahead) -> LDS (three buffers, rows padded to 72 elements against bank
-// conflicts), so the next block's first A fragments are read before the
-// barrier that ends a block; B goes from packed bits straight into registers.  Each GEMM is one launch over every tile of every entry, tiles
-// of one (entry, row stripe) placed on one XCD so the stripe is read into one
-// L2.
+// accumulators in AGPRs), K blocks of 64.  A, the packed B words and |g| go
+// from global memory straight into LDS (four buffers, loads issued three
+// blocks ahead; A rows unpadded with an XOR swizzle of their 16-byte chunks
+// against bank conflicts); B operands are expanded from the sign bits in
+// registers one K step ahead of the MFMAs that use them.  Each GEMM is one
+// launch over every tile of every entry, tiles of one (entry, row stripe)
+// placed on one XCD so the stripe is read into one L2.
 #include <algorithm>
 #include <type_traits>
 
@@ -171,16 +172,19 @@ __device__ inline u32x4 expand_b(uint32_t d, int b, const u32x4& s2) {
 template <int N>
 using Int = std::integral_constant<int, N>;
 
+constexpr int kPreBufs = 4;                              // LDS buffers of the K-block pipeline
+
 typedef __attribute__((address_space(3))) void lds_void;
 typedef const __attribute__((address_space(1))) void gbl_void;
 
-// s_waitcnt on the vector-memory counter only (other counters at their maximum),
-// then the workgroup barrier.  The memory clobber keeps the compiler from
-// moving LDS accesses across it.
+// Waits until at most VM vector-memory operations of this wave are
+// outstanding and all of its LDS reads have returned, then the workgroup
+// barrier.  The memory clobbers keep the compiler from moving LDS accesses
+// across it.
 template <int VM>
 __device__ inline void vm_wait_barrier() {
   static_assert(VM >= 0 && VM < 64, "vmcnt range");
-  constexpr int imm = (VM & 15) | (7 << 4) | (15 << 8) | ((VM >> 4) << 14);
+  constexpr int imm = (VM & 15) | (7 << 4) | (0 << 8) | ((VM >> 4) << 14);
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(imm);
   __builtin_amdgcn_s_barrier();
@@ -237,7 +241,7 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_prefill(PreArgs a) {
   const bool vec_ok = (lda & 7) == 0;
   const int nkb = (K + kPreBK - 1) / kPreBK;
 
-  // LDS, three buffers of: A [256 x 64] bf16 (swizzled) | B words [2 tiles][64 lanes] u32x4 | |g| [2][64] bf16
+  // LDS, kPreBufs buffers of: A [256 x 64] bf16 (swizzled) | B words [2 tiles][64 lanes] u32x4 | |g| [2][64] bf16
   constexpr int kBufA = kPreBM * kPreBK * 2, kBufB = 2 * 64 * 16, kBufG = 2 * kPreBK * 2;
   constexpr int kBuf = kBufA + kBufB + kBufG;
 
@@ -340,16 +344,22 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_prefill(PreArgs a) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-  // Pipeline over three LDS buffers: block kb + 2 is issued at the start of
+  // Pipeline over four LDS buffers: block kb + 3 is issued at the start of
   // block kb (into the buffer block kb - 1 used), and the barrier that ends
-  // block kb waits for this wave's loads of block kb + 1 first.  Inside a
+  // block kb waits for this wave's loads of block kb + 2 first, so both the
+  // current and the next block are complete in LDS during a block.  Inside a
   // block, K step ks multiplies while the A fragments and B operands of step
   // ks + 1 are read and expanded (for ks = 3: step 0 of the next block, whose
   // buffer is complete since the previous barrier; past the last block the
   // buffer is stale and the result unused).
   issue(0, 0);
   if (nkb > 1) issue(1, 1);
-  vm_wait_barrier<0>();
+  if (nkb > 2) {
+    issue(2, 2);
+    vm_wait_barrier<kAI>();
+  } else {
+    vm_wait_barrier<0>();
+  }
   u32x4 af[2][MB], bf[2][NB];
   read_a(0, 0, af[0]);
   u32x4 bw = read_b(0);
@@ -360,9 +370,9 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_prefill(PreArgs a) {
   }
 
   for (int kb = 0; kb < nkb; ++kb) {
-    const int cur = kb % 3, nxt = (kb + 1) % 3;
-    const bool more = kb + 2 < nkb;
-    if (more) issue(kb + 2, (kb + 2) % 3);
+    const int cur = kb & 3, nxt = (kb + 1) & 3;
+    const bool more = kb + 3 < nkb;
+    if (more) issue(kb + 3, (kb + 3) & 3);
     const u32x4 bwn = read_b(nxt);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -414,7 +424,7 @@ bool tile_straddles(const PrefillLayer& L, int nt) {
   return false;
 }
 constexpr int kThreads = 64 * kPreWM * kPreWNv;
-constexpr size_t kPreLds = 3 * (size_t)(kPreBM * kPreBK * 2 + 2 * 64 * 16 + 2 * kPreBK * 2);
+constexpr size_t kPreLds = kPreBufs * (size_t)(kPreBM * kPreBK * 2 + 2 * 64 * 16 + 2 * kPreBK * 2);
 
 }  // namespace
 

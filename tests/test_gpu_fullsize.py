@@ -1,0 +1,80 @@
+"""Full-size parity: whole layers of the benchmark stacks at their real shapes,
+run the way the benchmark runs them (one stack forward, HIP graph, the
+benchmark's regime), checked against the oracle on a seeded sample of output
+channels for every token (the oracle forms only the sampled rows of W).
+
+Workloads (shapes of "LittleBit: Ultra Low-Bit Quantization via Latent
+Factorization", experiments section: Llama-2 7B / 13B / 70B and Llama-3 8B
+linears; ranks from the sign-bit budget): decode at batch 1, 8, 16, 64 and
+prefill at 2048 tokens.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import binary_rank_gemm_amd as lb
+import oracle
+import synth
+from lbtest import assert_bf16_close, log, to_f64, x_f64, x_tensor
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+SAMPLE_ROWS = 48
+
+# (workload, tokens, regime, layers checked)
+CASES = [
+    ("llama2-70b-0.1bpw", 1, "decode", (0, 79)),
+    ("llama2-70b-0.1bpw", 8, "decode", (41,)),
+    ("llama2-70b-0.1bpw", 64, "decode", (7,)),
+    ("llama2-7b-0.1bpw", 1, "decode", (0, 31)),
+    ("llama3-8b-0.3bpw", 16, "decode", (3,)),
+    ("llama3-8b-0.3bpw", 2048, "prefill", (0,)),
+    ("llama2-13b-0.55bpw", 2048, "prefill", (39,)),
+]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _needs_gpu(gpu):
+    return gpu
+
+
+def ranks(wl, spec):
+    if wl.bpw is None:
+        return [wl.fixed_rank, wl.fixed_rank]
+    r = oracle.rank_for_bpw(spec.m, spec.n, Fraction(wl.bpw), spec.rank_mult)
+    return [r, r]
+
+
+@pytest.mark.parametrize("name,T,regime,layers", CASES, ids=[f"{c[0]}-T{c[1]}-{c[2]}" for c in CASES])
+def test_full_size_layers_sampled(name, T, regime, layers):
+    wl = synth.WORKLOADS[name]
+    reg = {"decode": lb.REGIME_DECODE, "prefill": lb.REGIME_PREFILL}[regime]
+    entries = []
+    for l in layers:
+        for j, s in enumerate(wl.mats):
+            entries.append((l, j, s, synth.layer_tensors(wl.wid, l, j, s.m, s.n, ranks(wl, s)),
+                            synth.layer_activations(wl, l, j, s.n, T, io="bf16")))
+    log(f"{name} T={T} {regime}: {len(entries)} linears")
+    lins = [lb.Linear.from_numpy(s.m, s.n, p) for _, _, s, p, _ in entries]
+    S = lb.Stack(lins)
+    xd = [x_tensor(x) for *_, x in entries]
+    ys = [torch.empty((T, s.m), dtype=torch.bfloat16, device="cuda") for _, _, s, _, _ in entries]
+    S.forward(xd, ys, regime=reg, use_graph=True)
+    torch.cuda.synchronize()
+    first = [y.clone() for y in ys]
+    for rep in range(3):                              # replays of the captured graph: bit-identical
+        S.forward(xd, ys, regime=reg, use_graph=True)
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(first, ys)):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"replay {rep}, entry {i} differs"
+    rng = np.random.default_rng(T * 1000 + layers[0])
+    for (l, j, s, p, x), y in zip(entries, ys):
+        rows = np.sort(rng.choice(s.m, size=min(SAMPLE_ROWS, s.m), replace=False))
+        ref = oracle.forward_rows(x_f64(x), p, s.m, s.n, rows)
+        got = to_f64(y)[:, rows]
+        st = assert_bf16_close(got, ref, f"{name} layer {l} {s.name} T={T}")
+        log(f"  layer {l} {s.name:5s} {s.m}x{s.n} r={p[0]['rank']}: E_rms {st['erms']:.2e} "
+            f"E_max/rms {st['emax_rel_rms']:.2e}")

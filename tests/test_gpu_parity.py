@@ -294,6 +294,7 @@ PREFILL_SHAPES = [
     (4096, 1024, [46, 46], 256),
     (2000, 300, [600], 129),             # single path
     (1024, 2048, [704, 704], 512),       # Llama-2-13B-like rank at 0.55 BPW
+    (4096, 14336, [478, 478], 256),      # long K: many blocks through the LDS pipeline
 ]
 
 
@@ -307,9 +308,10 @@ def test_prefill_parity(m, n, ranks, T):
     torch.cuda.synchronize()
     s = assert_bf16_close(to_f64(y), oracle.forward(x_f64(x), paths, m, n), f"prefill {m}x{n}")
     log(f"  E_rms={s['erms']:.2e} E_max/rms={s['emax_rel_rms']:.2e}")
-    y2 = lin.forward(x_tensor(x), regime=lb.REGIME_PREFILL)
-    torch.cuda.synchronize()
-    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    for _ in range(4):   # deterministic: repeated runs are bit-identical
+        y2 = lin.forward(x_tensor(x), regime=lb.REGIME_PREFILL)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
     # AUTO picks prefill at this token count
     if T >= lb.PREFILL_MIN_TOKENS:
         y3 = lin.forward(x_tensor(x))
