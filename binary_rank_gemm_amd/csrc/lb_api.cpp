@@ -92,13 +92,17 @@ struct DecodePlan {
   int count = 0;
   std::vector<DecEntry> entries_h;
   DecEntry* entries_d = nullptr;
-  WorkItem* items_d = nullptr;    // V items then U items, each longest first
+  WorkItem* items_d = nullptr;    // V items, longest first
+  UItem* uitems_d = nullptr;      // U items: balanced contiguous runs of quads
   int nv_items = 0, nu_items = 0;
+  size_t u_lds = 0;               // dynamic LDS of the U-stage launch
+  uint16_t* sink = nullptr;       // U-stage stores of lanes without an output land here
   Scratch work;                   // U-stage A images and correction sums of every entry
   void release() {
     if (entries_d) (void)hipFree(entries_d);
     if (items_d) (void)hipFree(items_d);
-    entries_d = nullptr; items_d = nullptr;
+    if (uitems_d) (void)hipFree(uitems_d);
+    entries_d = nullptr; items_d = nullptr; uitems_d = nullptr;
     work.release();
     T = -1;
     count = 0;
@@ -174,7 +178,7 @@ lb_status build_decode_plan(DecodePlan& P, const lb_linear* L, int count, int T)
   const int tb = (T + 7) / 8;
   const int ctm = decode_ct_max(T);
   P.entries_h.assign(count, DecEntry{});
-  std::vector<std::pair<double, WorkItem>> vitems, uitems;
+  std::vector<std::pair<double, WorkItem>> vitems;
   size_t work_bytes = 0;
   std::vector<size_t> img_off(count), cp_off(count);
   for (int e = 0; e < count; ++e) {
@@ -213,29 +217,65 @@ lb_status build_decode_plan(DecodePlan& P, const lb_linear* L, int count, int T)
     work_bytes += align256((size_t)E.npc * tb * kABytes);
     cp_off[e] = work_bytes;
     work_bytes += align256((size_t)E.np * kMaxGroups * 16 * sizeof(float));
-    const int nrg = (E.nrt + kDecodeRowTilesPerItem - 1) / kDecodeRowTilesPerItem;
-    for (int g = 0; g < nrg; ++g) {
-      const int rts = std::min(kDecodeRowTilesPerItem, E.nrt - g * kDecodeRowTilesPerItem);
-      const double cost = (double)rts * E.uw / 4.0 + 4.0;
-      uitems.push_back({cost, WorkItem{(uint32_t)e, (uint16_t)0, (uint16_t)g}});
-    }
   }
-  const std::vector<WorkItem> vlist = longest_first(vitems), ulist = longest_first(uitems);
-  std::vector<WorkItem> all(vlist);  // U items follow V items in one array
-  all.insert(all.end(), ulist.begin(), ulist.end());
+  // U items: the quads of all entries in order, cut into runs of equal cost (one
+  // 1 KB step per quad and 128-latent unit, plus the row-scale step of each
+  // batch), one run per workgroup slot of the machine
+  std::vector<UItem> ulist;
+  {
+    const int bq = decode_u_quads_per_item(decode_bucket(T));      // quads of one workgroup batch
+    double total = 0;
+    for (const DecEntry& E : P.entries_h) total += ((E.nrt + 3) / 4) * (E.npc + 1.0 / bq);
+    const double target = std::max(1.0, total / (decode_u_slots() * kDecodeUItemsPerSlot));
+    double acc = 0;
+    UItem cur{0, 0, 0, 0};
+    bool open = false;
+    for (int e = 0; e < count; ++e) {
+      const DecEntry& E = P.entries_h[e];
+      const int nq = (E.nrt + 3) / 4;
+      const double per = E.npc + 1.0 / bq;
+      for (int q = 0; q < nq; q += bq) {
+        const int n = std::min(bq, nq - q);
+        if (!open) {
+          cur = UItem{(uint32_t)e, (uint32_t)q, 0, 0};
+          open = true;
+        }
+        cur.count += n;
+        acc += n * per;
+        if (acc >= target) {
+          ulist.push_back(cur);
+          open = false;
+          acc = 0;
+        }
+      }
+    }
+    if (open) ulist.push_back(cur);
+  }
+  const std::vector<WorkItem> vlist = longest_first(vitems);
+  std::vector<WorkItem> all(vlist);
   // device buffers (callers synchronised with earlier launches before a rebuild)
-  HIP_TRY(P.work.ensure(std::max<size_t>(work_bytes, 256)));
+  const size_t sink_off = work_bytes;              // U-stage sink: 256 B per wave of every item
+  work_bytes += align256((size_t)std::max<size_t>(ulist.size(), 1) * kWavesPerGroup * 256);
+  work_bytes += kDmaPad;   // operand images are read in whole 1 KB pieces
+  HIP_TRY(P.work.ensure(work_bytes));
   for (int e = 0; e < count; ++e) {
     P.entries_h[e].aimg = reinterpret_cast<uint8_t*>(P.work.ptr) + img_off[e];
     P.entries_h[e].cpart = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(P.work.ptr) + cp_off[e]);
   }
   if (P.entries_d) HIP_TRY(hipFree(P.entries_d));
   if (P.items_d) HIP_TRY(hipFree(P.items_d));
-  P.entries_d = nullptr; P.items_d = nullptr;
+  if (P.uitems_d) HIP_TRY(hipFree(P.uitems_d));
+  P.entries_d = nullptr; P.items_d = nullptr; P.uitems_d = nullptr;
   HIP_TRY(hipMalloc(&P.entries_d, count * sizeof(DecEntry)));
   HIP_TRY(hipMalloc(&P.items_d, std::max<size_t>(all.size(), 1) * sizeof(WorkItem)));
+  HIP_TRY(hipMalloc(&P.uitems_d, std::max<size_t>(ulist.size(), 1) * sizeof(UItem)));
   HIP_TRY(hipMemcpy(P.entries_d, P.entries_h.data(), count * sizeof(DecEntry), hipMemcpyHostToDevice));
   if (!all.empty()) HIP_TRY(hipMemcpy(P.items_d, all.data(), all.size() * sizeof(WorkItem), hipMemcpyHostToDevice));
+  if (!ulist.empty()) HIP_TRY(hipMemcpy(P.uitems_d, ulist.data(), ulist.size() * sizeof(UItem), hipMemcpyHostToDevice));
+  std::vector<int> npcs;
+  for (const DecEntry& E : P.entries_h) npcs.push_back(E.npc);
+  P.u_lds = decode_u_lds_bytes(npcs.data(), count, T);
+  P.sink = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(P.work.ptr) + sink_off);
   P.nv_items = (int)vlist.size();
   P.nu_items = (int)ulist.size();
   P.T = T;
@@ -261,9 +301,11 @@ lb_status run_decode(DecodePlan& P, const lb_linear* L, int count, const void* c
     a.T = T;
     a.t0 = (int)t0;
     a.items = P.items_d;
+    a.uitems = P.uitems_d;
+    a.sink = P.sink;
+    a.nentries = count;
     HIP_TRY(launch_decode_v(a, P.nv_items, st));
-    a.items = P.items_d + P.nv_items;
-    HIP_TRY(launch_decode_u(a, P.nu_items, st));
+    HIP_TRY(launch_decode_u(a, P.nu_items, P.u_lds, st));
   }
   return LB_OK;
 }
@@ -400,9 +442,9 @@ lb_status lb_linear_create(int64_t d_out, int64_t d_in, const lb_path* paths, in
     uw += (int)W;
     total += align256(d_out * W * 4) + align256(d_in * W * 4);                  // canonical
     total += align256((d_out + d_in + r) * 2);                                   // fp16 scales
-    total += align256((size_t)nkc * nct * 64 * 4);                              // decode V
+    total += align256((size_t)nkc * nct * 64 * 4 + kDmaPad);                    // decode V
   }
-  total += align256((size_t)nrt * uw * 16 * 4);                                  // decode U
+  total += align256(decode_u_bytes(nrt, uw));                                    // decode U
   total += pre_bytes;
   L->uw = uw;
   hipError_t e = hipMalloc(&L->arena.base, total);
@@ -415,7 +457,9 @@ lb_status lb_linear_create(int64_t d_out, int64_t d_in, const lb_path* paths, in
     linear_free(L);
     return hip_fail(err, what);
   };
-  L->udec = reinterpret_cast<uint32_t*>(L->arena.take((size_t)nrt * uw * 16 * 4));
+  L->udec = reinterpret_cast<uint32_t*>(L->arena.take(decode_u_bytes(nrt, uw)));
+  // row tiles past the last one (padding of the last quad) must read as zero words
+  if ((e = hipMemsetAsync(L->udec, 0, decode_u_bytes(nrt, uw), st)) != hipSuccess) return bail(e, "clear U");
   int woff = 0;
   for (int p = 0; p < n_paths; ++p) {
     const lb_path& S = paths[p];
@@ -427,7 +471,7 @@ lb_status lb_linear_create(int64_t d_out, int64_t d_in, const lb_path* paths, in
     uint32_t* ucan = reinterpret_cast<uint32_t*>(L->arena.take(d_out * W * 4));
     uint32_t* vcan = reinterpret_cast<uint32_t*>(L->arena.take(d_in * W * 4));
     uint16_t* sc = reinterpret_cast<uint16_t*>(L->arena.take((d_out + d_in + r) * 2));
-    uint32_t* vdec = reinterpret_cast<uint32_t*>(L->arena.take((size_t)nkc * D.nct * 64 * 4));
+    uint32_t* vdec = reinterpret_cast<uint32_t*>(L->arena.take((size_t)nkc * D.nct * 64 * 4 + kDmaPad));
     D.u_can = ucan;
     D.v_can = vcan;
     D.h = sc;

@@ -31,6 +31,7 @@
 #include "lb_internal.h"
 #include <hip/hip_fp16.h>
 
+#include <algorithm>
 #include <type_traits>
 
 namespace lb {
@@ -38,10 +39,11 @@ namespace lb {
 namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kWaves = 4;
+constexpr int kWaves = kWavesPerGroup;
 
 // Pointers read from the entry table are generic; naming them global lets the
 // compiler use global (not flat) memory instructions.
@@ -60,6 +62,9 @@ __device__ inline uint16_t f32_to_bf16_rne(float f) {
   u += 0x7fffu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
 }
+
+// float -> bf16 bits, round to nearest even (the hardware conversion)
+__device__ inline uint16_t bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 template <int N>
 __device__ inline float ror16(float v) {  // rotate within a row of 16 lanes (DPP row_ror)
@@ -102,6 +107,12 @@ __device__ inline v8i expand_signs(uint32_t w) {
   return b;
 }
 
+// Byte offset of byte e (< 32) of MFMA row `row`, K group g in an fp8 A image:
+// two 1 KB halves holding bytes 0-15 and 16-31 of every (row, group), so the
+// two 16-byte reads of a wave each cover one contiguous 1 KB (no bank
+// conflicts); the e8m0 scales follow at byte 2048.
+__host__ __device__ inline int img_off(int row, int g, int e) { return (e >> 4) * 1024 + (row * 4 + g) * 16 + (e & 15); }
+
 __device__ inline v4f mfma(const v8i& a, const v8i& b, v4f c, int scale_a) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, scale_a, 0, 127);
 }
@@ -141,8 +152,8 @@ __device__ inline float convert_pair(const ConvLane& L, float t0, float t1, int 
   float l0 = __builtin_amdgcn_cvt_f32_fp8(lo, 0), l1 = __builtin_amdgcn_cvt_f32_fp8(lo, 1);
   const int mhi = 2 * tt, mlo = 2 * tt + 1;
   using U16 = typename std::conditional<std::is_same<Ptr, uint8_t*>::value, uint16_t, LB_GLOBAL uint16_t>::type;
-  *reinterpret_cast<U16*>(ab + (mhi * 4 + L.gdst) * 32 + L.edst) = (uint16_t)hi;
-  *reinterpret_cast<U16*>(ab + (mlo * 4 + L.gdst) * 32 + L.edst) = (uint16_t)lo;
+  *reinterpret_cast<U16*>(ab + img_off(mhi, L.gdst, L.edst)) = (uint16_t)hi;
+  *reinterpret_cast<U16*>(ab + img_off(mlo, L.gdst, L.edst)) = (uint16_t)lo;
   if (L.sub == 0) {
     ab[2048 + mhi * 4 + L.kb] = (uint8_t)(E + 127);
     ab[2048 + mlo * 4 + L.kb] = (uint8_t)(E + 127 - 4);
@@ -152,17 +163,16 @@ __device__ inline float convert_pair(const ConvLane& L, float t0, float t1, int 
 }
 
 // Reads lane (mr, gr)'s A operand and scale from an A image (LDS or global).
+// Rows past the real tokens hold stale values: MFMA rows are independent and
+// those rows of the result are never read.
 template <class Ptr>
-__device__ inline void load_a(Ptr ab, int mr, int gr, int rows, v8i& a, int& sc) {
-  const int mc = min(mr, rows - 1);   // rows >= 1; the load is unconditional, the value is selected
-  using V8 = typename std::conditional<std::is_same<Ptr, const uint8_t*>::value || std::is_same<Ptr, uint8_t*>::value,
-                                      const v8i, const LB_GLOBAL v8i>::type;
-  const v8i v = *reinterpret_cast<V8*>(ab + (mc * 4 + gr) * 32);
-  const int s = ab[2048 + mc * 4 + gr];
-  const bool ok = mr < rows;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) a[i] = ok ? v[i] : 0;
-  sc = ok ? s : 127;
+__device__ inline void load_a(Ptr ab, int mr, int gr, v8i& a, int& sc) {
+  using V4 = typename std::conditional<std::is_same<Ptr, const uint8_t*>::value || std::is_same<Ptr, uint8_t*>::value,
+                                      const v4i, const LB_GLOBAL v4i>::type;
+  const v4i lo = *reinterpret_cast<V4*>(ab + img_off(mr, gr, 0));
+  const v4i hi = *reinterpret_cast<V4*>(ab + img_off(mr, gr, 16));
+  a = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  sc = ab[2048 + mr * 4 + gr];
 }
 
 
@@ -257,7 +267,7 @@ __device__ void v_item(const DecArgs& a, const DecEntry& Eg, const void* xv, int
     v8i A[TB];
     int sc[TB];
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb) load_a(abuf + tb * kABytes, mr, gr, 2 * min(8, T - tb * 8), A[tb], sc[tb]);
+    for (int tb = 0; tb < TB; ++tb) load_a(abuf + tb * kABytes, mr, gr, A[tb], sc[tb]);
 #pragma unroll
     for (int c = 0; c < CTM; ++c) {
       if (c < nct) {
@@ -371,200 +381,298 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_v(DecArgs a) {
 // ---------------------------------------------------------------------------
 // U stage
 // ---------------------------------------------------------------------------
-// The item's fp8 A operand images (written by the V stage) are staged in LDS;
-// each wave owns every 4th row tile of the item and walks them in groups of 4
-// (acc[4][path][token block]).  When all images fit (npc * TB <= kUImgMax)
-// they are staged once and the next group's sign words and row scales are in
-// flight while the current group multiplies; otherwise every group runs the
-// images in passes.
-constexpr int kUImgMax = 8;
-
-template <int TM>
-struct UCtx {
-  static constexpr int TB = (TM + 7) / 8;
-  int np, nrt, npc, m, uw, pcoff1, woff[2], W[2];
-  const uint32_t* udec;
-  const uint16_t* h[2];
-  int T, rt0, nmine, nunits, mr, gr, lane;
-  float cval[2][TB][2];
-  LB_GLOBAL uint16_t* y;
-
-  // word offset (inside a row tile's block) and lane validity of unit u
-  __device__ void unit(int u, int& off, bool& ok, int& p, int& tb) const {
-    const int pc = u / TB;
-    tb = u % TB;
-    p = (np > 1 && pc >= pcoff1) ? 1 : 0;
-    const int w4 = 4 * (pc - (p ? pcoff1 : 0));
-    off = ((p ? woff[1] : woff[0]) + w4) * 16;
-    ok = w4 + gr < (p ? W[1] : W[0]);
-  }
-  __device__ void load_words(int grp, int u0, int nu, uint32_t (*w)[kUImgMax], uint32_t (*hv)[2]) const {
-    const LB_GLOBAL uint32_t* ud = gp(udec) + lane;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int rt = min(rt0 + 4 * (4 * grp + k), nrt - 1);
-      const LB_GLOBAL uint32_t* blk = ud + (int64_t)rt * uw * 16;
-#pragma unroll
-      for (int q = 0; q < kUImgMax; ++q) {
-        int off, p, tb;
-        bool ok;
-        unit(u0 + min(q, nu - 1), off, ok, p, tb);
-        w[k][q] = blk[off];
-      }
-      const int i = min(rt * 16 + mr, m - 1);
-      hv[k][0] = gp(h[0])[i];
-      hv[k][1] = gp(h[np > 1 ? 1 : 0])[i];
-    }
-  }
-  __device__ void multiply(int grp, int u0, int nu, const uint32_t (*w)[kUImgMax], const uint8_t* imgs,
-                           v4f (*acc)[2][TB]) const {
-#pragma unroll
-    for (int q = 0; q < kUImgMax; ++q) {
-      if (q < nu) {
-        int off, p, tb;
-        bool ok;
-        unit(u0 + q, off, ok, p, tb);
-        v8i A;
-        int sc;
-        load_a(imgs + q * kABytes, mr, gr, 2 * min(8, T - tb * 8), A, sc);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          if (4 * grp + k < nmine) {
-            const v8i B = expand_signs(ok ? w[k][q] : 0u);
-#pragma unroll
-            for (int pp = 0; pp < 2; ++pp)
-#pragma unroll
-              for (int tbb = 0; tbb < TB; ++tbb)
-                if (pp == p && tbb == tb) acc[k][pp][tbb] = mfma(A, B, acc[k][pp][tbb], sc);
-          }
-        }
-      }
-    }
-  }
-  // y = sum_p h_p (D_hi + D_lo + C_p) for the group's row tiles
-  __device__ void epilogue(int grp, const uint32_t (*hv)[2], v4f (*acc)[2][TB]) const {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int rt = rt0 + 4 * (4 * grp + k);
-      const int i = rt * 16 + mr;
-      if (4 * grp + k < nmine && i < m) {
-        const float h0 = f16f((uint16_t)hv[k][0]);
-        const float h1 = np > 1 ? f16f((uint16_t)hv[k][1]) : 0.f;
-#pragma unroll
-        for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const int t = tb * 8 + 2 * gr + q;
-            if (t < T) {
-              float v = h0 * ((acc[k][0][tb][2 * q] + acc[k][0][tb][2 * q + 1]) + cval[0][tb][q]);
-              if (np > 1) v += h1 * ((acc[k][1][tb][2 * q] + acc[k][1][tb][2 * q + 1]) + cval[1][tb][q]);
-              y[(int64_t)t * m + i] = f32_to_bf16_rne(v);
-            }
-          }
-      }
-    }
-  }
-};
+// Item = (entry, up to 16 quads of 4 row tiles); each wave takes every 4th
+// quad (kQW of them) and runs unit-major: for each 128-latent unit (path 0's,
+// then path 1's) it multiplies the unit's fp8 A operand (written by the V stage,
+// read from global memory one unit ahead) against the sign words of its quads.
+// The sign words stream through a private ring of kUDepth 1 KB LDS slots, one
+// direct-to-LDS load per (unit, quad) step issued kUDepth - 1 steps ahead; each
+// step's words are read from the ring one step ahead of the MFMAs.  Every step
+// issues exactly one load (past the end of the work it re-reads its last block
+// into a dead slot), so counting outstanding vector-memory operations tells
+// when a slot has landed.  Row scales are loaded and outputs stored outside
+// the stream.
+constexpr int kUDepth = 12;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(1))) void gbl_void;
 
-__device__ inline void stage_images(uint8_t* lds, const uint8_t* aimg, int u0, int nu) {
-  const LB_GLOBAL u32x4* src = reinterpret_cast<const LB_GLOBAL u32x4*>(gp(aimg) + (int64_t)u0 * kABytes);
-  u32x4* dst = reinterpret_cast<u32x4*>(lds);
-  for (int i = threadIdx.x; i < nu * (kABytes / 16); i += kThreads) dst[i] = src[i];
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
+// at lds_block + 16 l.
+__device__ inline void dma16(const LB_GLOBAL void* src, void* lds_block) {
+  __builtin_amdgcn_global_load_lds((gbl_void*)src, (lds_void*)lds_block, 16, 0, 0);
+}
+// Waits until at most VM vector-memory operations of this wave are outstanding
+// (LDS and export counters untouched).  The memory clobbers keep the compiler
+// from moving memory accesses across the wait.
+template <int VM>
+__device__ inline void vm_wait() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  constexpr int imm = (VM & 15) | (7 << 4) | (15 << 8) | ((VM >> 4) << 14);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(imm);
+  asm volatile("" ::: "memory");
+}
+// Waits for this wave's outstanding LDS reads.
+__device__ inline void lds_reads_wait() {
+  constexpr int imm = 15 | (7 << 4) | (0 << 8) | (3 << 14);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(imm);
+  asm volatile("" ::: "memory");
 }
 
-template <int TM>
-__device__ void u_item(const DecArgs& a, const DecEntry& Eg, void* yv, int rg, uint8_t* lds) {
-  using Ctx = UCtx<TM>;
-  constexpr int TB = Ctx::TB;
-  Ctx c;
-  c.np = Eg.np; c.nrt = Eg.nrt; c.npc = Eg.npc; c.m = Eg.m; c.uw = Eg.uw; c.pcoff1 = Eg.pcoff[1];
-  c.woff[0] = Eg.woff[0]; c.woff[1] = Eg.woff[1]; c.W[0] = Eg.p[0].W; c.W[1] = Eg.p[1].W;
-  c.udec = Eg.udec; c.h[0] = Eg.p[0].h; c.h[1] = Eg.p[1].h;
-  const uint8_t* aimg = Eg.aimg;
+constexpr int kUSlotsPerCU = 2;   // U workgroups per CU (two waves per SIMD)
+
+// Quads per wave and batch of a U segment: as many as fit next to the operands
+// of the NPC units (NPC == 0: one unit's) in about 150 registers.
+constexpr int u_quads_per_batch(int npc, int tb) {
+  const int opr = (npc > 0 ? npc : 1) * tb * 9 + 4;
+  const int per = 24 * tb + 4;
+  return opr + 4 * per <= 150 ? 4 : opr + 2 * per <= 150 ? 2 : 1;
+}
+
+// One U-stage segment: quads [qa, qb) of one entry, on this workgroup.
+//
+// Each wave takes every 4th quad and runs batches of kQW of them.  The data of
+// a batch streams through the wave's ring of kUDepth 1 KB LDS slots as steps,
+// one direct-to-LDS load each, issued kUDepth - 1 steps ahead: first the
+// batch's row scales, then for each 128-latent unit (path 0's, then path 1's)
+// the sign words of each quad.  The operands of the NPC units (NPC == 0: any
+// unit count, read from global memory unit by unit) are loaded before the
+// stream starts and stay in registers.
+//
+// The in-order vector-memory counter tells when a slot has landed: each step
+// issues exactly one load (past the end of the work it re-reads its last
+// block into a dead slot), and each batch ends with exactly kStores output
+// stores (lanes without an output write to a private sink), which the waits of
+// the next kUDepth - 2 steps allow for.
+template <int TM, int NPC>
+__device__ __attribute__((always_inline)) inline void u_segment(const DecArgs& a, const DecEntry& Eg, int e, int qa,
+                                                               int qb, uint8_t* ring) {
+  constexpr int TB = (TM + 7) / 8;
+  constexpr int kQW = u_quads_per_batch(NPC, TB);              // quads per wave per batch
+  constexpr int kQQ = TM == 1 ? 1 : 2;                         // token slots per lane and block
+  constexpr int kStores = kQW * 4 * TB * kQQ;                  // output stores of one batch
+  static_assert(kUDepth - 2 + kStores < 64, "vmcnt range");
+  // snapshot of the entry (the table is re-read otherwise)
+  const int np = Eg.np, m = Eg.m, uw = Eg.uw, npc = NPC > 0 ? NPC : Eg.npc;
+  const int npc0 = np > 1 ? Eg.pcoff[1] : npc;
+  const int woff1 = Eg.woff[1];
+  const LB_GLOBAL uint8_t* aimg = gp(static_cast<const uint8_t*>(Eg.aimg));
   const float* cpart = Eg.cpart;
   const int nvg0 = Eg.nvg[0], nvg1 = Eg.nvg[1];
-  const int tid = threadIdx.x, wave = tid >> 6;
-  c.lane = tid & 63; c.mr = c.lane & 15; c.gr = c.lane >> 4;
-  c.T = a.T;
-  c.nunits = c.npc * TB;
-  c.y = gp(reinterpret_cast<uint16_t*>(yv)) + (int64_t)a.t0 * c.m;
-  c.rt0 = rg * kDecodeRowTilesPerItem + wave;
-  c.nmine = c.rt0 < c.nrt ? min(kDecodeRowTilesPerItem / kWaves, (c.nrt - c.rt0 + kWaves - 1) / kWaves) : 0;
-  const int ngroups = (c.nmine + 3) / 4;
+  const LB_GLOBAL uint8_t* ubase = reinterpret_cast<const LB_GLOBAL uint8_t*>(gp(Eg.udec));
+  const LB_GLOBAL uint8_t* hb0 = reinterpret_cast<const LB_GLOBAL uint8_t*>(gp(Eg.p[0].h));
+  const LB_GLOBAL uint8_t* hb1 = reinterpret_cast<const LB_GLOBAL uint8_t*>(gp(np > 1 ? Eg.p[1].h : Eg.p[0].h));
+  void* yv = a.xs ? a.ys[e] : a.y0;
+  LB_GLOBAL uint16_t* y = gp(reinterpret_cast<uint16_t*>(yv)) + (int64_t)a.t0 * m;
+  const int T = a.T;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int mr = lane & 15, gr = lane >> 4;
+  LB_GLOBAL uint16_t* sink = gp(a.sink) + ((int64_t)blockIdx.x * kWaves + wave) * 128 + (lane & 15) * 8;
+  const int nmine = qa + wave < qb ? (qb - qa - wave + kWaves - 1) / kWaves : 0;   // quads of this wave
+  const int nb = (nmine + kQW - 1) / kQW;                                          // its batches
+  auto quad = [&](int jj) __attribute__((always_inline)) { return qa + wave + kWaves * jj; };
+  auto valid = [&](int b, int j) __attribute__((always_inline)) { return b * kQW + j < nmine; };
+
+  // correction sums C_p per token (V stage partials over its column groups)
+  float cval[2][TB][2];
 #pragma unroll
   for (int p = 0; p < 2; ++p)
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        const int t = tb * 8 + 2 * c.gr + q;
-        float s = 0.f;
-        if (p < c.np && t < c.T && t < TM)
-          for (int g = 0; g < (p ? nvg1 : nvg0); ++g) s += gp(cpart)[(p * kMaxGroups + g) * 16 + t];
-        c.cval[p][tb][q] = s;
+        const int t = tb * 8 + 2 * gr + q;
+        float sum = 0.f;
+        if (p < np && t < T && t < TM)
+          for (int g = 0; g < (p ? nvg1 : nvg0); ++g) sum += gp(cpart)[(p * kMaxGroups + g) * 16 + t];
+        cval[p][tb][q] = sum;
       }
+  constexpr int NA = NPC > 0 ? NPC : 1;
+  v8i A[NA][TB];
+  int sc[NA][TB];
+  auto load_img = [&](int u, v8i* Au, int* su) __attribute__((always_inline)) {
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) load_a(aimg + (int64_t)(u * TB + tb) * kABytes, mr, gr, Au[tb], su[tb]);
+  };
 
-  if (c.nunits <= kUImgMax) {
-    stage_images(lds, aimg, 0, c.nunits);
-    __syncthreads();
-    uint32_t wcur[4][kUImgMax], wnxt[4][kUImgMax], hcur[4][2], hnxt[4][2];
-    if (ngroups > 0) c.load_words(0, 0, c.nunits, wcur, hcur);
-    for (int grp = 0; grp < ngroups; ++grp) {
-      if (grp + 1 < ngroups) c.load_words(grp + 1, 0, c.nunits, wnxt, hnxt);
-      v4f acc[4][2][TB];
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-#pragma unroll
-        for (int p = 0; p < 2; ++p)
-#pragma unroll
-          for (int tb = 0; tb < TB; ++tb) acc[k][p][tb] = v4f{0.f, 0.f, 0.f, 0.f};
-      c.multiply(grp, 0, c.nunits, wcur, lds, acc);
-      c.epilogue(grp, hcur, acc);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-#pragma unroll
-        for (int q = 0; q < kUImgMax; ++q) wcur[k][q] = wnxt[k][q];
-        hcur[k][0] = hnxt[k][0];
-        hcur[k][1] = hnxt[k][1];
+  // issue cursor: batch ib; unit iu (-1: the batch's row-scale step); quad ij
+  int ib = 0, iu = -1, ij = 0;
+  const LB_GLOBAL uint8_t* last = ubase + lane * 16;
+  auto issue = [&](int slot) __attribute__((always_inline)) {
+    if (ib < nb) {
+      if (iu < 0) {
+        // row scales: lane l -> quad (l / 16) % kQW of the batch, path (l / 8) % 2, rows 8 (l % 8) .. + 7
+        const int jj = min(ib * kQW + (lane >> 4) % kQW, nmine - 1);
+        last = ((lane >> 3) & 1 ? hb1 : hb0) + (int64_t)quad(jj) * 128 + (lane & 7) * 16;
+        iu = 0;
+      } else {
+        const int w0 = iu < npc0 ? 4 * iu : woff1 + 4 * (iu - npc0);
+        last = ubase + ((int64_t)quad(ib * kQW + ij) * uw + w0) * 256 + lane * 16;
+        if (++ij == kQW || ib * kQW + ij >= nmine) {
+          ij = 0;
+          if (++iu == npc) {
+            iu = -1;
+            ++ib;
+          }
+        }
       }
     }
-    return;
+    dma16(last, ring + slot * 1024);
+  };
+
+  // prologue: the first kUDepth - 1 steps, then the operands; one wait covers all
+#pragma unroll
+  for (int k = 0; k < kUDepth - 1; ++k) issue(k);
+  if (NPC > 0) {
+#pragma unroll
+    for (int u = 0; u < NA; ++u) load_img(u, A[u], sc[u]);
   }
-  // general path: every group runs the operand images in passes (all waves
-  // take part in every pass because the staging is shared)
-  constexpr int kMaxGroupsPerWave = kDecodeRowTilesPerItem / kWaves / 4;
-  for (int grp = 0; grp < kMaxGroupsPerWave; ++grp) {
-    v4f acc[4][2][TB];
+  vm_wait<0>();
+
+  v4f acc[kQW][4][TB];
+  float part[kQW][4][TB][2];
+  uint32_t hraw[kQW][4];                           // (h0 | h1 << 16) of row mr of each row tile
+  auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
+    for (int j = 0; j < kQW; ++j)
 #pragma unroll
-      for (int p = 0; p < 2; ++p)
+      for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-        for (int tb = 0; tb < TB; ++tb) acc[k][p][tb] = v4f{0.f, 0.f, 0.f, 0.f};
-    uint32_t w[4][kUImgMax], hv[4][2];
-    for (int u0 = 0; u0 < c.nunits; u0 += kUImgMax) {
-      const int nu = min(kUImgMax, c.nunits - u0);
-      __syncthreads();
-      stage_images(lds, aimg, u0, nu);
-      __syncthreads();
-      if (grp < ngroups) {
-        c.load_words(grp, u0, nu, w, hv);
-        c.multiply(grp, u0, nu, w, lds, acc);
+        for (int tb = 0; tb < TB; ++tb) acc[j][rt][tb] = v4f{0.f, 0.f, 0.f, 0.f};
+  };
+  // part (+)= h_p (D_hi + D_lo + C_p); lane (mr, gr) holds MFMA rows 4 gr .. 4 gr + 3
+  // = (hi, lo) of tokens tb * 8 + 2 gr + {0, 1}, column mr = output row
+  auto fold = [&](int p, bool first) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < kQW; ++j)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const float h = f16f((uint16_t)(p ? hraw[j][rt] >> 16 : hraw[j][rt] & 0xffff));
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+          for (int qq = 0; qq < 2; ++qq) {
+            const float v = h * ((acc[j][rt][tb][2 * qq] + acc[j][rt][tb][2 * qq + 1]) + cval[p][tb][qq]);
+            part[j][rt][tb][qq] = first ? v : part[j][rt][tb][qq] + v;
+          }
+      }
+  };
+
+  // consumer: waits for step s's slot (see above) and returns it
+  int s = 0, since_store = kUDepth;
+  auto next_step = [&]() __attribute__((always_inline)) {
+    lds_reads_wait();                              // the slot reloaded next was read last step
+    issue((s + kUDepth - 1) % kUDepth);
+    if (since_store < kUDepth - 2) vm_wait<kUDepth - 2 + kStores>();
+    else vm_wait<kUDepth - 2>();
+    ++since_store;
+    const uint8_t* slot = ring + (s % kUDepth) * 1024;
+    ++s;
+    return slot;
+  };
+  auto unit = [&](int b, int u, const v8i* Au, const int* su) __attribute__((always_inline)) {
+    if (u == npc0 && u > 0) {                      // path 1 starts: fold path 0
+      fold(0, true);
+      zero_acc();
+    }
+#pragma unroll
+    for (int j = 0; j < kQW; ++j) {
+      if (valid(b, j)) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(next_step() + lane * 16);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          const v8i B = expand_signs(w[rt]);
+#pragma unroll
+          for (int tb = 0; tb < TB; ++tb) acc[j][rt][tb] = mfma(Au[tb], B, acc[j][rt][tb], su[tb]);
+        }
       }
     }
-    if (grp < ngroups) c.epilogue(grp, hv, acc);
+  };
+  for (int b = 0; b < nb; ++b) {
+    {  // the batch's row scales: [quad j][path][64 rows] fp16 in the slot
+      const uint16_t* hs = reinterpret_cast<const uint16_t*>(next_step());
+#pragma unroll
+      for (int j = 0; j < kQW; ++j)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+          hraw[j][rt] = (uint32_t)hs[(j * 2) * 64 + rt * 16 + mr] | ((uint32_t)hs[(j * 2 + 1) * 64 + rt * 16 + mr] << 16);
+    }
+    zero_acc();
+    if (NPC > 0) {
+#pragma unroll
+      for (int u = 0; u < NA; ++u) unit(b, u, A[u], sc[u]);
+    } else {
+      for (int u = 0; u < npc; ++u) {
+        load_img(u, A[0], sc[0]);
+        vm_wait<0>();                              // (keeps the count exact; the slow path)
+        unit(b, u, A[0], sc[0]);
+      }
+    }
+    if (npc0 < npc) fold(1, false);
+    else fold(0, true);
+    // y: lane (mr, gr) holds tokens tb * 8 + 2 gr + {0, 1} of output row mr of each row
+    // tile; every store is issued (kStores of them), lanes without an output hit the sink
+#pragma unroll
+    for (int j = 0; j < kQW; ++j)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const int i = (4 * quad(b * kQW + j) + rt) * 16 + mr;
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+          for (int qq = 0; qq < kQQ; ++qq) {
+            const int t = tb * 8 + 2 * gr + qq;
+            const bool ok = valid(b, j) && i < m && t < T;
+            LB_GLOBAL uint16_t* dst = ok ? y + (uint32_t)(t * m + i) : sink + (gr & 3) * 2 + qq;
+            *dst = bf16_bits(part[j][rt][tb][qq]);
+          }
+      }
+    since_store = 0;
   }
+  vm_wait<0>();                                    // no direct-to-LDS load may still be in flight
 }
 
-// One workgroup per U item (kDecodeRowTilesPerItem row tiles of 16 output rows).
 template <int TM>
 __global__ void __launch_bounds__(kThreads, 2) k_decode_u(DecArgs a) {
+  constexpr int TB = (TM + 7) / 8;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  const WorkItem wi = a.items[blockIdx.x];
-  void* y = a.xs ? a.ys[wi.entry] : a.y0;
-  u_item<TM>(a, a.entries[wi.entry], y, wi.group, lds);
+  const UItem it = a.uitems[blockIdx.x];
+  uint8_t* ring = lds + (threadIdx.x >> 6) * (kUDepth * 1024);
+  int e = (int)it.entry, qa = (int)it.quad0, left = (int)it.count;
+  while (left > 0 && e < a.nentries) {
+    const DecEntry& Eg = a.entries[e];
+    const int nq = (Eg.nrt + 3) / 4;
+    const int qb = min(nq, qa + left);
+    const int npc = Eg.npc;
+    if (TB == 1) {
+      switch (npc) {
+        case 1: u_segment<TM, 1>(a, Eg, e, qa, qb, ring); break;
+        case 2: u_segment<TM, 2>(a, Eg, e, qa, qb, ring); break;
+        case 3: u_segment<TM, 3>(a, Eg, e, qa, qb, ring); break;
+        case 4: u_segment<TM, 4>(a, Eg, e, qa, qb, ring); break;
+        case 5: u_segment<TM, 5>(a, Eg, e, qa, qb, ring); break;
+        case 6: u_segment<TM, 6>(a, Eg, e, qa, qb, ring); break;
+        case 7: u_segment<TM, 7>(a, Eg, e, qa, qb, ring); break;
+        case 8: u_segment<TM, 8>(a, Eg, e, qa, qb, ring); break;
+        default: u_segment<TM, 0>(a, Eg, e, qa, qb, ring); break;
+      }
+    } else {
+      switch (npc) {
+        case 1: u_segment<TM, 1>(a, Eg, e, qa, qb, ring); break;
+        case 2: u_segment<TM, 2>(a, Eg, e, qa, qb, ring); break;
+        case 3: u_segment<TM, 3>(a, Eg, e, qa, qb, ring); break;
+        case 4: u_segment<TM, 4>(a, Eg, e, qa, qb, ring); break;
+        default: u_segment<TM, 0>(a, Eg, e, qa, qb, ring); break;
+      }
+    }
+    left -= qb - qa;
+    qa = 0;
+    ++e;
+  }
 }
 
 size_t decode_lds_bytes(int T) {
@@ -588,9 +696,23 @@ hipError_t launch_decode_v(const DecArgs& a, int nitems, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_decode_u(const DecArgs& a, int nitems, hipStream_t st) {
+size_t decode_u_lds_bytes(const int* npc, int count, int T) {
+  (void)npc;
+  (void)count;
+  (void)T;
+  return (size_t)kWaves * kUDepth * 1024;
+}
+
+int decode_u_slots() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  return cus * kUSlotsPerCU;
+}
+
+hipError_t launch_decode_u(const DecArgs& a, int nitems, size_t lds, hipStream_t st) {
   if (nitems <= 0) return hipSuccess;
-  const size_t lds = (size_t)kUImgMax * kABytes;
   switch (decode_bucket(a.T)) {
     case 1: hipLaunchKernelGGL(k_decode_u<1>, dim3(nitems), dim3(kThreads), lds, st, a); break;
     case 2: hipLaunchKernelGGL(k_decode_u<2>, dim3(nitems), dim3(kThreads), lds, st, a); break;

@@ -60,6 +60,14 @@ struct WorkItem {
   uint16_t group;
 };
 
+constexpr int kWavesPerGroup = 4;   // waves of a decode workgroup
+
+// U-stage work item: a contiguous run of `count` quads (4 row tiles each) of the
+// concatenated entries, starting at quad `quad0` of entry `entry`.
+struct UItem {
+  uint32_t entry, quad0, count, pad;
+};
+
 // Launch-wide arguments of the two decode kernels.
 struct DecArgs {
   const DecEntry* entries;
@@ -67,13 +75,26 @@ struct DecArgs {
   void* const* ys;         // per entry output
   const void* x0;          // single-entry input when xs is null
   void* y0;
-  const WorkItem* items;   // this kernel's items, one workgroup each
+  const WorkItem* items;   // V items, one workgroup each
+  const UItem* uitems;     // U items, one workgroup each
+  uint16_t* sink;          // write target of output lanes that hold no output (256 B per U wave)
+  int nentries;
   int T, t0;               // tokens in this launch and the offset of its first token
 };
 
 // Tokens one decode launch handles (token blocks of 8, at most 2 blocks).
 constexpr int kDecodeMaxTokens = 16;
 constexpr int kDecodeRowTilesPerItem = 64;   // U work item = 1024 output rows
+// U work items: batches of quads (4 row tiles); a batch is 4 quads per wave (2
+// at 16 tokens) and an item holds kDecodeUBatches batches of all 4 waves
+constexpr int kDecodeUBatches = 1;
+__host__ __device__ constexpr int decode_u_quads_per_item(int bucket) { return bucket >= 16 ? 8 : 16; }
+__host__ __device__ constexpr int decode_u_item_quads(int bucket) { return decode_u_quads_per_item(bucket) * kDecodeUBatches; }
+constexpr int kDmaPad = 1024;                // slack after buffers read by 1 KB direct-to-LDS loads
+// bytes of the decode U layout: quads of 4 row tiles x uw words x 16 rows x 4 B, plus slack
+__host__ __device__ inline size_t decode_u_bytes(int nrt, int uw) {
+  return (size_t)((nrt + 3) / 4) * uw * 256 + kDmaPad;
+}
 // Token-count bucket of a decode launch (per-token state is sized by it) and the
 // most column tiles one V work item holds at that bucket.
 __host__ __device__ inline int decode_bucket(int T) { return T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : T <= 8 ? 8 : 16; }
@@ -95,6 +116,12 @@ hipError_t launch_exact(const PathDev* p, int np, int m, int n, const void* x, v
 
 // decode path: V-stage kernel then U-stage kernel, one workgroup per work item
 hipError_t launch_decode_v(const DecArgs& a, int nitems, hipStream_t st);
-hipError_t launch_decode_u(const DecArgs& a, int nitems, hipStream_t st);
+hipError_t launch_decode_u(const DecArgs& a, int nitems, size_t lds_bytes, hipStream_t st);
+// Workgroups of the U-stage kernel that run at once on the current device, and
+// U items per such slot (several, so that slots that stream faster take more).
+int decode_u_slots();
+constexpr int kDecodeUItemsPerSlot = 4;
+// LDS bytes of a U-stage launch over entries with npc[e] 128-latent units each
+size_t decode_u_lds_bytes(const int* npc, int count, int T);
 
 }  // namespace lb

@@ -68,7 +68,10 @@ __global__ void k_retile_v(const uint32_t* __restrict__ vcan, int n, int r, int 
   vdec[idx] = word;
 }
 
-// Decode U layout for one path: output (rt, woff + w, row) = permuted canonical word.
+// Decode U layout for one path: row tiles of 16 rows in quads, word-major inside
+// a quad: element (quad, woff + w, row, rt % 4) = permuted canonical word of row
+// 16 rt + row.  One (quad, 4 consecutive words) block is 1 KB: the 16 rows x 4
+// words x 4 row tiles one MFMA step of the decode U stage consumes.
 __global__ void k_retile_u(const uint32_t* __restrict__ ucan, int m, int W, int uw, int woff, int nrt,
                            uint32_t* __restrict__ udec) {
   int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -83,7 +86,7 @@ __global__ void k_retile_u(const uint32_t* __restrict__ ucan, int m, int W, int 
     uint32_t in = ucan[i * W + w];
     for (int e = 0; e < 32; ++e) out |= ((in >> e) & 1u) << fp4_bit_of_elem(e);
   }
-  udec[((int64_t)rt * uw + woff + w) * 16 + row] = out;
+  udec[(((int64_t)(rt >> 2) * uw + woff + w) * 16 + row) * 4 + (rt & 3)] = out;
 }
 
 }  // namespace
