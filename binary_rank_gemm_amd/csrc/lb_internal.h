@@ -120,7 +120,7 @@ hipError_t launch_decode_u(const DecArgs& a, int nitems, size_t lds_bytes, hipSt
 // Workgroups of the U-stage kernel that run at once on the current device, and
 // U items per such slot (several, so that slots that stream faster take more).
 int decode_u_slots();
-constexpr int kDecodeUItemsPerSlot = 4;
+constexpr int kDecodeUItemsPerSlot = 1;
 // LDS bytes of a U-stage launch over entries with npc[e] 128-latent units each
 size_t decode_u_lds_bytes(const int* npc, int count, int T);
 
