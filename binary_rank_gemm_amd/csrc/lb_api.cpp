@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <array>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -84,25 +85,29 @@ struct Scratch {
 // objects
 // ---------------------------------------------------------------------------
 
-// Decode launch plan: entries and the two kernels' per-workgroup item lists for
-// a given token count.  Owned by a linear (single forwards) or a stack.
+// Decode launch plan: entries and the three kernels' per-workgroup item lists
+// for a given token count.  Owned by a linear (single forwards) or a stack.
 struct DecodePlan {
   int T = -1;             // tokens per launch this plan was built for
-  int tb = 0;
   int count = 0;
   std::vector<DecEntry> entries_h;
   DecEntry* entries_d = nullptr;
-  WorkItem* items_d = nullptr;    // V items, longest first
-  UItem* uitems_d = nullptr;      // U items: balanced contiguous runs of quads
-  int nv_items = 0, nu_items = 0;
-  size_t u_lds = 0;               // dynamic LDS of the U-stage launch
-  uint16_t* sink = nullptr;       // U-stage stores of lanes without an output land here
-  Scratch work;                   // U-stage A images and correction sums of every entry
+  VItem* vitems_d = nullptr;      // V items, largest first
+  MItem* mitems_d = nullptr;      // mid items, one per (entry, path)
+  UItem* uitems_d = nullptr;      // U items, largest first
+  int nv = 0, nm = 0, nu = 0;
+  Scratch part;                   // V-stage partial slots
+  Scratch work;                   // U-stage A operands and correction sums of every entry
   void release() {
     if (entries_d) (void)hipFree(entries_d);
-    if (items_d) (void)hipFree(items_d);
+    if (vitems_d) (void)hipFree(vitems_d);
+    if (mitems_d) (void)hipFree(mitems_d);
     if (uitems_d) (void)hipFree(uitems_d);
-    entries_d = nullptr; items_d = nullptr; uitems_d = nullptr;
+    entries_d = nullptr;
+    vitems_d = nullptr;
+    mitems_d = nullptr;
+    uitems_d = nullptr;
+    part.release();
     work.release();
     T = -1;
     count = 0;
@@ -116,8 +121,10 @@ struct lb_linear_s {
   int64_t r[2] = {0, 0};
   Arena arena;
   PathDev paths[2] = {};
-  uint32_t* udec = nullptr;
-  int uw = 0;
+  uint16_t* gdec[2] = {nullptr, nullptr};   // g zero-padded to whole 128-row chunks
+  uint8_t* udec = nullptr;                  // decode U layout
+  uint16_t* hq = nullptr;                   // decode row scales per quad
+  UGeom ug = {};
   PrefillLayer pre = {};
   // single-forward state
   Scratch zexact;
@@ -126,9 +133,20 @@ struct lb_linear_s {
   hipStream_t last_stream = nullptr;
 };
 
+// The decode layouts (V and U sign words) of every linear of a stack copied
+// into one allocation, in stack order, so the decode kernels stream a single
+// contiguous region instead of hundreds of per-linear arenas.
+struct DecodeImage {
+  Scratch buf;
+  std::vector<const uint8_t*> udec;
+  std::vector<const uint16_t*> hq;
+  std::vector<std::array<const uint32_t*, 2>> vdec;
+};
+
 struct lb_stack_s {
   int device = 0;
   std::vector<lb_linear> linears;
+  DecodeImage dimg;
   std::vector<const PrefillLayer*> pre;
   DecodePlan plan;
   PrefillPlan pplan;
@@ -162,25 +180,45 @@ void linear_free(lb_linear L) {
 // decode plans
 // ---------------------------------------------------------------------------
 
-// Items sorted longest first (stable): the order the hardware dispatches them.
-std::vector<WorkItem> longest_first(const std::vector<std::pair<double, WorkItem>>& items) {
+// Items sorted largest first (stable): the order the hardware dispatches them.
+template <class Item>
+std::vector<Item> largest_first(const std::vector<std::pair<double, Item>>& items) {
   std::vector<int> order(items.size());
   for (size_t i = 0; i < items.size(); ++i) order[i] = (int)i;
   std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return items[a].first > items[b].first; });
-  std::vector<WorkItem> out;
+  std::vector<Item> out;
   for (int i : order) out.push_back(items[i].second);
   return out;
 }
 
+template <class Item>
+hipError_t upload(Item** dst, const std::vector<Item>& v) {
+  if (*dst) {
+    hipError_t e = hipFree(*dst);
+    if (e != hipSuccess) return e;
+    *dst = nullptr;
+  }
+  hipError_t e = hipMalloc(dst, std::max<size_t>(v.size(), 1) * sizeof(Item));
+  if (e == hipSuccess && !v.empty()) e = hipMemcpy(*dst, v.data(), v.size() * sizeof(Item), hipMemcpyHostToDevice);
+  return e;
+}
+
 // Builds (or reuses) the decode plan for `count` linears at `T` tokens per launch.
-lb_status build_decode_plan(DecodePlan& P, const lb_linear* L, int count, int T) {
+//   V items: each path's column tiles in groups of at most decode_v_tiles, each
+//     group's 128-row chunks cut into ranges of about kDecodeVItemBytes of sign
+//     words (at least 4 chunks, one per wave, where the path has them).
+//   mid items: one per (entry, path).
+//   U items: runs of 4 qw quads, qw quads per wave, about kDecodeUItemBytes.
+lb_status build_decode_plan(DecodePlan& P, const lb_linear* L, int count, int T, const DecodeImage* img = nullptr) {
   if (P.T == T && P.count == count) return LB_OK;
-  const int tb = (T + 7) / 8;
-  const int ctm = decode_ct_max(T);
+  const int bucket = decode_bucket(T), tb = (bucket + 7) / 8, ct_max = decode_v_tiles(bucket);
   P.entries_h.assign(count, DecEntry{});
-  std::vector<std::pair<double, WorkItem>> vitems;
+  std::vector<std::pair<double, VItem>> vl;
+  std::vector<std::pair<double, UItem>> ul;
+  std::vector<MItem> ml;
   size_t work_bytes = 0;
-  std::vector<size_t> img_off(count), cp_off(count);
+  std::vector<size_t> img_off(count), cv_off(count);
+  int slots = 0;
   for (int e = 0; e < count; ++e) {
     const lb_linear l = L[e];
     DecEntry& E = P.entries_h[e];
@@ -188,109 +226,70 @@ lb_status build_decode_plan(DecodePlan& P, const lb_linear* L, int count, int T)
     E.n = (int)l->n;
     E.np = l->np;
     E.nkc = (int)((l->n + kChunk - 1) / kChunk);
-    E.nrt = (int)((l->m + kTile - 1) / kTile);
-    E.udec = l->udec;
-    E.uw = l->uw;
-    int woff = 0, pc = 0;
+    E.xdirect = (l->n % 8) == 0;
+    E.ug = l->ug;
+    E.udec = img ? img->udec[e] : l->udec;
+    E.hq = img ? img->hq[e] : l->hq;
     for (int p = 0; p < l->np; ++p) {
       E.p[p] = l->paths[p];
-      E.woff[p] = woff;
-      woff += l->paths[p].W;
-      E.pcoff[p] = pc;
-      pc += (l->paths[p].r + kChunk - 1) / kChunk;
-      // column groups: balanced, even-sized (32-latent blocks never straddle two groups)
+      if (img) E.p[p].vdec = img->vdec[e][p];
+      E.gdec[p] = l->gdec[p];
       const int nct = l->paths[p].nct;
-      int groups = (nct + ctm - 1) / ctm;
-      int per = (nct + groups - 1) / groups;
-      per = std::min(ctm, per + (per & 1));
-      groups = (nct + per - 1) / per;
-      E.vct[p] = per;
-      E.nvg[p] = groups;
+      const int groups = (nct + ct_max - 1) / ct_max;
+      const int gt = (nct + groups - 1) / groups;
+      const double chunk_bytes = gt * 256.0;
+      const int max_split = std::max(1, E.nkc / kWavesPerGroup);
+      const int nsplit = std::max(1, std::min(max_split, (int)std::lround(E.nkc * chunk_bytes / kDecodeVItemBytes)));
+      ml.push_back(MItem{e, p, slots, groups, nsplit, gt, 0, 0});
       for (int g = 0; g < groups; ++g) {
-        const int cnt = std::min(per, nct - g * per);
-        const double cost = (double)E.nkc * (cnt + 1.0 + T / 4.0) + 8.0;
-        vitems.push_back({cost, WorkItem{(uint32_t)e, (uint16_t)p, (uint16_t)g}});
+        const int tile0 = g * gt, nt = std::min(gt, nct - tile0);
+        for (int sp = 0; sp < nsplit; ++sp) {
+          const int c0 = (int)((int64_t)E.nkc * sp / nsplit), c1 = (int)((int64_t)E.nkc * (sp + 1) / nsplit);
+          const double cost = (c1 - c0) * (nt * 256.0 + (bucket + 1) * 256.0);
+          vl.push_back({cost, VItem{e, p, tile0, nt, c0, c1, slots + g * nsplit + sp, 0}});
+        }
       }
+      slots += groups * nsplit;
     }
-    E.npc = pc;
     img_off[e] = work_bytes;
-    work_bytes += align256((size_t)E.npc * tb * kABytes);
-    cp_off[e] = work_bytes;
-    work_bytes += align256((size_t)E.np * kMaxGroups * 16 * sizeof(float));
-  }
-  // U items: the quads of all entries in order, cut into runs of equal cost (one
-  // 1 KB step per quad and 128-latent unit, plus the row-scale step of each
-  // batch), one run per workgroup slot of the machine
-  std::vector<UItem> ulist;
-  {
-    const int bq = decode_u_quads_per_item(decode_bucket(T));      // quads of one workgroup batch
-    double total = 0;
-    for (const DecEntry& E : P.entries_h) total += ((E.nrt + 3) / 4) * (E.npc + 1.0 / bq);
-    const double target = std::max(1.0, total / (decode_u_slots() * kDecodeUItemsPerSlot));
-    double acc = 0;
-    UItem cur{0, 0, 0, 0};
-    bool open = false;
-    for (int e = 0; e < count; ++e) {
-      const DecEntry& E = P.entries_h[e];
-      const int nq = (E.nrt + 3) / 4;
-      const double per = E.npc + 1.0 / bq;
-      for (int q = 0; q < nq; q += bq) {
-        const int n = std::min(bq, nq - q);
-        if (!open) {
-          cur = UItem{(uint32_t)e, (uint32_t)q, 0, 0};
-          open = true;
-        }
-        cur.count += n;
-        acc += n * per;
-        if (acc >= target) {
-          ulist.push_back(cur);
-          open = false;
-          acc = 0;
-        }
-      }
+    work_bytes += align256((size_t)E.ug.nu * tb * kABytes);
+    cv_off[e] = work_bytes;
+    work_bytes += align256(2 * 16 * sizeof(float));
+    const double qbytes = E.ug.qbytes + 256.0;
+    const int qw = std::max(1, (int)std::lround(kDecodeUItemBytes / (kWavesPerGroup * qbytes)));
+    for (int q0 = 0; q0 < E.ug.nq; q0 += kWavesPerGroup * qw) {
+      const int nq = std::min(kWavesPerGroup * qw, E.ug.nq - q0);
+      ul.push_back({nq * qbytes, UItem{e, q0, nq, qw}});
     }
-    if (open) ulist.push_back(cur);
   }
-  const std::vector<WorkItem> vlist = longest_first(vitems);
-  std::vector<WorkItem> all(vlist);
-  // device buffers (callers synchronised with earlier launches before a rebuild)
-  const size_t sink_off = work_bytes;              // U-stage sink: 256 B per wave of every item
-  work_bytes += align256((size_t)std::max<size_t>(ulist.size(), 1) * kWavesPerGroup * 256);
-  work_bytes += kDmaPad;   // operand images are read in whole 1 KB pieces
+  work_bytes += kDmaPad;
   HIP_TRY(P.work.ensure(work_bytes));
+  HIP_TRY(P.part.ensure(std::max<size_t>((size_t)slots * decode_slot_floats(bucket) * sizeof(float), 256)));
   for (int e = 0; e < count; ++e) {
     P.entries_h[e].aimg = reinterpret_cast<uint8_t*>(P.work.ptr) + img_off[e];
-    P.entries_h[e].cpart = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(P.work.ptr) + cp_off[e]);
+    P.entries_h[e].cval = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(P.work.ptr) + cv_off[e]);
   }
-  if (P.entries_d) HIP_TRY(hipFree(P.entries_d));
-  if (P.items_d) HIP_TRY(hipFree(P.items_d));
-  if (P.uitems_d) HIP_TRY(hipFree(P.uitems_d));
-  P.entries_d = nullptr; P.items_d = nullptr; P.uitems_d = nullptr;
-  HIP_TRY(hipMalloc(&P.entries_d, count * sizeof(DecEntry)));
-  HIP_TRY(hipMalloc(&P.items_d, std::max<size_t>(all.size(), 1) * sizeof(WorkItem)));
-  HIP_TRY(hipMalloc(&P.uitems_d, std::max<size_t>(ulist.size(), 1) * sizeof(UItem)));
-  HIP_TRY(hipMemcpy(P.entries_d, P.entries_h.data(), count * sizeof(DecEntry), hipMemcpyHostToDevice));
-  if (!all.empty()) HIP_TRY(hipMemcpy(P.items_d, all.data(), all.size() * sizeof(WorkItem), hipMemcpyHostToDevice));
-  if (!ulist.empty()) HIP_TRY(hipMemcpy(P.uitems_d, ulist.data(), ulist.size() * sizeof(UItem), hipMemcpyHostToDevice));
-  std::vector<int> npcs;
-  for (const DecEntry& E : P.entries_h) npcs.push_back(E.npc);
-  P.u_lds = decode_u_lds_bytes(npcs.data(), count, T);
-  P.sink = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(P.work.ptr) + sink_off);
-  P.nv_items = (int)vlist.size();
-  P.nu_items = (int)ulist.size();
+  const std::vector<VItem> vlist = largest_first(vl);
+  const std::vector<UItem> ulist = largest_first(ul);
+  HIP_TRY(upload(&P.entries_d, P.entries_h));
+  HIP_TRY(upload(&P.vitems_d, vlist));
+  HIP_TRY(upload(&P.mitems_d, ml));
+  HIP_TRY(upload(&P.uitems_d, ulist));
+  P.nv = (int)vlist.size();
+  P.nm = (int)ml.size();
+  P.nu = (int)ulist.size();
   P.T = T;
-  P.tb = tb;
   P.count = count;
   return LB_OK;
 }
 
-// Launches the two decode kernels over token slices of at most kDecodeMaxTokens.
+// Launches the three decode kernels over token slices of at most kDecodeMaxTokens.
 lb_status run_decode(DecodePlan& P, const lb_linear* L, int count, const void* const* xs_d, void* const* ys_d,
-                     const void* x0, void* y0, int64_t tokens, hipStream_t st) {
+                     const void* x0, void* y0, int64_t tokens, hipStream_t st, const DecodeImage* img = nullptr) {
   for (int64_t t0 = 0; t0 < tokens; t0 += kDecodeMaxTokens) {
     const int T = (int)std::min<int64_t>(kDecodeMaxTokens, tokens - t0);
     if (P.T != T && P.T != -1) HIP_TRY(hipStreamSynchronize(st));  // the plan is rewritten below
-    lb_status s = build_decode_plan(P, L, count, T);
+    lb_status s = build_decode_plan(P, L, count, T, img);
     if (s != LB_OK) return s;
     DecArgs a{};
     a.entries = P.entries_d;
@@ -300,12 +299,13 @@ lb_status run_decode(DecodePlan& P, const lb_linear* L, int count, const void* c
     a.y0 = y0;
     a.T = T;
     a.t0 = (int)t0;
-    a.items = P.items_d;
+    a.vitems = P.vitems_d;
+    a.mitems = P.mitems_d;
     a.uitems = P.uitems_d;
-    a.sink = P.sink;
-    a.nentries = count;
-    HIP_TRY(launch_decode_v(a, P.nv_items, st));
-    HIP_TRY(launch_decode_u(a, P.nu_items, P.u_lds, st));
+    a.part = reinterpret_cast<float*>(P.part.ptr);
+    HIP_TRY(launch_decode_v(a, P.nv, st));
+    HIP_TRY(launch_decode_mid(a, P.nm, st));
+    HIP_TRY(launch_decode_u(a, P.nu, st));
   }
   return LB_OK;
 }
@@ -432,21 +432,19 @@ lb_status lb_linear_create(int64_t d_out, int64_t d_in, const lb_path* paths, in
   L->np = n_paths;
   // sizes of every piece
   const int nkc = (int)((d_in + kChunk - 1) / kChunk);
-  const int nrt = (int)((d_out + kTile - 1) / kTile);
   size_t total = 0;
-  int uw = 0;
   size_t pre_bytes = prefill_layer_bytes(d_out, d_in, paths, n_paths);
   for (int p = 0; p < n_paths; ++p) {
     const int64_t r = paths[p].rank, W = words_per_row(r), nct = (r + kTile - 1) / kTile;
     L->r[p] = r;
-    uw += (int)W;
     total += align256(d_out * W * 4) + align256(d_in * W * 4);                  // canonical
     total += align256((d_out + d_in + r) * 2);                                   // fp16 scales
     total += align256((size_t)nkc * nct * 64 * 4 + kDmaPad);                    // decode V
+    total += align256((size_t)nkc * kChunk * 2);                                 // decode g
   }
-  total += align256(decode_u_bytes(nrt, uw));                                    // decode U
+  L->ug = u_geom(d_out, L->r, n_paths);
+  total += align256(decode_u_bytes(L->ug)) + align256(decode_h_bytes(L->ug));   // decode U, row scales
   total += pre_bytes;
-  L->uw = uw;
   hipError_t e = hipMalloc(&L->arena.base, total);
   if (e != hipSuccess) {
     delete L;
@@ -457,10 +455,11 @@ lb_status lb_linear_create(int64_t d_out, int64_t d_in, const lb_path* paths, in
     linear_free(L);
     return hip_fail(err, what);
   };
-  L->udec = reinterpret_cast<uint32_t*>(L->arena.take(decode_u_bytes(nrt, uw)));
-  // row tiles past the last one (padding of the last quad) must read as zero words
-  if ((e = hipMemsetAsync(L->udec, 0, decode_u_bytes(nrt, uw), st)) != hipSuccess) return bail(e, "clear U");
-  int woff = 0;
+  L->udec = reinterpret_cast<uint8_t*>(L->arena.take(decode_u_bytes(L->ug)));
+  L->hq = reinterpret_cast<uint16_t*>(L->arena.take(decode_h_bytes(L->ug)));
+  // the DMA slack after both is never used by a result, but keep it defined
+  if ((e = hipMemsetAsync(L->udec, 0, decode_u_bytes(L->ug), st)) != hipSuccess) return bail(e, "clear U");
+  if ((e = hipMemsetAsync(L->hq, 0, decode_h_bytes(L->ug), st)) != hipSuccess) return bail(e, "clear h");
   for (int p = 0; p < n_paths; ++p) {
     const lb_path& S = paths[p];
     const int64_t r = S.rank, W = words_per_row(r);
@@ -472,6 +471,7 @@ lb_status lb_linear_create(int64_t d_out, int64_t d_in, const lb_path* paths, in
     uint32_t* vcan = reinterpret_cast<uint32_t*>(L->arena.take(d_in * W * 4));
     uint16_t* sc = reinterpret_cast<uint16_t*>(L->arena.take((d_out + d_in + r) * 2));
     uint32_t* vdec = reinterpret_cast<uint32_t*>(L->arena.take((size_t)nkc * D.nct * 64 * 4 + kDmaPad));
+    L->gdec[p] = reinterpret_cast<uint16_t*>(L->arena.take((size_t)nkc * kChunk * 2));
     D.u_can = ucan;
     D.v_can = vcan;
     D.h = sc;
@@ -484,9 +484,18 @@ lb_status lb_linear_create(int64_t d_out, int64_t d_in, const lb_path* paths, in
     if ((e = hipMemcpyAsync(sc + d_out, S.g, d_in * 2, hipMemcpyDefault, st)) != hipSuccess) return bail(e, "copy g");
     if ((e = hipMemcpyAsync(sc + d_out + d_in, S.l, r * 2, hipMemcpyDefault, st)) != hipSuccess) return bail(e, "copy l");
     if ((e = launch_retile_v_decode(vcan, (int)d_in, (int)r, vdec, st)) != hipSuccess) return bail(e, "retile V");
-    if ((e = launch_retile_u_decode(ucan, (int)d_out, (int)r, (int)W, uw, woff, L->udec, st)) != hipSuccess)
+    if ((e = hipMemsetAsync(L->gdec[p], 0, (size_t)nkc * kChunk * 2, st)) != hipSuccess) return bail(e, "clear g");
+    if ((e = hipMemcpyAsync(L->gdec[p], D.g, d_in * 2, hipMemcpyDeviceToDevice, st)) != hipSuccess)
+      return bail(e, "copy g");
+  }
+  {
+    const int W[2] = {L->paths[0].W, n_paths > 1 ? L->paths[1].W : 0};
+    if ((e = launch_decode_u_layout(L->paths[0].u_can, n_paths > 1 ? L->paths[1].u_can : nullptr, (int)d_out, W, L->ug,
+                                    L->udec, st)) != hipSuccess)
       return bail(e, "retile U");
-    woff += (int)W;
+    if ((e = launch_decode_h_layout(L->paths[0].h, n_paths > 1 ? L->paths[1].h : nullptr, (int)d_out, L->ug.nq, L->hq,
+                                    st)) != hipSuccess)
+      return bail(e, "row scales");
   }
   if ((e = prefill_layer_build(L->pre, L->arena.take(pre_bytes), pre_bytes, d_out, d_in, L->paths, n_paths, st)) !=
       hipSuccess)
@@ -555,6 +564,49 @@ lb_status lb_linear_destroy(lb_linear L) {
   return LB_OK;
 }
 
+namespace {
+
+// Copies the decode layouts of the stack's linears into one allocation (see
+// DecodeImage); the linears' own copies stay in place for single forwards.
+hipError_t build_decode_image(DecodeImage& D, const std::vector<lb_linear>& lins) {
+  size_t total = 0;
+  std::vector<size_t> off;
+  for (lb_linear L : lins) {
+    const int nkc = (int)((L->n + kChunk - 1) / kChunk);
+    for (int p = 0; p < L->np; ++p) {
+      off.push_back(total);
+      total += align256((size_t)nkc * L->paths[p].nct * 64 * 4 + kDmaPad);
+    }
+    off.push_back(total);
+    total += align256(decode_u_bytes(L->ug));
+    off.push_back(total);
+    total += align256(decode_h_bytes(L->ug));
+  }
+  // the linears' layouts were written on their creation streams
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = D.buf.ensure(std::max<size_t>(total, 256));
+  if (e != hipSuccess) return e;
+  uint8_t* base = reinterpret_cast<uint8_t*>(D.buf.ptr);
+  size_t k = 0;
+  for (lb_linear L : lins) {
+    const int nkc = (int)((L->n + kChunk - 1) / kChunk);
+    std::array<const uint32_t*, 2> v = {nullptr, nullptr};
+    for (int p = 0; p < L->np; ++p) {
+      const size_t bytes = (size_t)nkc * L->paths[p].nct * 64 * 4 + kDmaPad;
+      if ((e = hipMemcpy(base + off[k], L->paths[p].vdec, bytes, hipMemcpyDeviceToDevice)) != hipSuccess) return e;
+      v[p] = reinterpret_cast<const uint32_t*>(base + off[k++]);
+    }
+    if ((e = hipMemcpy(base + off[k], L->udec, decode_u_bytes(L->ug), hipMemcpyDeviceToDevice)) != hipSuccess) return e;
+    D.udec.push_back(base + off[k++]);
+    if ((e = hipMemcpy(base + off[k], L->hq, decode_h_bytes(L->ug), hipMemcpyDeviceToDevice)) != hipSuccess) return e;
+    D.hq.push_back(reinterpret_cast<const uint16_t*>(base + off[k++]));
+    D.vdec.push_back(v);
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
 lb_status lb_stack_create(const lb_linear* linears, int32_t count, lb_stack* out) {
   if (!out || !linears) return fail(LB_ERR_INVALID_ARGUMENT, "null pointer");
   if (count <= 0) return fail(LB_ERR_INVALID_ARGUMENT, "count must be positive");
@@ -571,6 +623,7 @@ lb_status lb_stack_create(const lb_linear* linears, int32_t count, lb_stack* out
   hipError_t e = hipMalloc(&S->xs_d, count * sizeof(void*));
   if (e == hipSuccess) e = hipMalloc(&S->ys_d, count * sizeof(void*));
   if (e == hipSuccess) e = hipStreamCreateWithFlags(&S->cap_stream, hipStreamNonBlocking);
+  if (e == hipSuccess) e = build_decode_image(S->dimg, S->linears);
   if (e != hipSuccess) {
     lb_stack_destroy(S);
     return hip_fail(e, "lb_stack_create");
@@ -585,7 +638,7 @@ namespace {
 lb_status stack_launch(lb_stack S, lb_regime rg, int64_t tokens, lb_dtype io, hipStream_t st) {
   const int count = (int)S->linears.size();
   if (rg == LB_REGIME_DECODE)
-    return run_decode(S->plan, S->linears.data(), count, S->xs_d, S->ys_d, nullptr, nullptr, tokens, st);
+    return run_decode(S->plan, S->linears.data(), count, S->xs_d, S->ys_d, nullptr, nullptr, tokens, st, &S->dimg);
   if (rg == LB_REGIME_PREFILL) {
     HIP_TRY(prefill_run(S->pplan, S->pre.data(), count, S->xs_h.data(), S->ys_h.data(), (int)tokens, st, false));
     return LB_OK;
@@ -609,7 +662,7 @@ lb_status stack_prepare(lb_stack S, lb_regime rg, int64_t tokens) {
   const int count = (int)S->linears.size();
   if (rg == LB_REGIME_DECODE) {
     const int T = (int)std::min<int64_t>(tokens, kDecodeMaxTokens);
-    lb_status s = build_decode_plan(S->plan, S->linears.data(), count, T);
+    lb_status s = build_decode_plan(S->plan, S->linears.data(), count, T, &S->dimg);
     if (s != LB_OK) return s;
     if (tokens > kDecodeMaxTokens && tokens % kDecodeMaxTokens) {
       // a ragged last slice uses another plan shape: keep direct launches for it
@@ -701,6 +754,7 @@ lb_status lb_stack_destroy(lb_stack S) {
   S->plan.release();
   prefill_plan_release(S->pplan);
   S->zexact.release();
+  S->dimg.buf.release();
   delete S;
   return LB_OK;
 }

@@ -5,16 +5,20 @@
 // section "Key design"): t = x o g_p, z_p = t V_p, z'_p = z_p o l_p, and then
 // y = sum_p (z'_p U_p^T) o h_p (section "Residual compensation" for the sum).
 //
-// Two launches per step, each over static per-workgroup lists of work items
-// (balanced on the host, longest first), so workgroups never wait on each
-// other and the kernel boundary is the only synchronisation:
-//   V kernel, item (entry, path, column group): z'_p for up to 16 column tiles
-//     of 16 latents, reducing over all d_in rows; the four waves split the
-//     rows and combine partial sums in LDS in a fixed order (deterministic).
-//     Its epilogue converts z'_p straight into the U stage's fp8 A operand
-//     images and the U stage's correction sums.
-//   U kernel, item (entry, 256 output rows): streams U's sign words against
-//     those images and writes y for its rows, both paths.
+// Three launches per step, each over many small, evenly sized work items (one
+// workgroup each, handed out by the hardware dispatcher, several resident per
+// CU so that one item's start-up overlaps the others' streaming):
+//   V kernel, item (entry, path, column tiles, range of 128-row chunks): the
+//     four waves split the chunks, stream the sign words through per-wave rings
+//     of direct-to-LDS loads, and leave the item's partial sums of z_p (and of
+//     the correction term below) in a partial slot, combined across the waves
+//     in a fixed order.
+//   mid kernel, item (entry, path): sums the partial slots in a fixed order,
+//     forms z'_p and writes it as the U stage's fp8 A operands plus the U
+//     stage's correction sums.
+//   U kernel, item (entry, run of quads of 64 output rows): each wave streams
+//     its quads' sign words through its ring against the A operands held in
+//     registers, and writes y for its rows, both paths.
 //
 // Arithmetic (gfx950 v_mfma_scale_f32_16x16x128_f8f6f4, fp32 accumulate):
 //   * B operand = packed sign bits expanded to fp4 (e2m1) with one mask per
@@ -28,11 +32,18 @@
 //     block scales (the instruction's e8m0 scale operand), so the hi/lo pair
 //     carries about 8 significant bits (as bf16 does) and the two terms cost no
 //     extra MFMA for up to 8 tokens.
+//
+// Ring bookkeeping: every ring step is exactly one direct-to-LDS load issued
+// kRing - 1 steps ahead (past the end of the work a wave re-reads its last
+// block), and vector-memory operations complete in issue order, so "at most N
+// operations outstanding" tells when a slot has landed.  The U kernel's output
+// stores sit at fixed places in its step pattern and its waits allow for them.
 #include "lb_internal.h"
 #include <hip/hip_fp16.h>
 
 #include <algorithm>
 #include <type_traits>
+#include <utility>
 
 namespace lb {
 
@@ -55,13 +66,6 @@ __device__ inline const LB_GLOBAL T* gp(const T* p) { return (const LB_GLOBAL T*
 
 __device__ inline float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 __device__ inline float f16f(uint16_t b) { return __half2float(__ushort_as_half(b)); }
-
-__device__ inline uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
 
 // float -> bf16 bits, round to nearest even (the hardware conversion)
 __device__ inline uint16_t bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
@@ -176,223 +180,12 @@ __device__ inline void load_a(Ptr ab, int mr, int gr, v8i& a, int& sc) {
 }
 
 
-// ---------------------------------------------------------------------------
-// V stage
-// ---------------------------------------------------------------------------
-// TM: token-count bucket of the launch (1, 2, 4, 8 or 16): per-token state is
-// sized by TM, MFMA token blocks of 8 by TB.
-template <int TM>
-__device__ void v_item(const DecArgs& a, const DecEntry& Eg, const void* xv, int p, int grp, uint8_t* lds) {
-  constexpr int TB = (TM + 7) / 8;
-  constexpr int CTM = TM >= 8 ? 8 : 16;
-  // snapshot of the entry: the table lives in global memory this kernel also
-  // writes, so fields read in the loops would be re-loaded (and waited for)
-  struct {
-    int nkc, n, vct, nvg, pcoff;
-    uint8_t* aimg;
-    float* cpart;
-  } E = {Eg.nkc, Eg.n, Eg.vct[p], Eg.nvg[p], Eg.pcoff[p], Eg.aimg, Eg.cpart};
-  const PathDev P = Eg.p[p];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int mr = lane & 15, gr = lane >> 4;
-  const int cti = E.vct;
-  const int ct0 = grp * cti;
-  const int nct = min(cti, P.nct - ct0);
-  const int T = a.T, n = E.n;
-  const LB_GLOBAL uint16_t* x = gp(reinterpret_cast<const uint16_t*>(xv)) + (int64_t)a.t0 * n;
-  const LB_GLOBAL uint32_t* vdec = gp(P.vdec);
-  const LB_GLOBAL uint16_t* gsc = gp(P.g);
-  const LB_GLOBAL uint16_t* lsc = gp(P.l);
-
-  uint8_t* abuf = lds + wave * TB * kABytes;
-  float* red = reinterpret_cast<float*>(lds + kWaves * TB * kABytes);   // [CTM*TB][16][16]
-  float* cred = red + CTM * TB * 256;                                   // [16]
-  float* cblk = cred + 16;                                              // [16 tokens * 32 blocks]
-
-  ConvLane L(lane);
-  v4f acc[CTM][TB];
-#pragma unroll
-  for (int c = 0; c < CTM; ++c)
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb) acc[c][tb] = v4f{0.f, 0.f, 0.f, 0.f};
-  float cpart[TM];
-#pragma unroll
-  for (int t = 0; t < TM; ++t) cpart[t] = 0.f;
-
-  // software pipeline: the next chunk's sign words, activations and column
-  // scales are in flight while this chunk converts and multiplies.  Loads are
-  // unconditional (clamped index) and their raw values are not touched until
-  // the next iteration: any use (even a select) makes the compiler wait, and
-  // the in-order load counter would then drain everything in flight.
-  uint32_t wcur[CTM], wnxt[CTM];
-  uint32_t xcur[TM], xnxt[TM], gcur = 0, gnxt = 0;
-  const bool even_n = (n & 1) == 0;
-  auto fetch = [&](int kc, uint32_t* w, uint32_t* xp, uint32_t& gpair) {
-    const LB_GLOBAL uint32_t* vp = vdec + ((int64_t)kc * P.nct + ct0) * 64 + lane;
-#pragma unroll
-    for (int c = 0; c < CTM; ++c) w[c] = vp[min(c, nct - 1) * 64];
-    // lane l holds chunk elements 2l and 2l + 1 (L.kloc == 2 * lane)
-    const int k0 = min(kc * kChunk + L.kloc, (n - 1) & ~1);   // even, and k0 + 1 stays inside the arena
-    gpair = *reinterpret_cast<const LB_GLOBAL uint32_t*>(gsc + k0);
-    if (even_n) {
-#pragma unroll
-      for (int t = 0; t < TM; ++t)
-        xp[t] = *reinterpret_cast<const LB_GLOBAL uint32_t*>(x + (int64_t)min(t, T - 1) * n + k0);
-    } else {
-#pragma unroll
-      for (int t = 0; t < TM; ++t) {
-        const LB_GLOBAL uint16_t* xr = x + (int64_t)min(t, T - 1) * n;
-        xp[t] = (uint32_t)xr[k0] | ((uint32_t)xr[min(k0 + 1, n - 1)] << 16);
-      }
-    }
-  };
-  auto compute = [&](int kc, const uint32_t* wc, const uint32_t* xc, uint32_t gc) {
-    const int k0 = kc * kChunk + L.kloc;
-    const bool v0 = k0 < n, v1 = k0 + 1 < n;
-    const float g0 = v0 ? f16f((uint16_t)(gc & 0xffff)) * L.fcls : 0.f;
-    const float g1 = v1 ? f16f((uint16_t)(gc >> 16)) * L.fcls : 0.f;
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb) {
-      uint8_t* ab = abuf + tb * kABytes;
-#pragma unroll
-      for (int tt = 0; tt < 8; ++tt) {
-        const int t = tb * 8 + tt;
-        if (t < TM && t < T) {
-          const float x0 = bf16f((uint16_t)(xc[t] & 0xffff)), x1 = bf16f((uint16_t)(xc[t] >> 16));
-          cpart[t] += convert_pair(L, x0 * g0, x1 * g1, tt, ab);
-        }
-      }
-    }
-    wave_lds_fence();
-    v8i A[TB];
-    int sc[TB];
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb) load_a(abuf + tb * kABytes, mr, gr, A[tb], sc[tb]);
-#pragma unroll
-    for (int c = 0; c < CTM; ++c) {
-      if (c < nct) {
-        const v8i B = expand_signs(wc[c]);
-#pragma unroll
-        for (int tb = 0; tb < TB; ++tb) acc[c][tb] = mfma(A[tb], B, acc[c][tb], sc[tb]);
-      }
-    }
-    wave_lds_fence();
-  };
-  // chunks go in pairs (kc, kc + 4) with the next pair's loads in flight: up to
-  // three chunks ahead of the one being multiplied
-  uint32_t w2cur[CTM], w2nxt[CTM], x2cur[TM], x2nxt[TM], g2cur = 0, g2nxt = 0;
-  const int nkc = E.nkc;
-  if (wave < nkc) fetch(wave, wcur, xcur, gcur);
-  if (wave + kWaves < nkc) fetch(wave + kWaves, w2cur, x2cur, g2cur);
-  for (int kc = wave; kc < nkc; kc += 2 * kWaves) {
-    if (kc + 2 * kWaves < nkc) fetch(kc + 2 * kWaves, wnxt, xnxt, gnxt);
-    if (kc + 3 * kWaves < nkc) fetch(kc + 3 * kWaves, w2nxt, x2nxt, g2nxt);
-    compute(kc, wcur, xcur, gcur);
-    if (kc + kWaves < nkc) compute(kc + kWaves, w2cur, x2cur, g2cur);
-#pragma unroll
-    for (int c = 0; c < CTM; ++c) {
-      wcur[c] = wnxt[c];
-      w2cur[c] = w2nxt[c];
-    }
-#pragma unroll
-    for (int t = 0; t < TM; ++t) {
-      xcur[t] = xnxt[t];
-      x2cur[t] = x2nxt[t];
-    }
-    gcur = gnxt;
-    g2cur = g2nxt;
-  }
-
-  // fixed-order combine across waves: wave 0 stores, waves 1..3 add in turn
-  float cw[TM];
-#pragma unroll
-  for (int t = 0; t < TM; ++t) cw[t] = wave_sum(cpart[t]);
-  __syncthreads();
-  for (int wv = 0; wv < kWaves; ++wv) {
-    if (wave == wv) {
-#pragma unroll
-      for (int c = 0; c < CTM; ++c) {
-        if (c < nct) {
-#pragma unroll
-          for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              float* dst = red + ((c * TB + tb) * 16 + 4 * gr + i) * 16 + mr;
-              *dst = (wv == 0 ? 0.f : *dst) + acc[c][tb][i];
-            }
-        }
-      }
-      if (lane == 0) {
-#pragma unroll
-        for (int t = 0; t < TM; ++t) cred[t] = (wv == 0 ? 0.f : cred[t]) + cw[t];
-      }
-    }
-    __syncthreads();
-  }
-
-  // z' = (D_hi + D_lo + C) o l, converted into the U stage's A images: each
-  // 16-lane row takes one (token, 32-latent block).  The group owning the last
-  // column tile also writes the zero blocks that pad the path's last chunk.
-  const int j0 = 16 * ct0;                         // a multiple of 32 (groups hold an even tile count)
-  const int last = grp == E.nvg - 1;
-  const int nchunk = (P.r + kChunk - 1) / kChunk;
-  const int nblk = last ? 4 * nchunk - j0 / 32 : (nct + 1) / 2;
-  const int row = tid >> 4;                        // 16 rows of 16 lanes
-  ConvLane LR(lane);                               // lane role inside its 16-lane row: sub = lane & 15
-  for (int u = row; u < T * nblk; u += 16) {
-    const int t = u / nblk, blk = u % nblk;
-    const int jj = j0 + 32 * blk + 2 * LR.sub;     // this lane's two latents jj, jj + 1
-    const int tb = t / 8, tt = t % 8;
-    float v[2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int j = jj + q;
-      v[q] = 0.f;
-      if (j < P.r) {
-        const int c = (j - j0) / 16, col = j % 16;
-        const float* base = red + (c * TB + tb) * 256;
-        const float z = (base[(2 * tt) * 16 + col] + base[(2 * tt + 1) * 16 + col]) + cred[t];
-        v[q] = z * f16f(lsc[j]) * LR.fcls;
-      }
-    }
-    ConvLane LK(((jj % kChunk) / 32) * 16 + LR.sub);   // K position inside the 128-latent chunk
-    uint8_t* ab = E.aimg + ((int64_t)(E.pcoff + jj / kChunk) * TB + tb) * kABytes;   // global
-    const float cc = row16_sum(convert_pair(LK, v[0], v[1], tt, gp(ab)));
-    if (LR.sub == 0) cblk[u] = cc;
-  }
-  __syncthreads();
-  if (tid < T) {
-    float s = 0.f;
-    for (int blk = 0; blk < nblk; ++blk) s += cblk[tid * nblk + blk];
-    gp(E.cpart)[(p * kMaxGroups + grp) * 16 + tid] = s;
-  }
-}
-
-// One workgroup per V item; items are ordered longest first so the hardware
-// dispatcher balances the load.
-template <int TM>
-__global__ void __launch_bounds__(kThreads, 2) k_decode_v(DecArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  const WorkItem wi = a.items[blockIdx.x];
-  const void* x = a.xs ? a.xs[wi.entry] : a.x0;
-  v_item<TM>(a, a.entries[wi.entry], x, wi.path, wi.group, lds);
-}
 
 // ---------------------------------------------------------------------------
-// U stage
+// Ring of direct-to-LDS loads (one per wave)
 // ---------------------------------------------------------------------------
-// Item = (entry, up to 16 quads of 4 row tiles); each wave takes every 4th
-// quad (kQW of them) and runs unit-major: for each 128-latent unit (path 0's,
-// then path 1's) it multiplies the unit's fp8 A operand (written by the V stage,
-// read from global memory one unit ahead) against the sign words of its quads.
-// The sign words stream through a private ring of kUDepth 1 KB LDS slots, one
-// direct-to-LDS load per (unit, quad) step issued kUDepth - 1 steps ahead; each
-// step's words are read from the ring one step ahead of the MFMAs.  Every step
-// issues exactly one load (past the end of the work it re-reads its last block
-// into a dead slot), so counting outstanding vector-memory operations tells
-// when a slot has landed.  Row scales are loaded and outputs stored outside
-// the stream.
-constexpr int kUDepth = 12;
+constexpr int kRing = 8;                   // 1 KB slots per wave
+constexpr int kRingBytes = kRing * 1024;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
@@ -414,311 +207,627 @@ __device__ inline void vm_wait() {
   __builtin_amdgcn_s_waitcnt(imm);
   asm volatile("" ::: "memory");
 }
-// Waits for this wave's outstanding LDS reads.
-__device__ inline void lds_reads_wait() {
+// Waits for this wave's outstanding LDS accesses.
+__device__ inline void lds_wait() {
   constexpr int imm = 15 | (7 << 4) | (0 << 8) | (3 << 14);
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(imm);
   asm volatile("" ::: "memory");
 }
 
-constexpr int kUSlotsPerCU = 2;   // U workgroups per CU (two waves per SIMD)
-
-// Quads per wave and batch of a U segment: as many as fit next to the operands
-// of the NPC units (NPC == 0: one unit's) in about 150 registers.
-constexpr int u_quads_per_batch(int npc, int tb) {
-  const int opr = (npc > 0 ? npc : 1) * tb * 9 + 4;
-  const int per = 24 * tb + 4;
-  return opr + 4 * per <= 150 ? 4 : opr + 2 * per <= 150 ? 2 : 1;
+template <class F, int... I>
+__device__ __attribute__((always_inline)) inline void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, in order
+template <int N, class F>
+__device__ __attribute__((always_inline)) inline void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// One U-stage segment: quads [qa, qb) of one entry, on this workgroup.
-//
-// Each wave takes every 4th quad and runs batches of kQW of them.  The data of
-// a batch streams through the wave's ring of kUDepth 1 KB LDS slots as steps,
-// one direct-to-LDS load each, issued kUDepth - 1 steps ahead: first the
-// batch's row scales, then for each 128-latent unit (path 0's, then path 1's)
-// the sign words of each quad.  The operands of the NPC units (NPC == 0: any
-// unit count, read from global memory unit by unit) are loaded before the
-// stream starts and stay in registers.
-//
-// The in-order vector-memory counter tells when a slot has landed: each step
-// issues exactly one load (past the end of the work it re-reads its last
-// block into a dead slot), and each batch ends with exactly kStores output
-// stores (lanes without an output write to a private sink), which the waits of
-// the next kUDepth - 2 steps allow for.
-template <int TM, int NPC>
-__device__ __attribute__((always_inline)) inline void u_segment(const DecArgs& a, const DecEntry& Eg, int e, int qa,
-                                                               int qb, uint8_t* ring) {
-  constexpr int TB = (TM + 7) / 8;
-  constexpr int kQW = u_quads_per_batch(NPC, TB);              // quads per wave per batch
-  constexpr int kQQ = TM == 1 ? 1 : 2;                         // token slots per lane and block
-  constexpr int kStores = kQW * 4 * TB * kQQ;                  // output stores of one batch
-  static_assert(kUDepth - 2 + kStores < 64, "vmcnt range");
-  // snapshot of the entry (the table is re-read otherwise)
-  const int np = Eg.np, m = Eg.m, uw = Eg.uw, npc = NPC > 0 ? NPC : Eg.npc;
-  const int npc0 = np > 1 ? Eg.pcoff[1] : npc;
-  const int woff1 = Eg.woff[1];
-  const LB_GLOBAL uint8_t* aimg = gp(static_cast<const uint8_t*>(Eg.aimg));
-  const float* cpart = Eg.cpart;
-  const int nvg0 = Eg.nvg[0], nvg1 = Eg.nvg[1];
-  const LB_GLOBAL uint8_t* ubase = reinterpret_cast<const LB_GLOBAL uint8_t*>(gp(Eg.udec));
-  const LB_GLOBAL uint8_t* hb0 = reinterpret_cast<const LB_GLOBAL uint8_t*>(gp(Eg.p[0].h));
-  const LB_GLOBAL uint8_t* hb1 = reinterpret_cast<const LB_GLOBAL uint8_t*>(gp(np > 1 ? Eg.p[1].h : Eg.p[0].h));
-  void* yv = a.xs ? a.ys[e] : a.y0;
-  LB_GLOBAL uint16_t* y = gp(reinterpret_cast<uint16_t*>(yv)) + (int64_t)a.t0 * m;
-  const int T = a.T;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int mr = lane & 15, gr = lane >> 4;
-  LB_GLOBAL uint16_t* sink = gp(a.sink) + ((int64_t)blockIdx.x * kWaves + wave) * 128 + (lane & 15) * 8;
-  const int nmine = qa + wave < qb ? (qb - qa - wave + kWaves - 1) / kWaves : 0;   // quads of this wave
-  const int nb = (nmine + kQW - 1) / kQW;                                          // its batches
-  auto quad = [&](int jj) __attribute__((always_inline)) { return qa + wave + kWaves * jj; };
-  auto valid = [&](int b, int j) __attribute__((always_inline)) { return b * kQW + j < nmine; };
+// ---------------------------------------------------------------------------
+// V stage
+// ---------------------------------------------------------------------------
+// TM: token-count bucket of the launch (1, 2, 4, 8 or 16): per-token state is
+// sized by TM, MFMA token blocks of 8 by TB.
+template <int TM>
+struct VShape {
+  static constexpr int TB = (TM + 7) / 8;
+  static constexpr int CT = decode_v_tiles(TM);   // most column tiles of an item
+  static constexpr int SMAX = (CT + 3) / 4;       // sign steps per chunk (4 tiles each)
+  static constexpr int XS = (TM + 4) / 4;         // steps per chunk holding g and TM rows of x (256 B each)
+  static constexpr size_t lds = (size_t)kWaves * kRingBytes + (size_t)kWaves * TB * kABytes;
+};
 
-  // correction sums C_p per token (V stage partials over its column groups)
-  float cval[2][TB][2];
+// Partial sums of one wave's chunks: acc (z_p before the correction term) and
+// cpart (the correction term per token).  Fast form: every read goes through
+// the wave's ring (x rows of n % 8 == 0 elements).
+template <int TM>
+__device__ __attribute__((always_inline)) inline void v_stream(const DecArgs& a, const VItem& it, int n, int nct,
+                                                              const LB_GLOBAL uint8_t* xb, const LB_GLOBAL uint8_t* gdec,
+                                                              const LB_GLOBAL uint8_t* vdec, int ca, int cb, uint8_t* ring,
+                                                              uint8_t* abuf, v4f (&acc)[VShape<TM>::CT][VShape<TM>::TB],
+                                                              float (&cpart)[TM]) {
+  using S = VShape<TM>;
+  constexpr int TB = S::TB, XS = S::XS;
+  const int lane = threadIdx.x & 63, mr = lane & 15, gr = lane >> 4;
+  const int T = a.T, ntl = it.ntiles, ss = (ntl + 3) / 4, P = XS + ss;
+  // issue cursor: chunk ic, step ik inside the chunk (XS x/g steps, then ss sign steps)
+  int ic = ca, ik = 0;
+  const LB_GLOBAL uint8_t* last = gdec;
+  auto issue = [&](int slot) __attribute__((always_inline)) {
+    if (ic < cb) {
+      if (ik < XS) {
+        // lane l: row 4 ik + l / 16 of the step (0: g, 1 + t: token t), elements 8 (l % 16) .. + 7
+        const int rho = 4 * ik + (lane >> 4);
+        const int e0 = ic * kChunk + 8 * (lane & 15);
+        if (rho == 0) {
+          last = gdec + (int64_t)e0 * 2;
+        } else {
+          const int t = min(rho - 1, T - 1);
+          last = xb + ((int64_t)t * n + min(e0, n - 8)) * 2;
+        }
+      } else {
+        // lane l: 16 bytes of column tile 4 (ik - XS) + l / 16 of the item (the last one past the end)
+        const int tile = it.tile0 + min(4 * (ik - XS) + (lane >> 4), ntl - 1);
+        last = vdec + ((int64_t)ic * nct + tile) * 256 + (lane & 15) * 16;
+      }
+      if (++ik == P) {
+        ik = 0;
+        ++ic;
+      }
+    }
+    dma16(last, ring + slot * 1024);
+  };
+#pragma unroll
+  for (int k = 0; k < kRing - 1; ++k) issue(k);
+  int s = 0;
+  auto next_step = [&]() __attribute__((always_inline)) {
+    lds_wait();                                // the slot reloaded next was read last step
+    issue((s + kRing - 1) % kRing);
+    vm_wait<kRing - 1>();
+    const uint8_t* slot = ring + (s % kRing) * 1024;
+    ++s;
+    return slot;
+  };
+  const ConvLane L(lane);
+  for (int c = ca; c < cb; ++c) {
+    // this lane's elements kloc, kloc + 1 (= 2 lane, 2 lane + 1) of g and of each token row
+    uint32_t gpair = 0, xpair[TM];
+#pragma unroll
+    for (int t = 0; t < TM; ++t) xpair[t] = 0;
+#pragma unroll
+    for (int j = 0; j < XS; ++j) {
+      const uint8_t* slot = next_step();
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int rho = 4 * j + q;
+        if (rho == 0) gpair = *reinterpret_cast<const uint32_t*>(slot + 4 * lane);
+        else if (rho - 1 < TM) xpair[rho - 1] = *reinterpret_cast<const uint32_t*>(slot + q * 256 + 4 * lane);
+      }
+    }
+    const int k0 = c * kChunk + L.kloc;
+    const bool v0 = k0 < n, v1 = k0 + 1 < n;
+    const float g0 = f16f((uint16_t)(gpair & 0xffff)) * L.fcls, g1 = f16f((uint16_t)(gpair >> 16)) * L.fcls;
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) {
+        const int t = tb * 8 + tt;
+        if (t < TM && t < T) {
+          const float x0 = bf16f((uint16_t)(xpair[t] & 0xffff)), x1 = bf16f((uint16_t)(xpair[t] >> 16));
+          cpart[t] += convert_pair(L, v0 ? x0 * g0 : 0.f, v1 ? x1 * g1 : 0.f, tt, abuf + tb * kABytes);
+        }
+      }
+    }
+    wave_lds_fence();
+    v8i A[TB];
+    int sc[TB];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) load_a(abuf + tb * kABytes, mr, gr, A[tb], sc[tb]);
+    wave_lds_fence();
+#pragma unroll
+    for (int j = 0; j < S::SMAX; ++j) {
+      if (j < ss) {
+        const uint8_t* slot = next_step();
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = *reinterpret_cast<const uint32_t*>(slot + i * 256 + 4 * lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (4 * j + i < S::CT && 4 * j + i < ntl) {
+            const v8i B = expand_signs(w[i]);
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) acc[4 * j + i][tb] = mfma(A[tb], B, acc[4 * j + i][tb], sc[tb]);
+          }
+        }
+      }
+    }
+  }
+  vm_wait<0>();                                // no direct-to-LDS load may still be in flight
+}
+
+// The same partial sums with plain loads (x rows that 16-byte loads cannot
+// read: n % 8 != 0).  Slow, and only for odd shapes.
+template <int TM>
+__device__ __attribute__((always_inline)) inline void v_plain(const DecArgs& a, const VItem& it, int n, int nct,
+                                                             const LB_GLOBAL uint8_t* xb, const LB_GLOBAL uint8_t* gdec,
+                                                             const LB_GLOBAL uint8_t* vdec, int ca, int cb, uint8_t* abuf,
+                                                             v4f (&acc)[VShape<TM>::CT][VShape<TM>::TB],
+                                                             float (&cpart)[TM]) {
+  using S = VShape<TM>;
+  constexpr int TB = S::TB;
+  const int lane = threadIdx.x & 63, mr = lane & 15, gr = lane >> 4;
+  const int T = a.T, ntl = it.ntiles;
+  const ConvLane L(lane);
+  const LB_GLOBAL uint16_t* x = reinterpret_cast<const LB_GLOBAL uint16_t*>(xb);
+  const LB_GLOBAL uint16_t* g = reinterpret_cast<const LB_GLOBAL uint16_t*>(gdec);
+  for (int c = ca; c < cb; ++c) {
+    const int k0 = c * kChunk + L.kloc;
+    const bool v0 = k0 < n, v1 = k0 + 1 < n;
+    const float g0 = f16f(g[k0]) * L.fcls, g1 = f16f(g[k0 + 1]) * L.fcls;   // g is padded to whole chunks
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) {
+        const int t = tb * 8 + tt;
+        if (t < TM && t < T) {
+          const float x0 = v0 ? bf16f(x[(int64_t)t * n + k0]) : 0.f;
+          const float x1 = v1 ? bf16f(x[(int64_t)t * n + k0 + 1]) : 0.f;
+          cpart[t] += convert_pair(L, x0 * g0, x1 * g1, tt, abuf + tb * kABytes);
+        }
+      }
+    }
+    wave_lds_fence();
+    v8i A[TB];
+    int sc[TB];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) load_a(abuf + tb * kABytes, mr, gr, A[tb], sc[tb]);
+    wave_lds_fence();
+#pragma unroll
+    for (int i = 0; i < S::CT; ++i) {
+      if (i < ntl) {
+        const uint32_t w = *reinterpret_cast<const LB_GLOBAL uint32_t*>(vdec + ((int64_t)c * nct + it.tile0 + i) * 256 +
+                                                                       lane * 4);
+        const v8i B = expand_signs(w);
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) acc[i][tb] = mfma(A[tb], B, acc[i][tb], sc[tb]);
+      }
+    }
+  }
+}
+
+template <int TM>
+__global__ void __launch_bounds__(kThreads, 3) k_decode_v(DecArgs a) {
+  using S = VShape<TM>;
+  constexpr int TB = S::TB, CT = S::CT;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const VItem it = a.vitems[blockIdx.x];
+  const DecEntry& Eg = a.entries[it.entry];
+  const int tid = threadIdx.x, lane = tid & 63, mr = lane & 15, gr = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int p = it.path;
+  // snapshot of the entry
+  const int n = Eg.n, nct = Eg.p[p].nct, xdirect = Eg.xdirect;
+  const LB_GLOBAL uint8_t* vdec = reinterpret_cast<const LB_GLOBAL uint8_t*>(gp(Eg.p[p].vdec));
+  const LB_GLOBAL uint8_t* gdec = reinterpret_cast<const LB_GLOBAL uint8_t*>(gp(Eg.gdec[p]));
+  const void* xv = a.xs ? a.xs[it.entry] : a.x0;
+  const LB_GLOBAL uint8_t* xb = reinterpret_cast<const LB_GLOBAL uint8_t*>(gp(xv)) + (int64_t)a.t0 * n * 2;
+  uint8_t* ring = lds + wave * kRingBytes;
+  uint8_t* abuf = lds + kWaves * kRingBytes + wave * TB * kABytes;
+  // this wave's chunks: a contiguous quarter of the item's
+  const int cw = (it.c1 - it.c0 + kWaves - 1) / kWaves;
+  const int ca = min(it.c0 + wave * cw, it.c1), cb = min(ca + cw, it.c1);
+
+  v4f acc[CT][TB];
+#pragma unroll
+  for (int c = 0; c < CT; ++c)
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) acc[c][tb] = v4f{0.f, 0.f, 0.f, 0.f};
+  float cpart[TM];
+#pragma unroll
+  for (int t = 0; t < TM; ++t) cpart[t] = 0.f;
+  if (ca < cb) {
+    if (xdirect) v_stream<TM>(a, it, n, nct, xb, gdec, vdec, ca, cb, ring, abuf, acc, cpart);
+    else v_plain<TM>(a, it, n, nct, xb, gdec, vdec, ca, cb, abuf, acc, cpart);
+  }
+
+  // fixed-order combine across waves in the (now idle) ring memory: wave 0
+  // stores, waves 1..3 add in turn; then the slot is written
+  float cw_[TM];
+#pragma unroll
+  for (int t = 0; t < TM; ++t) cw_[t] = wave_sum(cpart[t]);
+  float* red = reinterpret_cast<float*>(lds);      // [tile][token][16]
+  float* cred = red + CT * TM * 16;                // [token]
+  const int ntl = it.ntiles;
+  __syncthreads();
+  for (int wv = 0; wv < kWaves; ++wv) {
+    if (wave == wv) {
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+        if (c < ntl) {
+#pragma unroll
+          for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+            for (int qq = 0; qq < 2; ++qq) {
+              const int t = tb * 8 + 2 * gr + qq;
+              if (t < TM) {
+                float* dst = red + (c * TM + t) * 16 + mr;
+                const float d = acc[c][tb][2 * qq] + acc[c][tb][2 * qq + 1];
+                *dst = (wv == 0 ? 0.f : *dst) + d;
+              }
+            }
+        }
+      }
+      if (lane == 0) {
+#pragma unroll
+        for (int t = 0; t < TM; ++t) cred[t] = (wv == 0 ? 0.f : cred[t]) + cw_[t];
+      }
+    }
+    __syncthreads();
+  }
+  LB_GLOBAL float* slot = gp(a.part) + (int64_t)it.slot * decode_slot_floats(TM);
+  for (int i = tid; i < ntl * TM * 16; i += kThreads) slot[i] = red[i];
+  if (tid < TM) slot[CT * TM * 16 + tid] = cred[tid];
+}
+
+// ---------------------------------------------------------------------------
+// mid stage
+// ---------------------------------------------------------------------------
+// z' = (sum of the partial sums + correction) o l for one path of one entry,
+// written as the U stage's A operands: each 16-lane row takes one (token,
+// 32-latent block), lane sub holding latents 2 sub and 2 sub + 1 of it.  Every
+// block of the path's units is written (zeros past the rank).
+template <int TM>
+__global__ void __launch_bounds__(kThreads) k_decode_mid(DecArgs a) {
+  constexpr int TB = (TM + 7) / 8, CT = decode_v_tiles(TM), SF = decode_slot_floats(TM);
+  __shared__ float cblk[kDecodeMaxTokens * 4 * (LB_MAX_RANK / kChunk)];
+  const MItem it = a.mitems[blockIdx.x];
+  const DecEntry& E = a.entries[it.entry];
+  const int p = it.path, r = E.p[p].r, T = a.T;
+  const LB_GLOBAL uint16_t* lsc = gp(E.p[p].l);
+  const LB_GLOBAL float* part = gp(a.part);
+  const int ufirst = p ? E.ug.nu0 : 0;
+  const int nblk = 4 * ((r + kChunk - 1) / kChunk);
+  const int tid = threadIdx.x, row = tid >> 4, sub = tid & 15;
+  for (int u = row; u < T * nblk; u += 16) {
+    const int t = u / nblk, blk = u % nblk, tb = t / 8, tt = t % 8;
+    const int jj = 32 * blk + 2 * sub;             // latents jj, jj + 1
+    const ConvLane LK(((jj % kChunk) / 32) * 16 + sub);
+    float v[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int j = jj + q;
+      v[q] = 0.f;
+      if (j < r) {
+        const int tile = j / 16, col = j % 16, g = tile / it.gtiles, tl = tile - g * it.gtiles;
+        const LB_GLOBAL float* sp = part + (int64_t)(it.slot0 + g * it.nsplit) * SF;
+        float d = 0.f, c = 0.f;
+        for (int s = 0; s < it.nsplit; ++s) {
+          d += sp[(int64_t)s * SF + (tl * TM + t) * 16 + col];
+          c += sp[(int64_t)s * SF + CT * TM * 16 + t];
+        }
+        v[q] = (d + c) * f16f(lsc[j]) * LK.fcls;
+      }
+    }
+    uint8_t* ab = E.aimg + ((int64_t)(ufirst + jj / kChunk) * TB + tb) * kABytes;
+    const float cc = row16_sum(convert_pair(LK, v[0], v[1], tt, gp(ab)));
+    if (sub == 0) cblk[u] = cc;
+  }
+  __syncthreads();
+  if (tid < T) {
+    float s = 0.f;
+    for (int blk = 0; blk < nblk; ++blk) s += cblk[tid * nblk + blk];
+    gp(E.cval)[p * 16 + tid] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// U stage
+// ---------------------------------------------------------------------------
+template <int TM>
+struct UShape {
+  static constexpr int TB = (TM + 7) / 8;
+  static constexpr int KQQ = TM == 1 ? 1 : 2;          // token slots per lane and block
+  static constexpr int KST = TM > 8 ? 2 : 1;           // output stores per quad (8 tokens x 64 rows each)
+  static constexpr int NMAX = TB == 1 ? 8 : 4;         // most units with operands held in registers
+  static constexpr int STG = KST * 1024;               // staging bytes per wave
+  static constexpr size_t lds = (size_t)kWaves * (kRingBytes + STG);
+};
+
+// Stores of this quad staged behind the position-i wait: at consumer position
+// s (i = s mod P) the window of ops issued after step s's load holds the stores
+// of every quad that ended at a position in [s - kRing + 1, s - 1].
+__host__ __device__ constexpr int u_stores_in_window(int i, int P) {
+  return i >= kRing - 1 ? 0 : (kRing - 1 - i + P - 1) / P;
+}
+
+// Per-lane state shared by both U forms.
+template <int TM>
+struct UCtx {
+  static constexpr int TB = UShape<TM>::TB;
+  int m, T, np, nu0;
+  LB_GLOBAL uint16_t* y;
+  float cv[2][TB][2];                              // U correction sums of the lane's tokens
+};
+
+// part (+)= h (D_hi + D_lo + C_p); lane (mr, gr) holds MFMA rows 4 gr .. 4 gr + 3
+// = (hi, lo) of tokens tb * 8 + 2 gr + {0, 1}, column mr = output row
+template <int TB>
+__device__ __attribute__((always_inline)) inline void u_fold(const v4f (&acc)[4][TB], const float (&h)[4],
+                                                            const float (&cv)[TB][2], float (&part)[4][TB][2],
+                                                            bool first) {
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq) {
+        const float v = h[rt] * ((acc[rt][tb][2 * qq] + acc[rt][tb][2 * qq + 1]) + cv[tb][qq]);
+        part[rt][tb][qq] = first ? v : part[rt][tb][qq] + v;
+      }
+}
+
+// Element-wise stores of one quad (any m), then a wait for all of them.
+template <int TM>
+__device__ __attribute__((always_inline)) inline void u_store_plain(const UCtx<TM>& C, int q,
+                                                                   const float (&part)[4][UShape<TM>::TB][2]) {
+  const int lane = threadIdx.x & 63, mr = lane & 15, gr = lane >> 4;
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int tb = 0; tb < UShape<TM>::TB; ++tb)
+#pragma unroll
+      for (int qq = 0; qq < UShape<TM>::KQQ; ++qq) {
+        const int t = tb * 8 + 2 * gr + qq, i = 64 * q + 16 * rt + mr;
+        if (t < C.T && i < C.m) C.y[(int64_t)t * C.m + i] = bf16_bits(part[rt][tb][qq]);
+      }
+  vm_wait<0>();
+}
+
+// One quad's outputs through the wave's staging area: KST stores of 16 bytes
+// per lane (lane l: token 8 k + l / 8, rows 8 (l % 8) .. + 7).  Lanes past the
+// last token repeat its store (same address, same value).
+template <int TM>
+__device__ __attribute__((always_inline)) inline void u_store_staged(const UCtx<TM>& C, int q,
+                                                                    const float (&part)[4][UShape<TM>::TB][2],
+                                                                    uint8_t* stg) {
+  const int lane = threadIdx.x & 63, mr = lane & 15, gr = lane >> 4;
+  uint16_t* s16 = reinterpret_cast<uint16_t*>(stg);
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int tb = 0; tb < UShape<TM>::TB; ++tb)
+#pragma unroll
+      for (int qq = 0; qq < UShape<TM>::KQQ; ++qq) {
+        const int t = tb * 8 + 2 * gr + qq;
+        if (t < TM) s16[t * 64 + rt * 16 + mr] = bf16_bits(part[rt][tb][qq]);
+      }
+  wave_lds_fence();
+#pragma unroll
+  for (int k = 0; k < UShape<TM>::KST; ++k) {
+    const int t = min(8 * k + (lane >> 3), C.T - 1);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(stg + t * 128 + (lane & 7) * 16);
+    *reinterpret_cast<LB_GLOBAL u32x4*>(C.y + (int64_t)t * C.m + 64 * q + (lane & 7) * 8) = v;
+  }
+  wave_lds_fence();
+}
+
+// Fast form: NPC units, operands in registers, every read through the ring.
+// Steps per quad: the row scales, then one per unit.
+template <int TM, int NPC>
+__device__ __attribute__((always_inline)) inline void u_stream(const DecArgs& a, const DecEntry& Eg, UCtx<TM>& C,
+                                                              int qa, int qb, uint8_t* ring, uint8_t* stg) {
+  using S = UShape<TM>;
+  constexpr int TB = S::TB, P = NPC + 1;
+  const int lane = threadIdx.x & 63, mr = lane & 15, gr = lane >> 4;
+  const UGeom g = Eg.ug;
+  const LB_GLOBAL uint8_t* udec = reinterpret_cast<const LB_GLOBAL uint8_t*>(gp(Eg.udec));
+  const LB_GLOBAL uint8_t* hq = reinterpret_cast<const LB_GLOBAL uint8_t*>(gp(Eg.hq));
+  const LB_GLOBAL uint8_t* aimg = reinterpret_cast<const LB_GLOBAL uint8_t*>(gp(static_cast<const uint8_t*>(Eg.aimg)));
+  // byte offset of each step inside a quad's data (this lane's 16 bytes)
+  int uoff[NPC];
+#pragma unroll
+  for (int u = 0; u < NPC; ++u) {
+    const bool half = (u == g.nu0 - 1 && g.half0) || (u == g.nu - 1 && g.half1);
+    uoff[u] = (u < g.nu0 ? 1024 * u : g.uoff1 + 1024 * (u - g.nu0)) + (half ? (lane & 31) : lane) * 16;
+  }
+  const int hoff = (lane & 15) * 16;
+  // step k of the wave's sequence (k = (quad - qa) * P + i) lands in slot k % kRing
+  auto issue_at = [&](int quad, int i, int slot) __attribute__((always_inline)) {
+    const int q = min(quad, qb - 1);               // past the end: re-read the last quad
+    const LB_GLOBAL uint8_t* src = i == 0 ? hq + (int64_t)q * 256 + hoff : udec + (int64_t)q * g.qbytes + uoff[i > 0 ? i - 1 : 0];
+    dma16(src, ring + slot * 1024);
+  };
+#pragma unroll
+  for (int k = 0; k < kRing - 1; ++k) issue_at(qa + k / P, k % P, k);
+  // operands (rows past 2 T are never read: skip their loads)
+  v8i A[NPC][TB];
+  int sc[NPC][TB];
+#pragma unroll
+  for (int u = 0; u < NPC; ++u)
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      if (mr < 2 * C.T) load_a(aimg + (int64_t)(u * TB + tb) * kABytes, mr, gr, A[u][tb], sc[u][tb]);
+      else {
+        A[u][tb] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+        sc[u][tb] = 127;
+      }
+    }
+  vm_wait<0>();
+
+  const bool fast_store = (C.m & 7) == 0;
+  int s = 0;
+  for (int q = qa; q < qb; ++q) {
+    v4f acc[4][TB];
+    float h[2][4];
+    float part[4][TB][2];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) acc[rt][tb] = v4f{0.f, 0.f, 0.f, 0.f};
+    static_for<P>([&](auto I) __attribute__((always_inline)) {
+      constexpr int i = decltype(I)::value;
+      lds_wait();                                  // the slot reloaded next was read last step
+      issue_at(q + (i + kRing - 1) / P, (i + kRing - 1) % P, (s + kRing - 1) % kRing);
+      vm_wait<kRing - 1 + S::KST * u_stores_in_window(i, P)>();
+      const uint8_t* slot = ring + (s % kRing) * 1024;
+      ++s;
+      if constexpr (i == 0) {
+        const uint16_t* hs = reinterpret_cast<const uint16_t*>(slot);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          h[0][rt] = f16f(hs[rt * 16 + mr]);
+          h[1][rt] = f16f(hs[64 + rt * 16 + mr]);
+        }
+      } else {
+        constexpr int u = i - 1;
+        const u32x4 w = *reinterpret_cast<const u32x4*>(slot + lane * 16);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          const v8i B = expand_signs(w[rt]);
+#pragma unroll
+          for (int tb = 0; tb < TB; ++tb) acc[rt][tb] = mfma(A[u][tb], B, acc[rt][tb], sc[u][tb]);
+        }
+        if (u == C.nu0 - 1 && u < NPC - 1) {       // path 0 ends before the last unit: fold it
+          u_fold<TB>(acc, h[0], C.cv[0], part, true);
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) acc[rt][tb] = v4f{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+    });
+    if (C.np > 1) u_fold<TB>(acc, h[1], C.cv[1], part, false);
+    else u_fold<TB>(acc, h[0], C.cv[0], part, true);
+    if (fast_store && 64 * q + 64 <= C.m) u_store_staged<TM>(C, q, part, stg);
+    else u_store_plain<TM>(C, q, part);
+  }
+  vm_wait<0>();                                    // no direct-to-LDS load may still be in flight
+}
+
+// Plain form (more units than the fast form holds): plain loads, one unit at a time.
+template <int TM>
+__device__ __attribute__((always_inline)) inline void u_plain(const DecArgs& a, const DecEntry& Eg, UCtx<TM>& C,
+                                                             int qa, int qb) {
+  using S = UShape<TM>;
+  constexpr int TB = S::TB;
+  const int lane = threadIdx.x & 63, mr = lane & 15, gr = lane >> 4;
+  const UGeom g = Eg.ug;
+  const LB_GLOBAL uint8_t* udec = reinterpret_cast<const LB_GLOBAL uint8_t*>(gp(Eg.udec));
+  const LB_GLOBAL uint16_t* hq = gp(Eg.hq);
+  const LB_GLOBAL uint8_t* aimg = reinterpret_cast<const LB_GLOBAL uint8_t*>(gp(static_cast<const uint8_t*>(Eg.aimg)));
+  for (int q = qa; q < qb; ++q) {
+    v4f acc[4][TB];
+    float h[2][4];
+    float part[4][TB][2];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      h[0][rt] = f16f(hq[(int64_t)q * 128 + rt * 16 + mr]);
+      h[1][rt] = f16f(hq[(int64_t)q * 128 + 64 + rt * 16 + mr]);
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) acc[rt][tb] = v4f{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int u = 0; u < g.nu; ++u) {
+      const bool half = (u == g.nu0 - 1 && g.half0) || (u == g.nu - 1 && g.half1);
+      const int off = (u < g.nu0 ? 1024 * u : g.uoff1 + 1024 * (u - g.nu0)) + (half ? (lane & 31) : lane) * 16;
+      const u32x4 w = *reinterpret_cast<const LB_GLOBAL u32x4*>(udec + (int64_t)q * g.qbytes + off);
+      v8i A[TB];
+      int sc[TB];
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) load_a(aimg + (int64_t)(u * TB + tb) * kABytes, mr, gr, A[tb], sc[tb]);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const v8i B = expand_signs(w[rt]);
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) acc[rt][tb] = mfma(A[tb], B, acc[rt][tb], sc[tb]);
+      }
+      if (u == g.nu0 - 1 && u < g.nu - 1) {
+        u_fold<TB>(acc, h[0], C.cv[0], part, true);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+          for (int tb = 0; tb < TB; ++tb) acc[rt][tb] = v4f{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    if (C.np > 1) u_fold<TB>(acc, h[1], C.cv[1], part, false);
+    else u_fold<TB>(acc, h[0], C.cv[0], part, true);
+    u_store_plain<TM>(C, q, part);
+  }
+}
+
+template <int TM>
+__global__ void __launch_bounds__(kThreads, TM >= 16 ? 2 : 3) k_decode_u(DecArgs a) {
+  using S = UShape<TM>;
+  constexpr int TB = S::TB;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const UItem it = a.uitems[blockIdx.x];
+  const DecEntry& Eg = a.entries[it.entry];
+  const int lane = threadIdx.x & 63, gr = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int qa = min(it.q0 + wave * it.qw, it.q0 + it.nq), qb = min(qa + it.qw, it.q0 + it.nq);
+  if (qa >= qb) return;                            // no barrier below: idle waves may leave
+  UCtx<TM> C;
+  C.m = Eg.m;
+  C.T = a.T;
+  C.np = Eg.np;
+  C.nu0 = Eg.ug.nu0;
+  void* yv = a.xs ? a.ys[it.entry] : a.y0;
+  C.y = gp(reinterpret_cast<uint16_t*>(yv)) + (int64_t)a.t0 * C.m;
+  const LB_GLOBAL float* cval = gp(Eg.cval);
 #pragma unroll
   for (int p = 0; p < 2; ++p)
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int t = tb * 8 + 2 * gr + q;
-        float sum = 0.f;
-        if (p < np && t < T && t < TM)
-          for (int g = 0; g < (p ? nvg1 : nvg0); ++g) sum += gp(cpart)[(p * kMaxGroups + g) * 16 + t];
-        cval[p][tb][q] = sum;
+      for (int qq = 0; qq < 2; ++qq) {
+        const int t = tb * 8 + 2 * gr + qq;
+        C.cv[p][tb][qq] = (p < C.np && t < C.T && t < TM) ? cval[p * 16 + t] : 0.f;
       }
-  constexpr int NA = NPC > 0 ? NPC : 1;
-  v8i A[NA][TB];
-  int sc[NA][TB];
-  auto load_img = [&](int u, v8i* Au, int* su) __attribute__((always_inline)) {
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb) load_a(aimg + (int64_t)(u * TB + tb) * kABytes, mr, gr, Au[tb], su[tb]);
-  };
-
-  // issue cursor: batch ib; unit iu (-1: the batch's row-scale step); quad ij
-  int ib = 0, iu = -1, ij = 0;
-  const LB_GLOBAL uint8_t* last = ubase + lane * 16;
-  auto issue = [&](int slot) __attribute__((always_inline)) {
-    if (ib < nb) {
-      if (iu < 0) {
-        // row scales: lane l -> quad (l / 16) % kQW of the batch, path (l / 8) % 2, rows 8 (l % 8) .. + 7
-        const int jj = min(ib * kQW + (lane >> 4) % kQW, nmine - 1);
-        last = ((lane >> 3) & 1 ? hb1 : hb0) + (int64_t)quad(jj) * 128 + (lane & 7) * 16;
-        iu = 0;
-      } else {
-        const int w0 = iu < npc0 ? 4 * iu : woff1 + 4 * (iu - npc0);
-        last = ubase + ((int64_t)quad(ib * kQW + ij) * uw + w0) * 256 + lane * 16;
-        if (++ij == kQW || ib * kQW + ij >= nmine) {
-          ij = 0;
-          if (++iu == npc) {
-            iu = -1;
-            ++ib;
-          }
-        }
-      }
-    }
-    dma16(last, ring + slot * 1024);
-  };
-
-  // prologue: the first kUDepth - 1 steps, then the operands; one wait covers all
-#pragma unroll
-  for (int k = 0; k < kUDepth - 1; ++k) issue(k);
-  if (NPC > 0) {
-#pragma unroll
-    for (int u = 0; u < NA; ++u) load_img(u, A[u], sc[u]);
-  }
-  vm_wait<0>();
-
-  v4f acc[kQW][4][TB];
-  float part[kQW][4][TB][2];
-  uint32_t hraw[kQW][4];                           // (h0 | h1 << 16) of row mr of each row tile
-  auto zero_acc = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int j = 0; j < kQW; ++j)
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int tb = 0; tb < TB; ++tb) acc[j][rt][tb] = v4f{0.f, 0.f, 0.f, 0.f};
-  };
-  // part (+)= h_p (D_hi + D_lo + C_p); lane (mr, gr) holds MFMA rows 4 gr .. 4 gr + 3
-  // = (hi, lo) of tokens tb * 8 + 2 gr + {0, 1}, column mr = output row
-  auto fold = [&](int p, bool first) __attribute__((always_inline)) {
-#pragma unroll
-    for (int j = 0; j < kQW; ++j)
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        const float h = f16f((uint16_t)(p ? hraw[j][rt] >> 16 : hraw[j][rt] & 0xffff));
-#pragma unroll
-        for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-          for (int qq = 0; qq < 2; ++qq) {
-            const float v = h * ((acc[j][rt][tb][2 * qq] + acc[j][rt][tb][2 * qq + 1]) + cval[p][tb][qq]);
-            part[j][rt][tb][qq] = first ? v : part[j][rt][tb][qq] + v;
-          }
-      }
-  };
-
-  // consumer: waits for step s's slot (see above) and returns it
-  int s = 0, since_store = kUDepth;
-  auto next_step = [&]() __attribute__((always_inline)) {
-    lds_reads_wait();                              // the slot reloaded next was read last step
-    issue((s + kUDepth - 1) % kUDepth);
-    if (since_store < kUDepth - 2) vm_wait<kUDepth - 2 + kStores>();
-    else vm_wait<kUDepth - 2>();
-    ++since_store;
-    const uint8_t* slot = ring + (s % kUDepth) * 1024;
-    ++s;
-    return slot;
-  };
-  auto unit = [&](int b, int u, const v8i* Au, const int* su) __attribute__((always_inline)) {
-    if (u == npc0 && u > 0) {                      // path 1 starts: fold path 0
-      fold(0, true);
-      zero_acc();
-    }
-#pragma unroll
-    for (int j = 0; j < kQW; ++j) {
-      if (valid(b, j)) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(next_step() + lane * 16);
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          const v8i B = expand_signs(w[rt]);
-#pragma unroll
-          for (int tb = 0; tb < TB; ++tb) acc[j][rt][tb] = mfma(Au[tb], B, acc[j][rt][tb], su[tb]);
-        }
-      }
-    }
-  };
-  for (int b = 0; b < nb; ++b) {
-    {  // the batch's row scales: [quad j][path][64 rows] fp16 in the slot
-      const uint16_t* hs = reinterpret_cast<const uint16_t*>(next_step());
-#pragma unroll
-      for (int j = 0; j < kQW; ++j)
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-          hraw[j][rt] = (uint32_t)hs[(j * 2) * 64 + rt * 16 + mr] | ((uint32_t)hs[(j * 2 + 1) * 64 + rt * 16 + mr] << 16);
-    }
-    zero_acc();
-    if (NPC > 0) {
-#pragma unroll
-      for (int u = 0; u < NA; ++u) unit(b, u, A[u], sc[u]);
-    } else {
-      for (int u = 0; u < npc; ++u) {
-        load_img(u, A[0], sc[0]);
-        vm_wait<0>();                              // (keeps the count exact; the slow path)
-        unit(b, u, A[0], sc[0]);
-      }
-    }
-    if (npc0 < npc) fold(1, false);
-    else fold(0, true);
-    // y: lane (mr, gr) holds tokens tb * 8 + 2 gr + {0, 1} of output row mr of each row
-    // tile; every store is issued (kStores of them), lanes without an output hit the sink
-#pragma unroll
-    for (int j = 0; j < kQW; ++j)
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        const int i = (4 * quad(b * kQW + j) + rt) * 16 + mr;
-#pragma unroll
-        for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-          for (int qq = 0; qq < kQQ; ++qq) {
-            const int t = tb * 8 + 2 * gr + qq;
-            const bool ok = valid(b, j) && i < m && t < T;
-            LB_GLOBAL uint16_t* dst = ok ? y + (uint32_t)(t * m + i) : sink + (gr & 3) * 2 + qq;
-            *dst = bf16_bits(part[j][rt][tb][qq]);
-          }
-      }
-    since_store = 0;
-  }
-  vm_wait<0>();                                    // no direct-to-LDS load may still be in flight
-}
-
-template <int TM>
-__global__ void __launch_bounds__(kThreads, 2) k_decode_u(DecArgs a) {
-  constexpr int TB = (TM + 7) / 8;
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  const UItem it = a.uitems[blockIdx.x];
-  uint8_t* ring = lds + (threadIdx.x >> 6) * (kUDepth * 1024);
-  int e = (int)it.entry, qa = (int)it.quad0, left = (int)it.count;
-  while (left > 0 && e < a.nentries) {
-    const DecEntry& Eg = a.entries[e];
-    const int nq = (Eg.nrt + 3) / 4;
-    const int qb = min(nq, qa + left);
-    const int npc = Eg.npc;
-    if (TB == 1) {
-      switch (npc) {
-        case 1: u_segment<TM, 1>(a, Eg, e, qa, qb, ring); break;
-        case 2: u_segment<TM, 2>(a, Eg, e, qa, qb, ring); break;
-        case 3: u_segment<TM, 3>(a, Eg, e, qa, qb, ring); break;
-        case 4: u_segment<TM, 4>(a, Eg, e, qa, qb, ring); break;
-        case 5: u_segment<TM, 5>(a, Eg, e, qa, qb, ring); break;
-        case 6: u_segment<TM, 6>(a, Eg, e, qa, qb, ring); break;
-        case 7: u_segment<TM, 7>(a, Eg, e, qa, qb, ring); break;
-        case 8: u_segment<TM, 8>(a, Eg, e, qa, qb, ring); break;
-        default: u_segment<TM, 0>(a, Eg, e, qa, qb, ring); break;
-      }
-    } else {
-      switch (npc) {
-        case 1: u_segment<TM, 1>(a, Eg, e, qa, qb, ring); break;
-        case 2: u_segment<TM, 2>(a, Eg, e, qa, qb, ring); break;
-        case 3: u_segment<TM, 3>(a, Eg, e, qa, qb, ring); break;
-        case 4: u_segment<TM, 4>(a, Eg, e, qa, qb, ring); break;
-        default: u_segment<TM, 0>(a, Eg, e, qa, qb, ring); break;
-      }
-    }
-    left -= qb - qa;
-    qa = 0;
-    ++e;
-  }
-}
-
-size_t decode_lds_bytes(int T) {
-  const int tb = (decode_bucket(T) + 7) / 8;
-  return (size_t)kWaves * tb * kABytes + (size_t)decode_ct_max(T) * tb * 256 * 4 + (16 + 16 * 32) * 4;
+  uint8_t* ring = lds + wave * kRingBytes;
+  uint8_t* stg = lds + kWaves * kRingBytes + wave * S::STG;
+  const int nu = Eg.ug.nu;
+  static_for<S::NMAX>([&](auto I) __attribute__((always_inline)) {
+    constexpr int k = decltype(I)::value + 1;
+    if (nu == k) u_stream<TM, k>(a, Eg, C, qa, qb, ring, stg);
+  });
+  if (nu > S::NMAX) u_plain<TM>(a, Eg, C, qa, qb);
 }
 
 }  // namespace
 
 hipError_t launch_decode_v(const DecArgs& a, int nitems, hipStream_t st) {
   if (nitems <= 0) return hipSuccess;
-  const int tm = decode_bucket(a.T);
-  const size_t lds = decode_lds_bytes(a.T);
-  switch (tm) {
-    case 1: hipLaunchKernelGGL(k_decode_v<1>, dim3(nitems), dim3(kThreads), lds, st, a); break;
-    case 2: hipLaunchKernelGGL(k_decode_v<2>, dim3(nitems), dim3(kThreads), lds, st, a); break;
-    case 4: hipLaunchKernelGGL(k_decode_v<4>, dim3(nitems), dim3(kThreads), lds, st, a); break;
-    case 8: hipLaunchKernelGGL(k_decode_v<8>, dim3(nitems), dim3(kThreads), lds, st, a); break;
-    default: hipLaunchKernelGGL(k_decode_v<16>, dim3(nitems), dim3(kThreads), lds, st, a); break;
+  switch (decode_bucket(a.T)) {
+    case 1: hipLaunchKernelGGL(k_decode_v<1>, dim3(nitems), dim3(kThreads), VShape<1>::lds, st, a); break;
+    case 2: hipLaunchKernelGGL(k_decode_v<2>, dim3(nitems), dim3(kThreads), VShape<2>::lds, st, a); break;
+    case 4: hipLaunchKernelGGL(k_decode_v<4>, dim3(nitems), dim3(kThreads), VShape<4>::lds, st, a); break;
+    case 8: hipLaunchKernelGGL(k_decode_v<8>, dim3(nitems), dim3(kThreads), VShape<8>::lds, st, a); break;
+    default: hipLaunchKernelGGL(k_decode_v<16>, dim3(nitems), dim3(kThreads), VShape<16>::lds, st, a); break;
   }
   return hipGetLastError();
 }
 
-size_t decode_u_lds_bytes(const int* npc, int count, int T) {
-  (void)npc;
-  (void)count;
-  (void)T;
-  return (size_t)kWaves * kUDepth * 1024;
-}
-
-int decode_u_slots() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus <= 0)
-    cus = 256;
-  return cus * kUSlotsPerCU;
-}
-
-hipError_t launch_decode_u(const DecArgs& a, int nitems, size_t lds, hipStream_t st) {
+hipError_t launch_decode_mid(const DecArgs& a, int nitems, hipStream_t st) {
   if (nitems <= 0) return hipSuccess;
   switch (decode_bucket(a.T)) {
-    case 1: hipLaunchKernelGGL(k_decode_u<1>, dim3(nitems), dim3(kThreads), lds, st, a); break;
-    case 2: hipLaunchKernelGGL(k_decode_u<2>, dim3(nitems), dim3(kThreads), lds, st, a); break;
-    case 4: hipLaunchKernelGGL(k_decode_u<4>, dim3(nitems), dim3(kThreads), lds, st, a); break;
-    case 8: hipLaunchKernelGGL(k_decode_u<8>, dim3(nitems), dim3(kThreads), lds, st, a); break;
-    default: hipLaunchKernelGGL(k_decode_u<16>, dim3(nitems), dim3(kThreads), lds, st, a); break;
+    case 1: hipLaunchKernelGGL(k_decode_mid<1>, dim3(nitems), dim3(kThreads), 0, st, a); break;
+    case 2: hipLaunchKernelGGL(k_decode_mid<2>, dim3(nitems), dim3(kThreads), 0, st, a); break;
+    case 4: hipLaunchKernelGGL(k_decode_mid<4>, dim3(nitems), dim3(kThreads), 0, st, a); break;
+    case 8: hipLaunchKernelGGL(k_decode_mid<8>, dim3(nitems), dim3(kThreads), 0, st, a); break;
+    default: hipLaunchKernelGGL(k_decode_mid<16>, dim3(nitems), dim3(kThreads), 0, st, a); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_u(const DecArgs& a, int nitems, hipStream_t st) {
+  if (nitems <= 0) return hipSuccess;
+  switch (decode_bucket(a.T)) {
+    case 1: hipLaunchKernelGGL(k_decode_u<1>, dim3(nitems), dim3(kThreads), UShape<1>::lds, st, a); break;
+    case 2: hipLaunchKernelGGL(k_decode_u<2>, dim3(nitems), dim3(kThreads), UShape<2>::lds, st, a); break;
+    case 4: hipLaunchKernelGGL(k_decode_u<4>, dim3(nitems), dim3(kThreads), UShape<4>::lds, st, a); break;
+    case 8: hipLaunchKernelGGL(k_decode_u<8>, dim3(nitems), dim3(kThreads), UShape<8>::lds, st, a); break;
+    default: hipLaunchKernelGGL(k_decode_u<16>, dim3(nitems), dim3(kThreads), UShape<16>::lds, st, a); break;
   }
   return hipGetLastError();
 }

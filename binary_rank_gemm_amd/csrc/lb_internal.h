@@ -16,9 +16,8 @@ namespace lb {
 //     Lane l of tile (kc, ct) holds column j = 16 ct + l%16 and the 32 rows
 //     k = 128 kc + 32 (l/16) + e, e = 8 v + q (v = 0..3, q = 0..7), with the
 //     sign of row k at bit 4 q + 3 - v (bit set <=> -1).
-//   U: [rt = m/16 row tiles][path][w = 0..W_p-1][16 rows] uint32, where word w
-//     of output row i is canonical word w of that row with its bits permuted
-//     the same way (latent j = 32 w + e at bit 4 q + 3 - v).
+//   U: see UGeom; word w of output row i is canonical word w of that row
+//     with its bits permuted the same way (latent j = 32 w + e at bit 4 q + 3 - v).
 // ---------------------------------------------------------------------------
 constexpr int kChunk = 128;   // K extent of one MFMA
 constexpr int kTile = 16;     // M/N extent of one MFMA
@@ -36,69 +35,105 @@ struct PathDev {
   int r, W, nct;
 };
 
+constexpr int kABytes = 2048 + 64;      // one fp8 A operand image: 16 rows x 4 groups x 32 B + scales
+constexpr int kDmaPad = 1024;           // slack after buffers read by 1 KB direct-to-LDS loads
+
+// Decode U layout of one linear: quads of 64 output rows; inside a quad, each
+// path's 128-latent units in order, 1 KB each ([4 words][16 rows][4 row tiles]
+// uint32, so that lane 16 w + row of a 64-lane load gets the four row tiles'
+// word w), except that the last unit of a path is 512 B (words 0 and 1 only)
+// when the path's rank leaves at most 64 latents in it.
+struct UGeom {
+  int nq;            // quads
+  int nu0, nu;       // units of path 0; units of both paths
+  int half0, half1;  // the last unit of path 0 / path 1 is a half unit
+  int uoff1;         // byte offset of path 1's first unit inside a quad
+  int qbytes;        // bytes of one quad
+};
+inline UGeom u_geom(int64_t m, const int64_t* r, int np) {
+  UGeom g{};
+  g.nq = (int)((m + 63) / 64);
+  int bytes[2] = {0, 0}, nu[2] = {0, 0}, half[2] = {0, 0};
+  for (int p = 0; p < np; ++p) {
+    nu[p] = (int)((r[p] + kChunk - 1) / kChunk);
+    const int rem = (int)(r[p] % kChunk);
+    half[p] = rem != 0 && rem <= kChunk / 2;
+    bytes[p] = nu[p] * 1024 - half[p] * 512;
+  }
+  g.nu0 = nu[0];
+  g.nu = nu[0] + nu[1];
+  g.half0 = half[0];
+  g.half1 = half[1];
+  g.uoff1 = bytes[0];
+  g.qbytes = bytes[0] + bytes[1];
+  return g;
+}
+inline size_t decode_u_bytes(const UGeom& g) { return (size_t)g.nq * g.qbytes + kDmaPad; }
+// row scales of both paths per quad: [quad][path][64 rows] fp16
+inline size_t decode_h_bytes(const UGeom& g) { return (size_t)g.nq * 256 + kDmaPad; }
+
 // One entry of a decode launch: a linear plus its activations.
 struct DecEntry {
   PathDev p[2];
-  const uint32_t* udec;    // decode U layout, both paths
-  uint8_t* aimg;           // U-stage fp8 A operand images [npc][tb][kABytes], written by the V stage
-  float* cpart;            // U-stage C partial sums [np][kMaxGroups][16], written by the V stage
-  int m, n, np, nkc, nrt, uw;   // uw = sum_p W_p (words per row, U layout)
-  int vct[2];              // column tiles per V work item, per path
-  int nvg[2];              // V work items (column groups) per path
-  int woff[2];             // word offset of each path inside a U-layout row
-  int pcoff[2];            // first 128-latent chunk of each path in aimg
-  int npc;                 // chunks over both paths
+  const uint16_t* gdec[2];   // g of each path, zero-padded to whole 128-row chunks
+  const uint8_t* udec;       // decode U layout (UGeom)
+  const uint16_t* hq;        // row scales per quad
+  uint8_t* aimg;             // U-stage fp8 A operands [unit][tb][kABytes] (written by the mid kernel)
+  float* cval;               // U-stage correction sums [path][16 tokens] (written by the mid kernel)
+  int m, n, np, nkc;
+  int xdirect;               // n % 8 == 0: rows of x are read with 16-byte loads
+  UGeom ug;
 };
 
-constexpr int kMaxGroups = 32;          // column groups per path (rank <= 4096, >= 8 tiles per group)
-constexpr int kABytes = 2048 + 64;      // one fp8 A operand image: 16 rows x 4 groups x 32 B + scales
-
-// Work item: V stage (entry, path, column group) or U stage (entry, 16 row tiles).
-struct WorkItem {
-  uint32_t entry;
-  uint16_t path;
-  uint16_t group;
+// V-stage work item (one workgroup): column tiles [tile0, tile0 + ntiles) of
+// one path over chunks [c0, c1) of 128 input rows; its partial sums go to
+// partial slot `slot`.
+struct VItem {
+  int entry, path, tile0, ntiles, c0, c1, slot, pad;
+};
+// Mid-stage work item (one workgroup): one path of one entry; its V items are
+// `ngroups` column groups of `gtiles` tiles, each split into `nsplit` chunk
+// ranges, with partial slots slot0 + group * nsplit + split.
+struct MItem {
+  int entry, path, slot0, ngroups, nsplit, gtiles, pad0, pad1;
+};
+// U-stage work item (one workgroup): quads [q0, q0 + nq) of one entry, qw
+// consecutive quads per wave.
+struct UItem {
+  int entry, q0, nq, qw;
 };
 
 constexpr int kWavesPerGroup = 4;   // waves of a decode workgroup
 
-// U-stage work item: a contiguous run of `count` quads (4 row tiles each) of the
-// concatenated entries, starting at quad `quad0` of entry `entry`.
-struct UItem {
-  uint32_t entry, quad0, count, pad;
-};
-
-// Launch-wide arguments of the two decode kernels.
+// Launch-wide arguments of the decode kernels.
 struct DecArgs {
   const DecEntry* entries;
   const void* const* xs;   // per entry input (device array), or null: use x0 / y0
   void* const* ys;         // per entry output
   const void* x0;          // single-entry input when xs is null
   void* y0;
-  const WorkItem* items;   // V items, one workgroup each
-  const UItem* uitems;     // U items, one workgroup each
-  uint16_t* sink;          // write target of output lanes that hold no output (256 B per U wave)
-  int nentries;
+  const VItem* vitems;
+  const MItem* mitems;
+  const UItem* uitems;
+  float* part;             // V-stage partial sums, decode_slot_floats(bucket) per slot
   int T, t0;               // tokens in this launch and the offset of its first token
 };
 
 // Tokens one decode launch handles (token blocks of 8, at most 2 blocks).
 constexpr int kDecodeMaxTokens = 16;
-constexpr int kDecodeRowTilesPerItem = 64;   // U work item = 1024 output rows
-// U work items: batches of quads (4 row tiles); a batch is 4 quads per wave (2
-// at 16 tokens) and an item holds kDecodeUBatches batches of all 4 waves
-constexpr int kDecodeUBatches = 1;
-__host__ __device__ constexpr int decode_u_quads_per_item(int bucket) { return bucket >= 16 ? 8 : 16; }
-__host__ __device__ constexpr int decode_u_item_quads(int bucket) { return decode_u_quads_per_item(bucket) * kDecodeUBatches; }
-constexpr int kDmaPad = 1024;                // slack after buffers read by 1 KB direct-to-LDS loads
-// bytes of the decode U layout: quads of 4 row tiles x uw words x 16 rows x 4 B, plus slack
-__host__ __device__ inline size_t decode_u_bytes(int nrt, int uw) {
-  return (size_t)((nrt + 3) / 4) * uw * 256 + kDmaPad;
+// Token-count bucket of a decode launch (per-token state is sized by it).
+__host__ __device__ inline constexpr int decode_bucket(int T) {
+  return T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : T <= 8 ? 8 : 16;
 }
-// Token-count bucket of a decode launch (per-token state is sized by it) and the
-// most column tiles one V work item holds at that bucket.
-__host__ __device__ inline int decode_bucket(int T) { return T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : T <= 8 ? 8 : 16; }
-__host__ __device__ inline int decode_ct_max(int T) { return decode_bucket(T) >= 8 ? 8 : 16; }
+// Column tiles of one V item, and the floats of one partial slot:
+// [tile][token][16 columns] sums, then 16 correction sums.
+__host__ __device__ inline constexpr int decode_v_tiles(int bucket) { return bucket >= 16 ? 12 : 20; }
+__host__ __device__ inline constexpr int decode_slot_floats(int bucket) {
+  return decode_v_tiles(bucket) * 16 * bucket + 16;
+}
+// Sizes the planner aims at per V and U work item (bytes of sign words).
+constexpr int kDecodeVItemBytes = 96 * 1024;
+constexpr int kDecodeUItemBytes = 96 * 1024;
 
 // ---------------------------------------------------------------------------
 // kernel launchers (defined in the .hip files)
@@ -107,21 +142,19 @@ hipError_t launch_validate_signs(const int8_t* s, int64_t count, int* bad_flag, 
 hipError_t launch_pack_signs(const int8_t* s, int64_t rows, int64_t rank, uint32_t* out, hipStream_t st);
 hipError_t launch_unpack_signs(const uint32_t* w, int64_t rows, int64_t rank, int8_t* out, hipStream_t st);
 hipError_t launch_retile_v_decode(const uint32_t* vcan, int n, int r, uint32_t* vdec, hipStream_t st);
-hipError_t launch_retile_u_decode(const uint32_t* ucan, int m, int r, int W, int uw, int woff,
-                                  uint32_t* udec, hipStream_t st);
 
 // fp32 exact path: z' then y, one linear
 hipError_t launch_exact(const PathDev* p, int np, int m, int n, const void* x, void* y, int T,
                         int io_fp32, float* zbuf, int rpad, hipStream_t st);
 
-// decode path: V-stage kernel then U-stage kernel, one workgroup per work item
+// decode path: V stage, mid stage, U stage, one workgroup per work item
 hipError_t launch_decode_v(const DecArgs& a, int nitems, hipStream_t st);
-hipError_t launch_decode_u(const DecArgs& a, int nitems, size_t lds_bytes, hipStream_t st);
-// Workgroups of the U-stage kernel that run at once on the current device, and
-// U items per such slot (several, so that slots that stream faster take more).
-int decode_u_slots();
-constexpr int kDecodeUItemsPerSlot = 1;
-// LDS bytes of a U-stage launch over entries with npc[e] 128-latent units each
-size_t decode_u_lds_bytes(const int* npc, int count, int T);
+hipError_t launch_decode_mid(const DecArgs& a, int nitems, hipStream_t st);
+hipError_t launch_decode_u(const DecArgs& a, int nitems, hipStream_t st);
+// layouts of the decode U stage (built once per linear)
+hipError_t launch_decode_u_layout(const uint32_t* ucan0, const uint32_t* ucan1, int m, const int* W, const UGeom& g,
+                                  uint8_t* udec, hipStream_t st);
+hipError_t launch_decode_h_layout(const uint16_t* h0, const uint16_t* h1, int m, int nq, uint16_t* hq,
+                                  hipStream_t st);
 
 }  // namespace lb

@@ -68,25 +68,47 @@ __global__ void k_retile_v(const uint32_t* __restrict__ vcan, int n, int r, int 
   vdec[idx] = word;
 }
 
-// Decode U layout for one path: row tiles of 16 rows in quads, word-major inside
-// a quad: element (quad, woff + w, row, rt % 4) = permuted canonical word of row
-// 16 rt + row.  One (quad, 4 consecutive words) block is 1 KB: the 16 rows x 4
-// words x 4 row tiles one MFMA step of the decode U stage consumes.
-__global__ void k_retile_u(const uint32_t* __restrict__ ucan, int m, int W, int uw, int woff, int nrt,
-                           uint32_t* __restrict__ udec) {
-  int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  int64_t total = (int64_t)nrt * W * 16;
-  if (idx >= total) return;
-  int row = (int)(idx % 16);
-  int w = (int)((idx / 16) % W);
-  int rt = (int)(idx / (16 * (int64_t)W));
-  int64_t i = (int64_t)16 * rt + row;
+// Decode U layout (UGeom): one thread per uint32 of every quad's blocks.
+// Thread (quad, unit u, lane l = 16 w + row, rt) writes word 4 u' + w of output
+// row 64 quad + 16 rt + row of the unit's path (u' = unit inside the path),
+// bit-permuted; words past the path's rank and rows past m are zero.  Half
+// units hold words 0 and 1 only.
+__global__ void k_u_layout(const uint32_t* __restrict__ u0, const uint32_t* __restrict__ u1, int m, int W0, int W1,
+                           UGeom g, uint8_t* __restrict__ udec) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_quad = (int64_t)g.nu * 256;   // threads per quad (64 lanes x 4 row tiles per unit)
+  if (idx >= (int64_t)g.nq * per_quad) return;
+  const int q = (int)(idx / per_quad);
+  const int rem = (int)(idx % per_quad);
+  const int u = rem / 256, l = (rem % 256) / 4, rt = rem % 4;
+  const int p = u < g.nu0 ? 0 : 1;
+  const int up = p ? u - g.nu0 : u;
+  const bool half = p ? (g.half1 && u == g.nu - 1) : (g.half0 && u == g.nu0 - 1);
+  if (half && l >= 32) return;
+  const int w = l / 16, row = l % 16;
+  const int word = 4 * up + w;
+  const int W = p ? W1 : W0;
+  const uint32_t* uc = p ? u1 : u0;
+  const int64_t i = (int64_t)64 * q + 16 * rt + row;
   uint32_t out = 0;
-  if (i < m) {
-    uint32_t in = ucan[i * W + w];
+  if (i < m && word < W) {
+    const uint32_t in = uc[i * W + word];
     for (int e = 0; e < 32; ++e) out |= ((in >> e) & 1u) << fp4_bit_of_elem(e);
   }
-  udec[(((int64_t)(rt >> 2) * uw + woff + w) * 16 + row) * 4 + (rt & 3)] = out;
+  const int uoff = p ? g.uoff1 + 1024 * up : 1024 * up;
+  *reinterpret_cast<uint32_t*>(udec + (int64_t)q * g.qbytes + uoff + (l * 4 + rt) * 4) = out;
+}
+
+// Row scales per quad: hq[quad][path][64] = h_path[64 quad + i] (zero past m
+// and for a missing second path).
+__global__ void k_h_layout(const uint16_t* __restrict__ h0, const uint16_t* __restrict__ h1, int m, int nq,
+                           uint16_t* __restrict__ hq) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)nq * 128) return;
+  const int q = (int)(idx / 128), p = (int)((idx / 64) % 2), i = (int)(idx % 64);
+  const int64_t row = (int64_t)64 * q + i;
+  const uint16_t* h = p ? h1 : h0;
+  hq[idx] = (h && row < m) ? h[row] : (uint16_t)0;
 }
 
 }  // namespace
@@ -118,12 +140,18 @@ hipError_t launch_retile_v_decode(const uint32_t* vcan, int n, int r, uint32_t* 
   return hipGetLastError();
 }
 
-hipError_t launch_retile_u_decode(const uint32_t* ucan, int m, int r, int W, int uw, int woff,
-                                  uint32_t* udec, hipStream_t st) {
-  (void)r;
-  int nrt = (m + kTile - 1) / kTile;
-  int64_t total = (int64_t)nrt * W * 16;
-  hipLaunchKernelGGL(k_retile_u, dim3(blocks_for(total)), dim3(kThreads), 0, st, ucan, m, W, uw, woff, nrt, udec);
+hipError_t launch_decode_u_layout(const uint32_t* ucan0, const uint32_t* ucan1, int m, const int* W, const UGeom& g,
+                                  uint8_t* udec, hipStream_t st) {
+  const int64_t total = (int64_t)g.nq * g.nu * 256;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_u_layout, dim3(blocks_for(total)), dim3(kThreads), 0, st, ucan0, ucan1, m, W[0], W[1], g, udec);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_h_layout(const uint16_t* h0, const uint16_t* h1, int m, int nq, uint16_t* hq,
+                                  hipStream_t st) {
+  const int64_t total = (int64_t)nq * 128;
+  hipLaunchKernelGGL(k_h_layout, dim3(blocks_for(total)), dim3(kThreads), 0, st, h0, h1, m, nq, hq);
   return hipGetLastError();
 }
 
