@@ -256,10 +256,12 @@ lb_status build_decode_plan(DecodePlan& P, const lb_linear* L, int count, int T,
     cv_off[e] = work_bytes;
     work_bytes += align256(2 * 16 * sizeof(float));
     const double qbytes = E.ug.qbytes + 256.0;
-    const int qw = std::max(1, (int)std::lround(kDecodeUItemBytes / (kWavesPerGroup * qbytes)));
+    const int qw = std::max(1, std::min(decode_u_qw_max(bucket),
+                                        (int)std::lround(kDecodeUItemBytes / (kWavesPerGroup * qbytes))));
     for (int q0 = 0; q0 < E.ug.nq; q0 += kWavesPerGroup * qw) {
       const int nq = std::min(kWavesPerGroup * qw, E.ug.nq - q0);
-      ul.push_back({nq * qbytes, UItem{e, q0, nq, qw}});
+      // a short run (small entries, the last run) is spread over all four waves
+      ul.push_back({nq * qbytes, UItem{e, q0, nq, (nq + kWavesPerGroup - 1) / kWavesPerGroup}});
     }
   }
   work_bytes += kDmaPad;

@@ -63,6 +63,23 @@ template <class T>
 __device__ inline LB_GLOBAL T* gp(T* p) { return (LB_GLOBAL T*)p; }
 template <class T>
 __device__ inline const LB_GLOBAL T* gp(const T* p) { return (const LB_GLOBAL T*)p; }
+// Launch-constant tables (work items, entries, pointer arrays) are read as
+// constant memory, so uniform reads of them become scalar loads instead of
+// vector loads queued behind the streaming traffic.
+#define LB_CONST __attribute__((address_space(4)))
+template <class T>
+__device__ inline const LB_CONST T* cp(const T* p) { return (const LB_CONST T*)p; }
+// copy of a constant-memory struct (word by word: copy constructors take generic references)
+template <class T>
+__device__ inline T cld(const LB_CONST T* p) {
+  static_assert(sizeof(T) % 4 == 0, "word-sized struct");
+  T v;
+  const LB_CONST int* src = (const LB_CONST int*)p;
+  int* dst = reinterpret_cast<int*>(&v);
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(T) / 4); ++i) dst[i] = src[i];
+  return v;
+}
 
 __device__ inline float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 __device__ inline float f16f(uint16_t b) { return __half2float(__ushort_as_half(b)); }
@@ -184,7 +201,7 @@ __device__ inline void load_a(Ptr ab, int mr, int gr, v8i& a, int& sc) {
 // ---------------------------------------------------------------------------
 // Ring of direct-to-LDS loads (one per wave)
 // ---------------------------------------------------------------------------
-constexpr int kRing = 8;                   // 1 KB slots per wave
+constexpr int kRing = 10;                  // 1 KB slots per wave
 constexpr int kRingBytes = kRing * 1024;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -402,8 +419,8 @@ __global__ void __launch_bounds__(kThreads, 3) k_decode_v(DecArgs a) {
   using S = VShape<TM>;
   constexpr int TB = S::TB, CT = S::CT;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  const VItem it = a.vitems[blockIdx.x];
-  const DecEntry& Eg = a.entries[it.entry];
+  const VItem it = cld(cp(a.vitems) + blockIdx.x);
+  const LB_CONST DecEntry& Eg = cp(a.entries)[it.entry];
   const int tid = threadIdx.x, lane = tid & 63, mr = lane & 15, gr = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int p = it.path;
@@ -411,7 +428,7 @@ __global__ void __launch_bounds__(kThreads, 3) k_decode_v(DecArgs a) {
   const int n = Eg.n, nct = Eg.p[p].nct, xdirect = Eg.xdirect;
   const LB_GLOBAL uint8_t* vdec = reinterpret_cast<const LB_GLOBAL uint8_t*>(gp(Eg.p[p].vdec));
   const LB_GLOBAL uint8_t* gdec = reinterpret_cast<const LB_GLOBAL uint8_t*>(gp(Eg.gdec[p]));
-  const void* xv = a.xs ? a.xs[it.entry] : a.x0;
+  const void* xv = a.xs ? cp(a.xs)[it.entry] : a.x0;
   const LB_GLOBAL uint8_t* xb = reinterpret_cast<const LB_GLOBAL uint8_t*>(gp(xv)) + (int64_t)a.t0 * n * 2;
   uint8_t* ring = lds + wave * kRingBytes;
   uint8_t* abuf = lds + kWaves * kRingBytes + wave * TB * kABytes;
@@ -482,8 +499,8 @@ template <int TM>
 __global__ void __launch_bounds__(kThreads) k_decode_mid(DecArgs a) {
   constexpr int TB = (TM + 7) / 8, CT = decode_v_tiles(TM), SF = decode_slot_floats(TM);
   __shared__ float cblk[kDecodeMaxTokens * 4 * (LB_MAX_RANK / kChunk)];
-  const MItem it = a.mitems[blockIdx.x];
-  const DecEntry& E = a.entries[it.entry];
+  const MItem it = cld(cp(a.mitems) + blockIdx.x);
+  const LB_CONST DecEntry& E = cp(a.entries)[it.entry];
   const int p = it.path, r = E.p[p].r, T = a.T;
   const LB_GLOBAL uint16_t* lsc = gp(E.p[p].l);
   const LB_GLOBAL float* part = gp(a.part);
@@ -525,22 +542,19 @@ __global__ void __launch_bounds__(kThreads) k_decode_mid(DecArgs a) {
 // ---------------------------------------------------------------------------
 // U stage
 // ---------------------------------------------------------------------------
+// Outputs are staged in LDS for all of a wave's quads and stored after its
+// stream has drained: a store inside the stream would hold up the in-order
+// completion count of every load behind it for the store's own latency.
 template <int TM>
 struct UShape {
   static constexpr int TB = (TM + 7) / 8;
   static constexpr int KQQ = TM == 1 ? 1 : 2;          // token slots per lane and block
   static constexpr int KST = TM > 8 ? 2 : 1;           // output stores per quad (8 tokens x 64 rows each)
   static constexpr int NMAX = TB == 1 ? 8 : 4;         // most units with operands held in registers
-  static constexpr int STG = KST * 1024;               // staging bytes per wave
+  static constexpr int QW = decode_u_qw_max(TM);       // most quads per wave
+  static constexpr int STG = QW * TM * 128;            // staging bytes per wave
   static constexpr size_t lds = (size_t)kWaves * (kRingBytes + STG);
 };
-
-// Stores of this quad staged behind the position-i wait: at consumer position
-// s (i = s mod P) the window of ops issued after step s's load holds the stores
-// of every quad that ended at a position in [s - kRing + 1, s - 1].
-__host__ __device__ constexpr int u_stores_in_window(int i, int P) {
-  return i >= kRing - 1 ? 0 : (kRing - 1 - i + P - 1) / P;
-}
 
 // Per-lane state shared by both U forms.
 template <int TM>
@@ -585,15 +599,11 @@ __device__ __attribute__((always_inline)) inline void u_store_plain(const UCtx<T
   vm_wait<0>();
 }
 
-// One quad's outputs through the wave's staging area: KST stores of 16 bytes
-// per lane (lane l: token 8 k + l / 8, rows 8 (l % 8) .. + 7).  Lanes past the
-// last token repeat its store (same address, same value).
+// One quad's outputs into the wave's staging area: [token][64 rows] bf16.
 template <int TM>
-__device__ __attribute__((always_inline)) inline void u_store_staged(const UCtx<TM>& C, int q,
-                                                                    const float (&part)[4][UShape<TM>::TB][2],
-                                                                    uint8_t* stg) {
+__device__ __attribute__((always_inline)) inline void u_stage(const float (&part)[4][UShape<TM>::TB][2], uint8_t* stq) {
   const int lane = threadIdx.x & 63, mr = lane & 15, gr = lane >> 4;
-  uint16_t* s16 = reinterpret_cast<uint16_t*>(stg);
+  uint16_t* s16 = reinterpret_cast<uint16_t*>(stq);
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -603,25 +613,34 @@ __device__ __attribute__((always_inline)) inline void u_store_staged(const UCtx<
         const int t = tb * 8 + 2 * gr + qq;
         if (t < TM) s16[t * 64 + rt * 16 + mr] = bf16_bits(part[rt][tb][qq]);
       }
+}
+
+// Staged quads [qa, qa + nst) to y: KST stores of 16 bytes per lane and quad
+// (lane l: token 8 k + l / 8, rows 8 (l % 8) .. + 7).  Lanes past the last
+// token repeat its store (same address, same value).
+template <int TM>
+__device__ __attribute__((always_inline)) inline void u_flush(const UCtx<TM>& C, int qa, int nst, const uint8_t* stg) {
+  const int lane = threadIdx.x & 63;
   wave_lds_fence();
+  for (int j = 0; j < nst; ++j) {
 #pragma unroll
-  for (int k = 0; k < UShape<TM>::KST; ++k) {
-    const int t = min(8 * k + (lane >> 3), C.T - 1);
-    const u32x4 v = *reinterpret_cast<const u32x4*>(stg + t * 128 + (lane & 7) * 16);
-    *reinterpret_cast<LB_GLOBAL u32x4*>(C.y + (int64_t)t * C.m + 64 * q + (lane & 7) * 8) = v;
+    for (int k = 0; k < UShape<TM>::KST; ++k) {
+      const int t = min(8 * k + (lane >> 3), C.T - 1);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stg + (j * TM + t) * 128 + (lane & 7) * 16);
+      *reinterpret_cast<LB_GLOBAL u32x4*>(C.y + (int64_t)t * C.m + 64 * (qa + j) + (lane & 7) * 8) = v;
+    }
   }
-  wave_lds_fence();
 }
 
 // Fast form: NPC units, operands in registers, every read through the ring.
 // Steps per quad: the row scales, then one per unit.
 template <int TM, int NPC>
-__device__ __attribute__((always_inline)) inline void u_stream(const DecArgs& a, const DecEntry& Eg, UCtx<TM>& C,
+__device__ __attribute__((always_inline)) inline void u_stream(const DecArgs& a, const LB_CONST DecEntry& Eg, UCtx<TM>& C,
                                                               int qa, int qb, uint8_t* ring, uint8_t* stg) {
   using S = UShape<TM>;
   constexpr int TB = S::TB, P = NPC + 1;
   const int lane = threadIdx.x & 63, mr = lane & 15, gr = lane >> 4;
-  const UGeom g = Eg.ug;
+  const UGeom g = cld(&Eg.ug);
   const LB_GLOBAL uint8_t* udec = reinterpret_cast<const LB_GLOBAL uint8_t*>(gp(Eg.udec));
   const LB_GLOBAL uint8_t* hq = reinterpret_cast<const LB_GLOBAL uint8_t*>(gp(Eg.hq));
   const LB_GLOBAL uint8_t* aimg = reinterpret_cast<const LB_GLOBAL uint8_t*>(gp(static_cast<const uint8_t*>(Eg.aimg)));
@@ -639,9 +658,9 @@ __device__ __attribute__((always_inline)) inline void u_stream(const DecArgs& a,
     const LB_GLOBAL uint8_t* src = i == 0 ? hq + (int64_t)q * 256 + hoff : udec + (int64_t)q * g.qbytes + uoff[i > 0 ? i - 1 : 0];
     dma16(src, ring + slot * 1024);
   };
-#pragma unroll
-  for (int k = 0; k < kRing - 1; ++k) issue_at(qa + k / P, k % P, k);
-  // operands (rows past 2 T are never read: skip their loads)
+  // operands first (rows past 2 T are never read: skip their loads), then the
+  // ring's first steps, then a wait for the operands alone (loads complete in
+  // issue order), which leaves the ring's loads in flight
   v8i A[NPC][TB];
   int sc[NPC][TB];
 #pragma unroll
@@ -654,9 +673,12 @@ __device__ __attribute__((always_inline)) inline void u_stream(const DecArgs& a,
         sc[u][tb] = 127;
       }
     }
-  vm_wait<0>();
+#pragma unroll
+  for (int k = 0; k < kRing - 1; ++k) issue_at(qa + k / P, k % P, k);
+  vm_wait<kRing - 1>();
 
-  const bool fast_store = (C.m & 7) == 0;
+  // quads whose 64 rows are whole (and 16-byte aligned in y) are staged
+  const int nst = (C.m & 7) == 0 ? max(0, min(qb, C.m / 64) - qa) : 0;
   int s = 0;
   for (int q = qa; q < qb; ++q) {
     v4f acc[4][TB];
@@ -670,7 +692,7 @@ __device__ __attribute__((always_inline)) inline void u_stream(const DecArgs& a,
       constexpr int i = decltype(I)::value;
       lds_wait();                                  // the slot reloaded next was read last step
       issue_at(q + (i + kRing - 1) / P, (i + kRing - 1) % P, (s + kRing - 1) % kRing);
-      vm_wait<kRing - 1 + S::KST * u_stores_in_window(i, P)>();
+      vm_wait<kRing - 1>();
       const uint8_t* slot = ring + (s % kRing) * 1024;
       ++s;
       if constexpr (i == 0) {
@@ -700,20 +722,21 @@ __device__ __attribute__((always_inline)) inline void u_stream(const DecArgs& a,
     });
     if (C.np > 1) u_fold<TB>(acc, h[1], C.cv[1], part, false);
     else u_fold<TB>(acc, h[0], C.cv[0], part, true);
-    if (fast_store && 64 * q + 64 <= C.m) u_store_staged<TM>(C, q, part, stg);
+    if (q - qa < nst) u_stage<TM>(part, stg + (q - qa) * TM * 128);
     else u_store_plain<TM>(C, q, part);
   }
   vm_wait<0>();                                    // no direct-to-LDS load may still be in flight
+  u_flush<TM>(C, qa, nst, stg);
 }
 
 // Plain form (more units than the fast form holds): plain loads, one unit at a time.
 template <int TM>
-__device__ __attribute__((always_inline)) inline void u_plain(const DecArgs& a, const DecEntry& Eg, UCtx<TM>& C,
+__device__ __attribute__((always_inline)) inline void u_plain(const DecArgs& a, const LB_CONST DecEntry& Eg, UCtx<TM>& C,
                                                              int qa, int qb) {
   using S = UShape<TM>;
   constexpr int TB = S::TB;
   const int lane = threadIdx.x & 63, mr = lane & 15, gr = lane >> 4;
-  const UGeom g = Eg.ug;
+  const UGeom g = cld(&Eg.ug);
   const LB_GLOBAL uint8_t* udec = reinterpret_cast<const LB_GLOBAL uint8_t*>(gp(Eg.udec));
   const LB_GLOBAL uint16_t* hq = gp(Eg.hq);
   const LB_GLOBAL uint8_t* aimg = reinterpret_cast<const LB_GLOBAL uint8_t*>(gp(static_cast<const uint8_t*>(Eg.aimg)));
@@ -761,8 +784,8 @@ __global__ void __launch_bounds__(kThreads, TM >= 16 ? 2 : 3) k_decode_u(DecArgs
   using S = UShape<TM>;
   constexpr int TB = S::TB;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  const UItem it = a.uitems[blockIdx.x];
-  const DecEntry& Eg = a.entries[it.entry];
+  const UItem it = cld(cp(a.uitems) + blockIdx.x);
+  const LB_CONST DecEntry& Eg = cp(a.entries)[it.entry];
   const int lane = threadIdx.x & 63, gr = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int qa = min(it.q0 + wave * it.qw, it.q0 + it.nq), qb = min(qa + it.qw, it.q0 + it.nq);
@@ -772,7 +795,7 @@ __global__ void __launch_bounds__(kThreads, TM >= 16 ? 2 : 3) k_decode_u(DecArgs
   C.T = a.T;
   C.np = Eg.np;
   C.nu0 = Eg.ug.nu0;
-  void* yv = a.xs ? a.ys[it.entry] : a.y0;
+  void* yv = a.xs ? cp(a.ys)[it.entry] : a.y0;
   C.y = gp(reinterpret_cast<uint16_t*>(yv)) + (int64_t)a.t0 * C.m;
   const LB_GLOBAL float* cval = gp(Eg.cval);
 #pragma unroll

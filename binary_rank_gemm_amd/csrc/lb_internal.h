@@ -131,6 +131,9 @@ __host__ __device__ inline constexpr int decode_v_tiles(int bucket) { return buc
 __host__ __device__ inline constexpr int decode_slot_floats(int bucket) {
   return decode_v_tiles(bucket) * 16 * bucket + 16;
 }
+// Most quads per wave of a U item at a token bucket (the wave stages all of
+// its outputs in LDS: 2 KB, or 8 KB at 16 tokens where fewer items fit a CU).
+__host__ __device__ inline constexpr int decode_u_qw_max(int bucket) { return bucket >= 16 ? 4 : 16 / bucket; }
 // Sizes the planner aims at per V and U work item (bytes of sign words).
 constexpr int kDecodeVItemBytes = 96 * 1024;
 constexpr int kDecodeUItemBytes = 96 * 1024;
