@@ -87,21 +87,24 @@ def build_stack(wl, T, lb, torch, limit_layers=None):
 
 
 def time_steps(fn, steps, warmup, torch):
+    """Warm up, then time exactly `steps` calls: wall clock between two device
+    synchronisations, and one pair of HIP events on the launch stream around
+    the same region (per-step events would add their own gaps to the stream)."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     st = torch.cuda.current_stream()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for a, b in evs:
-        a.record(st)
+    ev0.record(st)
+    for _ in range(steps):
         fn()
-        b.record(st)
+    ev1.record(st)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = [a.elapsed_time(b) for a, b in evs]   # ms, each step on its own stream interval
-    return wall, per
+    return wall, ev0.elapsed_time(ev1) / steps   # seconds; ms per step on the stream
 
 
 def cpu_baseline(wl, ranks_of, T, budget_s=15.0):
@@ -160,12 +163,11 @@ def run_decode(args, lb, torch):
         wl = dataclasses.replace(wl, layers=min(args.layers, wl.layers))
     S = lb.Stack(lins)
     fn = lambda: S.forward(xs, ys, regime=lb.REGIME_DECODE, use_graph=True)
-    wall, per = time_steps(fn, args.steps, args.warmup, torch)
+    wall, kern_ms = time_steps(fn, args.steps, args.warmup, torch)
     byts, flops = algorithmic(wl, ranks_of, T)
     ms = wall * 1e3 / args.steps
-    kern_ms = float(np.mean(per))
     gbps = byts / (kern_ms * 1e-3) / 1e9
-    return dict(wl=wl, T=T, ranks_of=ranks_of, ms=ms, kern_ms=kern_ms, per=per, bytes=byts, flops=flops,
+    return dict(wl=wl, T=T, ranks_of=ranks_of, ms=ms, kern_ms=kern_ms, bytes=byts, flops=flops,
                 gbps=gbps, stack=S, lins=lins)
 
 
@@ -179,9 +181,8 @@ def run_prefill(args, lb, torch, workload):
         wl = dataclasses.replace(wl, layers=min(args.layers, wl.layers))
     S = lb.Stack(lins)
     fn = lambda: S.forward(xs, ys, regime=lb.REGIME_PREFILL, use_graph=True)
-    wall, per = time_steps(fn, max(2, args.steps // 10), max(1, args.warmup // 5), torch)
+    wall, kern_ms = time_steps(fn, max(2, args.steps // 10), max(1, args.warmup // 5), torch)
     byts, flops = algorithmic(wl, ranks_of, T)
-    kern_ms = float(np.mean(per))
     return dict(workload=f"{wl.name} prefill, {wl.count} linears, {T} tokens", tokens=T, ms_per_step=kern_ms,
                 tflops=flops / (kern_ms * 1e-3) / 1e12, frac_of_bf16_peak=flops / (kern_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
                 algorithmic_tflop=flops / 1e12)
@@ -190,8 +191,9 @@ def run_prefill(args, lb, torch, workload):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    # the GPU's clocks take some tens of milliseconds of load to settle
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="cfg5-decode", choices=sorted(WORKLOADS))
     ap.add_argument("--layers", type=int, default=None, help="limit the stack to this many layers (not for reports)")
     ap.add_argument("--no-prefill", action="store_true")
@@ -247,7 +249,6 @@ def main():
                    "tokens": T, "linears": wl.count, "ranks": {s.name: r["ranks_of"][j][0] for j, s in enumerate(wl.mats)}},
         "hbm_gbps": round(r["gbps"], 1),
         "hbm_frac": round(r["gbps"] / HBM_PEAK_GBPS, 4),
-        "step_us_p10_p50_p90": [round(float(np.percentile(r["per"], q)) * 1e3, 2) for q in (10, 50, 90)],
         "roofline": {
             "bound": "hbm",
             "kernel": "decode step: k_decode_v then k_decode_u over all linears (one graph launch)",

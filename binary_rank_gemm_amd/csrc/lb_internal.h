@@ -135,8 +135,8 @@ __host__ __device__ inline constexpr int decode_slot_floats(int bucket) {
 // its outputs in LDS: 2 KB, or 8 KB at 16 tokens where fewer items fit a CU).
 __host__ __device__ inline constexpr int decode_u_qw_max(int bucket) { return bucket >= 16 ? 4 : 16 / bucket; }
 // Sizes the planner aims at per V and U work item (bytes of sign words).
-constexpr int kDecodeVItemBytes = 96 * 1024;
-constexpr int kDecodeUItemBytes = 96 * 1024;
+constexpr int kDecodeVItemBytes = 192 * 1024;
+constexpr int kDecodeUItemBytes = 192 * 1024;
 
 // ---------------------------------------------------------------------------
 // kernel launchers (defined in the .hip files)
