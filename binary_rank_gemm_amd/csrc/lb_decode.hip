@@ -449,43 +449,64 @@ __global__ void __launch_bounds__(kThreads, 3) k_decode_v(DecArgs a) {
     else v_plain<TM>(a, it, n, nct, xb, gdec, vdec, ca, cb, abuf, acc, cpart);
   }
 
-  // fixed-order combine across waves in the (now idle) ring memory: wave 0
-  // stores, waves 1..3 add in turn; then the slot is written
+  // fixed-order combine across waves in the (now idle) ring memory
   float cw_[TM];
 #pragma unroll
   for (int t = 0; t < TM; ++t) cw_[t] = wave_sum(cpart[t]);
-  float* red = reinterpret_cast<float*>(lds);      // [tile][token][16]
-  float* cred = red + CT * TM * 16;                // [token]
   const int ntl = it.ntiles;
-  __syncthreads();
-  for (int wv = 0; wv < kWaves; ++wv) {
-    if (wave == wv) {
+  LB_GLOBAL float* slot = gp(a.part) + (int64_t)it.slot * decode_slot_floats(TM);
+  // lane (mr, gr) holds MFMA rows 4 gr .. 4 gr + 3 = (hi, lo) of tokens
+  // tb * 8 + 2 gr + {0, 1}, column mr
+  auto wave_part = [&](float* dst, bool add) __attribute__((always_inline)) {
 #pragma unroll
-      for (int c = 0; c < CT; ++c) {
-        if (c < ntl) {
+    for (int c = 0; c < CT; ++c) {
+      if (c < ntl) {
 #pragma unroll
-          for (int tb = 0; tb < TB; ++tb)
+        for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-            for (int qq = 0; qq < 2; ++qq) {
-              const int t = tb * 8 + 2 * gr + qq;
-              if (t < TM) {
-                float* dst = red + (c * TM + t) * 16 + mr;
-                const float d = acc[c][tb][2 * qq] + acc[c][tb][2 * qq + 1];
-                *dst = (wv == 0 ? 0.f : *dst) + d;
-              }
+          for (int qq = 0; qq < 2; ++qq) {
+            const int t = tb * 8 + 2 * gr + qq;
+            if (t < TM) {
+              float* d = dst + (c * TM + t) * 16 + mr;
+              const float v = acc[c][tb][2 * qq] + acc[c][tb][2 * qq + 1];
+              *d = add ? *d + v : v;
             }
-        }
-      }
-      if (lane == 0) {
-#pragma unroll
-        for (int t = 0; t < TM; ++t) cred[t] = (wv == 0 ? 0.f : cred[t]) + cw_[t];
+          }
       }
     }
+  };
+  __syncthreads();
+  if constexpr (kWaves * (CT * TM * 16 + TM) * 4 <= kRingBytes * kWaves) {
+    // each wave writes its own copy, then every thread adds the four in wave order
+    float* red = reinterpret_cast<float*>(lds);    // [wave][tile][token][16]
+    float* cred = red + kWaves * CT * TM * 16;     // [wave][token]
+    wave_part(red + wave * CT * TM * 16, false);
+    if (lane == 0) {
+#pragma unroll
+      for (int t = 0; t < TM; ++t) cred[wave * TM + t] = cw_[t];
+    }
     __syncthreads();
+    for (int i = tid; i < ntl * TM * 16; i += kThreads)
+      slot[i] = ((red[i] + red[CT * TM * 16 + i]) + red[2 * CT * TM * 16 + i]) + red[3 * CT * TM * 16 + i];
+    if (tid < TM) slot[CT * TM * 16 + tid] = ((cred[tid] + cred[TM + tid]) + cred[2 * TM + tid]) + cred[3 * TM + tid];
+    return;
+  } else {
+    // wave 0 stores, waves 1..3 add in turn
+    float* red = reinterpret_cast<float*>(lds);    // [tile][token][16]
+    float* cred = red + CT * TM * 16;              // [token]
+    for (int wv = 0; wv < kWaves; ++wv) {
+      if (wave == wv) {
+        wave_part(red, wv != 0);
+        if (lane == 0) {
+#pragma unroll
+          for (int t = 0; t < TM; ++t) cred[t] = (wv == 0 ? 0.f : cred[t]) + cw_[t];
+        }
+      }
+      __syncthreads();
+    }
+    for (int i = tid; i < ntl * TM * 16; i += kThreads) slot[i] = red[i];
+    if (tid < TM) slot[CT * TM * 16 + tid] = cred[tid];
   }
-  LB_GLOBAL float* slot = gp(a.part) + (int64_t)it.slot * decode_slot_floats(TM);
-  for (int i = tid; i < ntl * TM * 16; i += kThreads) slot[i] = red[i];
-  if (tid < TM) slot[CT * TM * 16 + tid] = cred[tid];
 }
 
 // ---------------------------------------------------------------------------
