@@ -4,8 +4,8 @@
 Default workload: the Llama-2-70B-shaped stack at 0.1 sign bits per weight
 (80 layers x {q, k, v, o, gate, up, down}, both paths, 560 linears, 0.91 GB
 of packed signs + fp16 scales), decode at batch 1, run as one lb_stack_forward
-per step (HIP graph replay of the two decode kernels, V stage then U stage,
-each over every linear of the stack).  Inputs are seeded synthetic data
+per step (HIP graph replay of the three decode kernels, V stage, mid stage
+and U stage, each over every linear of the stack).  Inputs are seeded synthetic data
 resident in HBM before timing starts.
 
 Prints one JSON line: the decode step's microseconds per token and achieved
@@ -251,7 +251,7 @@ def main():
         "hbm_frac": round(r["gbps"] / HBM_PEAK_GBPS, 4),
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode step: k_decode_v then k_decode_u over all linears (one graph launch)",
+            "kernel": "decode step: k_decode_v, k_decode_mid, k_decode_u over all linears (one graph launch)",
             "achieved": round(r["gbps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(r["gbps"] / HBM_PEAK_GBPS, 4),
             "traffic": read_traffic("lb_decode.hip", args.workload),
