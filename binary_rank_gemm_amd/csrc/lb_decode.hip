@@ -258,7 +258,9 @@ struct VShape {
 
 // Partial sums of one wave's chunks: acc (z_p before the correction term) and
 // cpart (the correction term per token).  Fast form: every read goes through
-// the wave's ring (x rows of n % 8 == 0 elements).
+// the wave's ring (x rows of n % 8 == 0 elements).  The chunks go in groups of
+// G (two at one token, so that one 1 KB step carries both chunks' g and x
+// rows), each group being its x/g steps followed by each chunk's sign steps.
 template <int TM>
 __device__ __attribute__((always_inline)) inline void v_stream(const DecArgs& a, const VItem& it, int n, int nct,
                                                               const LB_GLOBAL uint8_t* xb, const LB_GLOBAL uint8_t* gdec,
@@ -267,31 +269,47 @@ __device__ __attribute__((always_inline)) inline void v_stream(const DecArgs& a,
                                                               float (&cpart)[TM]) {
   using S = VShape<TM>;
   constexpr int TB = S::TB, XS = S::XS;
+  constexpr int G = TM == 1 ? 2 : 1;           // chunks per group
   const int lane = threadIdx.x & 63, mr = lane & 15, gr = lane >> 4;
-  const int T = a.T, ntl = it.ntiles, ss = (ntl + 3) / 4, P = XS + ss;
-  // issue cursor: chunk ic, step ik inside the chunk (XS x/g steps, then ss sign steps)
-  int ic = ca, ik = 0;
+  const int T = a.T, ntl = it.ntiles, ss = (ntl + 3) / 4;
+  // issue cursor: group of chunks [ic, ic + ng), step ik of the group (XS x/g
+  // steps, then chunk ic + jc's sign step js)
+  int ic = ca, ik = 0, jc = 0, js = 0;
+  int ng = min(G, cb - ca);
   const LB_GLOBAL uint8_t* last = gdec;
   auto issue = [&](int slot) __attribute__((always_inline)) {
     if (ic < cb) {
       if (ik < XS) {
-        // lane l: row 4 ik + l / 16 of the step (0: g, 1 + t: token t), elements 8 (l % 16) .. + 7
-        const int rho = 4 * ik + (lane >> 4);
-        const int e0 = ic * kChunk + 8 * (lane & 15);
-        if (rho == 0) {
-          last = gdec + (int64_t)e0 * 2;
+        if constexpr (G == 2) {
+          // lane l: 16 bytes (elements 8 (l % 16) .. + 7) of g (l / 16 even) or x (odd) of chunk ic + l / 32
+          const int c = ic + min(lane >> 5, ng - 1);
+          const int e0 = c * kChunk + 8 * (lane & 15);
+          last = (lane >> 4) & 1 ? xb + (int64_t)min(e0, n - 8) * 2 : gdec + (int64_t)e0 * 2;
         } else {
-          const int t = min(rho - 1, T - 1);
-          last = xb + ((int64_t)t * n + min(e0, n - 8)) * 2;
+          // lane l: row 4 ik + l / 16 of the step (0: g, 1 + t: token t), elements 8 (l % 16) .. + 7
+          const int rho = 4 * ik + (lane >> 4);
+          const int e0 = ic * kChunk + 8 * (lane & 15);
+          if (rho == 0) {
+            last = gdec + (int64_t)e0 * 2;
+          } else {
+            const int t = min(rho - 1, T - 1);
+            last = xb + ((int64_t)t * n + min(e0, n - 8)) * 2;
+          }
         }
+        ++ik;
       } else {
-        // lane l: 16 bytes of column tile 4 (ik - XS) + l / 16 of the item (the last one past the end)
-        const int tile = it.tile0 + min(4 * (ik - XS) + (lane >> 4), ntl - 1);
-        last = vdec + ((int64_t)ic * nct + tile) * 256 + (lane & 15) * 16;
-      }
-      if (++ik == P) {
-        ik = 0;
-        ++ic;
+        // lane l: 16 bytes of column tile 4 js + l / 16 of the item (the last one past the end)
+        const int tile = it.tile0 + min(4 * js + (lane >> 4), ntl - 1);
+        last = vdec + ((int64_t)(ic + jc) * nct + tile) * 256 + (lane & 15) * 16;
+        if (++js == ss) {
+          js = 0;
+          if (++jc == ng) {
+            ic += ng;
+            ng = min(G, cb - ic);
+            ik = 0;
+            jc = 0;
+          }
+        }
       }
     }
     dma16(last, ring + slot * 1024);
@@ -308,54 +326,71 @@ __device__ __attribute__((always_inline)) inline void v_stream(const DecArgs& a,
     return slot;
   };
   const ConvLane L(lane);
-  for (int c = ca; c < cb; ++c) {
-    // this lane's elements kloc, kloc + 1 (= 2 lane, 2 lane + 1) of g and of each token row
-    uint32_t gpair = 0, xpair[TM];
+  for (int c0 = ca; c0 < cb; c0 += G) {
+    const int ngc = min(G, cb - c0);
+    // this lane's elements kloc, kloc + 1 (= 2 lane, 2 lane + 1) of g and of each token row, per chunk
+    uint32_t gpair[G], xpair[G][TM];
 #pragma unroll
-    for (int t = 0; t < TM; ++t) xpair[t] = 0;
+    for (int g = 0; g < G; ++g) {
+      gpair[g] = 0;
+#pragma unroll
+      for (int t = 0; t < TM; ++t) xpair[g][t] = 0;
+    }
 #pragma unroll
     for (int j = 0; j < XS; ++j) {
       const uint8_t* slot = next_step();
+      if constexpr (G == 2) {
+        gpair[0] = *reinterpret_cast<const uint32_t*>(slot + 4 * lane);
+        xpair[0][0] = *reinterpret_cast<const uint32_t*>(slot + 256 + 4 * lane);
+        gpair[1] = *reinterpret_cast<const uint32_t*>(slot + 512 + 4 * lane);
+        xpair[1][0] = *reinterpret_cast<const uint32_t*>(slot + 768 + 4 * lane);
+      } else {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int rho = 4 * j + q;
-        if (rho == 0) gpair = *reinterpret_cast<const uint32_t*>(slot + 4 * lane);
-        else if (rho - 1 < TM) xpair[rho - 1] = *reinterpret_cast<const uint32_t*>(slot + q * 256 + 4 * lane);
-      }
-    }
-    const int k0 = c * kChunk + L.kloc;
-    const bool v0 = k0 < n, v1 = k0 + 1 < n;
-    const float g0 = f16f((uint16_t)(gpair & 0xffff)) * L.fcls, g1 = f16f((uint16_t)(gpair >> 16)) * L.fcls;
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb) {
-#pragma unroll
-      for (int tt = 0; tt < 8; ++tt) {
-        const int t = tb * 8 + tt;
-        if (t < TM && t < T) {
-          const float x0 = bf16f((uint16_t)(xpair[t] & 0xffff)), x1 = bf16f((uint16_t)(xpair[t] >> 16));
-          cpart[t] += convert_pair(L, v0 ? x0 * g0 : 0.f, v1 ? x1 * g1 : 0.f, tt, abuf + tb * kABytes);
+        for (int q = 0; q < 4; ++q) {
+          const int rho = 4 * j + q;
+          if (rho == 0) gpair[0] = *reinterpret_cast<const uint32_t*>(slot + 4 * lane);
+          else if (rho - 1 < TM) xpair[0][rho - 1] = *reinterpret_cast<const uint32_t*>(slot + q * 256 + 4 * lane);
         }
       }
     }
-    wave_lds_fence();
-    v8i A[TB];
-    int sc[TB];
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb) load_a(abuf + tb * kABytes, mr, gr, A[tb], sc[tb]);
-    wave_lds_fence();
+    for (int g = 0; g < G; ++g) {
+      if (g < ngc) {
+        const int k0 = (c0 + g) * kChunk + L.kloc;
+        const bool v0 = k0 < n, v1 = k0 + 1 < n;
+        const float g0 = f16f((uint16_t)(gpair[g] & 0xffff)) * L.fcls, g1 = f16f((uint16_t)(gpair[g] >> 16)) * L.fcls;
 #pragma unroll
-    for (int j = 0; j < S::SMAX; ++j) {
-      if (j < ss) {
-        const uint8_t* slot = next_step();
-        uint32_t w[4];
+        for (int tb = 0; tb < TB; ++tb) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = *reinterpret_cast<const uint32_t*>(slot + i * 256 + 4 * lane);
+          for (int tt = 0; tt < 8; ++tt) {
+            const int t = tb * 8 + tt;
+            if (t < TM && t < T) {
+              const float x0 = bf16f((uint16_t)(xpair[g][t] & 0xffff)), x1 = bf16f((uint16_t)(xpair[g][t] >> 16));
+              cpart[t] += convert_pair(L, v0 ? x0 * g0 : 0.f, v1 ? x1 * g1 : 0.f, tt, abuf + tb * kABytes);
+            }
+          }
+        }
+        wave_lds_fence();
+        v8i A[TB];
+        int sc[TB];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (4 * j + i < S::CT && 4 * j + i < ntl) {
-            const v8i B = expand_signs(w[i]);
+        for (int tb = 0; tb < TB; ++tb) load_a(abuf + tb * kABytes, mr, gr, A[tb], sc[tb]);
+        wave_lds_fence();
 #pragma unroll
-            for (int tb = 0; tb < TB; ++tb) acc[4 * j + i][tb] = mfma(A[tb], B, acc[4 * j + i][tb], sc[tb]);
+        for (int j = 0; j < S::SMAX; ++j) {
+          if (j < ss) {
+            const uint8_t* slot = next_step();
+            uint32_t w[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w[i] = *reinterpret_cast<const uint32_t*>(slot + i * 256 + 4 * lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              if (4 * j + i < S::CT && 4 * j + i < ntl) {
+                const v8i B = expand_signs(w[i]);
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb) acc[4 * j + i][tb] = mfma(A[tb], B, acc[4 * j + i][tb], sc[tb]);
+              }
+            }
           }
         }
       }
