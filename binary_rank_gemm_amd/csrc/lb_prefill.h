@@ -39,6 +39,7 @@ struct PreEntry {
 struct PreItem {
   int entry;                 // < 0: idle slot
   int mt, nt;
+  int str;                   // GEMM1: a wave's columns reach into both paths
 };
 
 // Launch plan of the prefill kernels for a list of linears at T tokens.
@@ -46,8 +47,8 @@ struct PrefillPlan {
   int T = -1;
   int count = 0;
   PreEntry* entries_d = nullptr;
-  PreItem* items_d = nullptr;       // GEMM1 items (single-path waves, then mixed), GEMM2 items
-  int n1 = 0, n1s = 0, n2 = 0;
+  PreItem* items_d = nullptr;       // GEMM1 items, then GEMM2 items
+  int n1 = 0, n2 = 0;
   void* zbuf = nullptr;
   size_t zbytes = 0;
   std::vector<PreEntry> entries_h;

@@ -12,8 +12,8 @@
 // B operand pair is one shift and one bit-field insert of the sign bits into
 // a bf16 pair of magnitudes.
 //
-// Workgroup tile 256 x 256 (4 waves of 128 x 128, 32x32x16 MFMA, fp32
-// accumulators in AGPRs), K blocks of 64.  A, the packed B words and |g| go
+// Workgroup tile 256 x 256 (8 waves of 128 x 64, two per SIMD, 32x32x16
+// MFMA, fp32 accumulators in AGPRs), K blocks of 64.  A, the packed B words and |g| go
 // from global memory straight into LDS (four buffers, loads issued three
 // blocks ahead; A rows unpadded with an XOR swizzle of their 16-byte chunks
 // against bank conflicts); B operands are expanded from the sign bits in
@@ -203,7 +203,7 @@ __device__ inline int a_slot_chunk(int s) { return (s & 7) ^ ((s >> 3) & 7); }
 // only): some wave's columns cross from the primary path into the residual
 // one, so |g| is chosen per column block.
 template <int MODE, int WM, int WN, bool STR>
-__global__ void __launch_bounds__(64 * WM * WN, 1) k_prefill(PreArgs a) {
+__device__ __forceinline__ void prefill_tile(const PreArgs& a, const PreItem& it) {
   constexpr int kWaves = WM * WN, kNT = 64 * kWaves;
   constexpr int MB = kPreBM / WM / 32, NB = kPreBN / WN / 32;
   constexpr int kAI = kPreBM * 8 / kNT;                 // A loads (16 B per lane) per wave per block
@@ -211,8 +211,6 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_prefill(PreArgs a) {
   static_assert(kWaves >= 3, "waves 0, 1, 2 carry the B words and |g|");
   static_assert(MODE == 1 || !STR, "only GEMM1 columns span paths");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  const PreItem it = a.items[blockIdx.x];
-  if (it.entry < 0) return;
   const PreEntry& Eg = a.entries[it.entry];
   const PrefillLayer L = Eg.L;
   const int T = a.T;
@@ -410,8 +408,22 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) k_prefill(PreArgs a) {
   }
 }
 
+// One workgroup per tile; GEMM1 tiles where a wave's columns reach into both
+// paths take the body that picks |g| per column block.
+template <int MODE, int WM, int WN>
+__global__ void __launch_bounds__(64 * WM * WN, 1) k_prefill(PreArgs a) {
+  const PreItem it = a.items[blockIdx.x];
+  if (it.entry < 0) return;
+  if constexpr (MODE == 1) {
+    if (it.str) prefill_tile<1, WM, WN, true>(a, it);
+    else prefill_tile<1, WM, WN, false>(a, it);
+  } else {
+    prefill_tile<2, WM, WN, false>(a, it);
+  }
+}
+
 // wave layout of the prefill GEMMs
-constexpr int kPreWM = 2, kPreWNv = 2;
+constexpr int kPreWM = 2, kPreWNv = 4;
 constexpr int kWaveCols = kPreBN / kPreWNv;
 
 // true when a wave of GEMM1 tile nt has columns of both paths
@@ -525,7 +537,7 @@ std::vector<PreItem> xcd_order(const std::vector<std::vector<PreItem>>& stripes)
   }
   size_t len = 0;
   for (auto& v : per) len = std::max(len, v.size());
-  std::vector<PreItem> out(len * kXcd, PreItem{-1, 0, 0});
+  std::vector<PreItem> out(len * kXcd, PreItem{-1, 0, 0, 0});
   for (int x = 0; x < kXcd; ++x)
     for (size_t i = 0; i < per[x].size(); ++i) out[i * kXcd + x] = per[x][i];
   return out;
@@ -536,7 +548,7 @@ std::vector<PreItem> xcd_order(const std::vector<std::vector<PreItem>>& stripes)
 hipError_t prefill_prepare(PrefillPlan& P, const PrefillLayer* const* layers, int count, int T,
                            const void* const* xs, void* const* ys) {
   const int mts = (T + kPreBM - 1) / kPreBM;
-  std::vector<std::vector<PreItem>> s1, s1s, s2;
+  std::vector<std::vector<PreItem>> s1, s2;
   size_t zoff = 0;
   std::vector<size_t> zoffs(count);
   P.entries_h.assign(count, PreEntry{});
@@ -547,15 +559,14 @@ hipError_t prefill_prepare(PrefillPlan& P, const PrefillLayer* const* layers, in
     zoff += align256((size_t)T * L.Rp * 2);
     const int nt1 = (L.Rp + kPreBN - 1) / kPreBN, nt2 = (L.m + kPreBN - 1) / kPreBN;
     for (int mt = 0; mt < mts; ++mt) {
-      std::vector<PreItem> a, as, b;
-      for (int nt = 0; nt < nt1; ++nt) (tile_straddles(L, nt) ? as : a).push_back(PreItem{e, mt, nt});
-      for (int nt = 0; nt < nt2; ++nt) b.push_back(PreItem{e, mt, nt});
+      std::vector<PreItem> a, b;
+      for (int nt = 0; nt < nt1; ++nt) a.push_back(PreItem{e, mt, nt, tile_straddles(L, nt) ? 1 : 0});
+      for (int nt = 0; nt < nt2; ++nt) b.push_back(PreItem{e, mt, nt, 0});
       s1.push_back(a);
-      if (!as.empty()) s1s.push_back(as);
       s2.push_back(b);
     }
   }
-  std::vector<PreItem> i1 = xcd_order(s1), i1s = xcd_order(s1s), i2 = xcd_order(s2);
+  std::vector<PreItem> i1 = xcd_order(s1), i2 = xcd_order(s2);
   if (zoff > P.zbytes) {
     if (P.zbuf) {
       hipError_t e = hipFree(P.zbuf);
@@ -577,15 +588,13 @@ hipError_t prefill_prepare(PrefillPlan& P, const PrefillLayer* const* layers, in
   P.entries_d = nullptr;
   P.items_d = nullptr;
   hipError_t e = hipMalloc(&P.entries_d, count * sizeof(PreEntry));
-  if (e == hipSuccess) e = hipMalloc(&P.items_d, (i1.size() + i1s.size() + i2.size()) * sizeof(PreItem));
+  if (e == hipSuccess) e = hipMalloc(&P.items_d, (i1.size() + i2.size()) * sizeof(PreItem));
   if (e == hipSuccess) e = hipMemcpy(P.entries_d, P.entries_h.data(), count * sizeof(PreEntry), hipMemcpyHostToDevice);
   if (e != hipSuccess) return e;
   std::vector<PreItem> all(i1);
-  all.insert(all.end(), i1s.begin(), i1s.end());
   all.insert(all.end(), i2.begin(), i2.end());
   if ((e = hipMemcpy(P.items_d, all.data(), all.size() * sizeof(PreItem), hipMemcpyHostToDevice)) != hipSuccess) return e;
   P.n1 = (int)i1.size();
-  P.n1s = (int)i1s.size();
   P.n2 = (int)i2.size();
   P.T = T;
   P.count = count;
@@ -613,14 +622,11 @@ hipError_t prefill_run(PrefillPlan& P, const PrefillLayer* const* layers, int co
   a.entries = P.entries_d;
   a.T = T;
   a.items = P.items_d;
-  if (P.n1 > 0) hipLaunchKernelGGL((k_prefill<1, kPreWM, kPreWNv, false>), dim3(P.n1), dim3(kThreads), kPreLds, st, a);
+  if (P.n1 > 0) hipLaunchKernelGGL((k_prefill<1, kPreWM, kPreWNv>), dim3(P.n1), dim3(kThreads), kPreLds, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   a.items = P.items_d + P.n1;
-  if (P.n1s > 0) hipLaunchKernelGGL((k_prefill<1, kPreWM, kPreWNv, true>), dim3(P.n1s), dim3(kThreads), kPreLds, st, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  a.items = P.items_d + P.n1 + P.n1s;
-  hipLaunchKernelGGL((k_prefill<2, kPreWM, kPreWNv, false>), dim3(P.n2), dim3(kThreads), kPreLds, st, a);
+  hipLaunchKernelGGL((k_prefill<2, kPreWM, kPreWNv>), dim3(P.n2), dim3(kThreads), kPreLds, st, a);
   return hipGetLastError();
 }
 
