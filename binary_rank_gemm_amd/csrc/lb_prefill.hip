@@ -33,6 +33,10 @@ namespace {
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 
 #define LB_GLOBAL __attribute__((address_space(1)))
 template <class T>
@@ -379,31 +383,94 @@ __device__ __forceinline__ void prefill_tile(const PreArgs& a, const PreItem& it
       const uint32_t dn = ks < 3 ? bw[ks + 1] : bwn[0];
       const u32x4 g0 = MODE == 1 ? read_g(rb, rks, bpath[0]) : u32x4{};
       const u32x4 g1 = (MODE == 1 && STR) ? read_g(rb, rks, !bpath[0]) : u32x4{};
+      // the LDS reads of step ks + 1 go out before this step's MFMAs (the
+      // scheduler would otherwise sink them next to their use and expose
+      // their latency at every step)
+      __builtin_amdgcn_sched_barrier(0);
       make_b(dn, g0, g1, kpath(ks < 3 ? kb : kb + 1, rks), bf[(ks + 1) & 1]);
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) acc[mb][b] = mfma32(af[ks & 1][mb], bf[ks & 1][b], acc[mb][b]);
+        for (int mb = 0; mb < MB; ++mb) acc[mb][b] = mfma32(bf[ks & 1][b], af[ks & 1][mb], acc[mb][b]);
     }
     bw = bwn;
     if (more) vm_wait_barrier<kAI>();
     else vm_wait_barrier<0>();
   }
 
-  // ---- epilogue: lane holds D[8 (q/4) + 4 kg + q%4][l32] of each 32x32 block
+  // ---- epilogue.  The MFMAs take the B operand as their first factor, so
+  // block (mb, b) holds the transposed product: lane (l32, kg) has output row
+  // l32 of the block and columns 8 j + 4 kg + i (j, i = 0..3) in q = 4 j + i,
+  // i.e. four runs of four adjacent columns (8 bytes of bf16 each).  When rows
+  // of C are 16-byte aligned, the workgroup stages its bf16 tile in LDS (free:
+  // every wave is past the loop's last barrier, which waited for all LDS
+  // reads) and writes whole 512-byte row segments; otherwise each run goes
+  // straight out.
+  const bool c_stage = (ldc & 7) == 0;
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    const int col = n0 + wcol + 32 * b + l32;
-    if (col < N) {
-      const float ls = MODE == 1 ? gp(L.lpad)[col] : 1.f;
-      LB_GLOBAL uint16_t* cp = gp(C) + col;
+    const int cb = n0 + wcol + 32 * b + 4 * kg;
+    float ls[16];
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+    for (int q = 0; q < 16; ++q) ls[q] = 1.f;
+    if (MODE == 1) {
+      // GEMM1: N = Rp is a multiple of 64, so a run is wholly inside or outside
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int row = m0 + wm * MB * 32 + mb * 32 + 8 * (q >> 2) + 4 * kg + (q & 3);
-          if (row < T) cp[(int64_t)row * ldc] = f32_to_bf16_rne(acc[mb][b][q] * ls);
+      for (int j = 0; j < 4; ++j)
+        if (cb + 8 * j < N) {
+          const f4 v = *reinterpret_cast<const LB_GLOBAL f4*>(gp(L.lpad) + cb + 8 * j);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ls[4 * j + i] = v[i];
         }
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int rt = wm * MB * 32 + mb * 32 + l32;   // row inside the tile
+      const int row = m0 + rt;
+      LB_GLOBAL uint16_t* cp = gp(C) + (int64_t)row * ldc;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int col = cb + 8 * j;
+        const f2 lo = {acc[mb][b][4 * j] * ls[4 * j], acc[mb][b][4 * j + 1] * ls[4 * j + 1]};
+        const f2 hi = {acc[mb][b][4 * j + 2] * ls[4 * j + 2], acc[mb][b][4 * j + 3] * ls[4 * j + 3]};
+        const uint32_t w0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf2));
+        const uint32_t w1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf2));
+        if (c_stage) {
+          // 8-byte slot (col - n0) / 4 of tile row rt, XOR-swizzled by rt % 16
+          // so that the 16 rows a write phase covers hit distinct banks
+          const int slot = ((col - n0) >> 2) ^ (rt & 15);
+          *reinterpret_cast<u32x2*>(lds + rt * (kPreBN * 2) + slot * 8) = u32x2{w0, w1};
+        } else if (row < T) {
+          const uint32_t w[2] = {w0, w1};
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (col + i < N) cp[col + i] = (uint16_t)(w[i >> 1] >> (16 * (i & 1)));
+        }
+      }
+    }
+  }
+  if (c_stage) {
+    __syncthreads();
+    constexpr int kChunks = kPreBM * kPreBN / 8;   // 16-byte chunks of the tile
+    const int tid_all = threadIdx.x;
+#pragma unroll 4
+    for (int c = tid_all; c < kChunks; c += kNT) {
+      const int rt = c / (kPreBN / 8), ch = c % (kPreBN / 8);
+      const int row = m0 + rt, col = n0 + ch * 8;
+      if (row >= T || col >= N) continue;
+      // logical slots 2 ch, 2 ch + 1 sit in the 16-byte chunk ch ^ (r / 2),
+      // in swapped order when r is odd (r = rt % 16)
+      const int r = rt & 15;
+      u32x4 v = *reinterpret_cast<const u32x4*>(lds + rt * (kPreBN * 2) + ((ch ^ (r >> 1)) * 16));
+      if (r & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+      LB_GLOBAL uint16_t* cp = gp(C) + (int64_t)row * ldc + col;
+      if (col + 7 < N) {
+        *reinterpret_cast<LB_GLOBAL u32x4*>(cp) = v;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (col + i < N) cp[i] = (uint16_t)(v[i >> 1] >> (16 * (i & 1)));
+      }
     }
   }
 }
@@ -437,6 +504,7 @@ bool tile_straddles(const PrefillLayer& L, int nt) {
 }
 constexpr int kThreads = 64 * kPreWM * kPreWNv;
 constexpr size_t kPreLds = kPreBufs * (size_t)(kPreBM * kPreBK * 2 + 2 * 64 * 16 + 2 * kPreBK * 2);
+static_assert(kPreLds >= (size_t)kPreBM * kPreBN * 2, "the epilogue stages the bf16 tile in the LDS buffers");
 
 }  // namespace
 
