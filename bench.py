@@ -4,8 +4,9 @@
 Default workload: the Llama-2-70B-shaped stack at 0.1 sign bits per weight
 (80 layers x {q, k, v, o, gate, up, down}, both paths, 560 linears, 0.91 GB
 of packed signs + fp16 scales), decode at batch 1, run as one lb_stack_forward
-per step (HIP graph replay of the three decode kernels, V stage, mid stage
-and U stage, each over every linear of the stack).  Inputs are seeded synthetic data
+per step (three kernel launches, V stage, mid stage and U stage, each over
+every linear of the stack; the HIP-graph replay of the same three is timed
+beside it).  Inputs are seeded synthetic data
 resident in HBM before timing starts.
 
 Prints one JSON line: the decode step's microseconds per token and achieved
@@ -107,6 +108,172 @@ def time_steps(fn, steps, warmup, torch):
     return wall, ev0.elapsed_time(ev1) / steps   # seconds; ms per step on the stream
 
 
+def replay_stats(fn, torch, n=50, cold_mb=0):
+    """n replays enqueued back to back, each bracketed by its own pair of HIP
+    events on the launch stream (the host runs ahead, so a bracket holds the
+    replay's GPU time, not the host's launch latency); with cold_mb, a scratch
+    buffer of that size (written once) is read before each replay, outside its
+    bracket, so the replay finds none of its data in the 256 MB Infinity Cache
+    (and no dirty scratch lines are left to write back during it).
+    Returns p10 / p50 / p90 in microseconds."""
+    st = torch.cuda.current_stream()
+    scratch = torch.ones((cold_mb << 20) // 4, dtype=torch.float32, device="cuda") if cold_mb else None
+    evs = []
+    fn()
+    torch.cuda.synchronize()
+    for i in range(n):
+        if scratch is not None:
+            scratch.sum()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        fn()
+        e1.record(st)
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    times = [a.elapsed_time(b) * 1e3 for a, b in evs]
+    q = np.percentile(np.array(times), [10, 50, 90])
+    return {"p10": round(float(q[0]), 2), "p50": round(float(q[1]), 2), "p90": round(float(q[2]), 2)}
+
+
+def achievable_peaks(torch):
+    """What this GPU reaches on plain work, measured in the same run: a graph
+    replay of one tiny kernel (launch floor), a streaming read of 4 GiB (the
+    library's plain-load probe; torch's sum and copy beside it), a large bf16
+    GEMM (hipBLASLt through torch.matmul)."""
+    out = {}
+    st = torch.cuda.current_stream()
+    tiny = torch.zeros(1, device="cuda")
+    tiny.add_(1)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        tiny.add_(1)
+    torch.cuda.synchronize()
+    out["launch_floor_us"] = replay_stats(g.replay, torch, n=50)["p50"]
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(reps):
+            fn()
+        e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3   # seconds per call
+
+    big = torch.ones(1 << 30, dtype=torch.float32, device="cuda")
+    import binary_rank_gemm_amd as lb
+    t = timed(lambda: lb.probe_stream_read(big), 10)
+    out["probe_read_gbps"] = round(big.numel() * 4 / t / 1e9, 1)
+    t = timed(lambda: big.sum(), 10)
+    out["sum_read_gbps"] = round(big.numel() * 4 / t / 1e9, 1)
+    dst = torch.empty_like(big)
+    t = timed(lambda: dst.copy_(big), 10)
+    out["copy_read_write_gbps"] = round(2 * big.numel() * 4 / t / 1e9, 1)
+    del big, dst
+    a = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    t = timed(lambda: a @ b, 20)
+    out["bf16_gemm_8192_tflops"] = round(2 * 8192 ** 3 / t / 1e12, 1)
+    del a, b
+    torch.cuda.empty_cache()
+    return out
+
+
+def dense_comparators(torch, wl_dec, ranks_dec, wl_pre, ranks_pre, T_pre):
+    """The same shapes run the dense way, for the pages' comparison with an
+    fp16 model and with decompress-then-compute: (1) dense bf16 weights, one
+    GEMV per linear per token; (2) W rebuilt per forward from its factors as
+    bf16 GEMMs, then the GEMV; (3) dense bf16 prefill GEMMs.  One layer's
+    weights are generated and reused for every layer (each layer's weights
+    exceed the Infinity Cache, so every GEMV still streams them from HBM).
+    Dense weights are [m, n] as a PyTorch Linear holds them (F.linear: one 2-D
+    GEMM per call, hipBLASLt's preferred NT form); no batched products."""
+    st = torch.cuda.current_stream()
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(reps):
+            fn()
+        e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
+
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1234)
+    out = {}
+    # (1) dense decode (weights [m, n] as a PyTorch Linear holds them; y = x W^T)
+    wts = [torch.randn(s.m, s.n, device="cuda", dtype=torch.bfloat16, generator=gen) for s in wl_dec.mats]
+    xs = [torch.randn(1, s.n, device="cuda", dtype=torch.bfloat16, generator=gen) for s in wl_dec.mats]
+
+    def dense_step():
+        for _ in range(wl_dec.layers):
+            for x, w in zip(xs, wts):
+                torch.nn.functional.linear(x, w)
+    out["dense_bf16_decode_us_per_token"] = round(timed(dense_step, 3) * 1e6, 1)
+    del wts
+    # (2) decompress-then-compute: W = sum_p (h o U o l)(V o g)^T rebuilt as bf16 GEMMs, then the GEMV
+    facs = []
+    for j, s in enumerate(wl_dec.mats):
+        per = []
+        for r in ranks_dec[j]:
+            a = torch.randn(s.m, r, device="cuda", dtype=torch.bfloat16, generator=gen)
+            b = torch.randn(r, s.n, device="cuda", dtype=torch.bfloat16, generator=gen)
+            per.append((a, b))
+        facs.append(per)
+    wbuf = [torch.empty(s.m, s.n, device="cuda", dtype=torch.bfloat16) for s in wl_dec.mats]
+    xs_t = [x.t().contiguous() for x in xs]   # [n, 1]
+
+    def rebuild_step():
+        for _ in range(wl_dec.layers):
+            for per, w, xt in zip(facs, wbuf, xs_t):
+                torch.matmul(per[0][0], per[0][1], out=w)
+                for a, b in per[1:]:
+                    w.addmm_(a, b)
+                torch.matmul(w, xt)
+    out["decompress_then_compute_us_per_token"] = round(timed(rebuild_step, 1) * 1e6, 1)
+    del facs, wbuf
+    # (3) dense prefill
+    wts = [torch.randn(s.m, s.n, device="cuda", dtype=torch.bfloat16, generator=gen) for s in wl_pre.mats]
+    xs = [torch.randn(T_pre, s.n, device="cuda", dtype=torch.bfloat16, generator=gen) for s in wl_pre.mats]
+
+    def dense_prefill():
+        for _ in range(wl_pre.layers):
+            for x, w in zip(xs, wts):
+                torch.nn.functional.linear(x, w)
+    out["dense_bf16_prefill_ms"] = round(timed(dense_prefill, 3) * 1e3, 2)
+    del wts, xs
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_info():
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            blas = f"{info[0].get('internal_api')} ({info[0].get('num_threads')} threads)"
+    except Exception:
+        pass
+    return dict(cpu_model=model, cpu_count=os.cpu_count(), affinity=len(os.sched_getaffinity(0)), blas=blas)
+
+
 def cpu_baseline(wl, ranks_of, T, budget_s=15.0):
     """The oracle (explicit W, fp64) on whole layers of the workload until the
     time budget is spent; scaled to the full stack per token."""
@@ -115,13 +282,17 @@ def cpu_baseline(wl, ranks_of, T, budget_s=15.0):
     t_start = time.perf_counter()
     done_layers = 0
     elapsed = 0.0
+    elapsed_f = 0.0
     for l in range(wl.layers):
         for j, s in enumerate(wl.mats):
             paths = synth.layer_tensors(wl.wid, l, j, s.m, s.n, ranks_of[j])
             x = oracle.decode_bf16(synth.layer_activations(wl, l, j, s.n, T, io="bf16"))
             t0 = time.perf_counter()
             oracle.forward(x, paths, s.m, s.n)
-            elapsed += time.perf_counter() - t0
+            t1 = time.perf_counter()
+            oracle.forward_factored(x, paths, s.m, s.n)
+            elapsed += t1 - t0
+            elapsed_f += time.perf_counter() - t1
         done_layers += 1
         if time.perf_counter() - t_start > budget_s:
             break
@@ -137,7 +308,9 @@ def cpu_baseline(wl, ranks_of, T, budget_s=15.0):
     return dict(value=per_layer * wl.layers * 1e6 / T, unit="us/token", cores=threads, kind="oracle",
                 sample=f"{done_layers} of {wl.layers} layers ({done_layers * len(wl.mats)} linears), "
                        f"T={T}, explicit fp64 W then x W^T; scaled to the full stack",
-                seconds=round(elapsed, 2))
+                seconds=round(elapsed, 2),
+                factored_fp64_us_per_token=round(elapsed_f / done_layers * wl.layers * 1e6 / T, 1),
+                **cpu_info())
 
 
 def read_traffic(kernel_file, workload):
@@ -162,13 +335,17 @@ def run_decode(args, lb, torch):
     if args.layers:
         wl = dataclasses.replace(wl, layers=min(args.layers, wl.layers))
     S = lb.Stack(lins)
-    fn = lambda: S.forward(xs, ys, regime=lb.REGIME_DECODE, use_graph=True)
+    # direct launches of the decode kernels: on this ROCm a HIP graph replay
+    # adds ~13 us of its own per replay (timed below and reported beside)
+    fn = lambda: S.forward(xs, ys, regime=lb.REGIME_DECODE, use_graph=False)
     wall, kern_ms = time_steps(fn, args.steps, args.warmup, torch)
+    fn_g = lambda: S.forward(xs, ys, regime=lb.REGIME_DECODE, use_graph=True)
+    _, graph_ms = time_steps(fn_g, args.steps, args.warmup, torch)
     byts, flops = algorithmic(wl, ranks_of, T)
     ms = wall * 1e3 / args.steps
     gbps = byts / (kern_ms * 1e-3) / 1e9
-    return dict(wl=wl, T=T, ranks_of=ranks_of, ms=ms, kern_ms=kern_ms, bytes=byts, flops=flops,
-                gbps=gbps, stack=S, lins=lins)
+    return dict(wl=wl, T=T, ranks_of=ranks_of, ms=ms, kern_ms=kern_ms, graph_ms=graph_ms, bytes=byts, flops=flops,
+                gbps=gbps, stack=S, lins=lins, xs=xs, ys=ys)
 
 
 def run_prefill(args, lb, torch, workload):
@@ -199,6 +376,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-only", action="store_true", help="time only the prefill stack (for profiling)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the per-replay and cold-cache timings, the achievable-peak probes and the dense comparators")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="before timing, run one device-to-device copy of this many MiB (a known-size "
                          "reference for the FETCH_SIZE / WRITE_SIZE counters)")
@@ -251,14 +430,19 @@ def main():
         "hbm_frac": round(r["gbps"] / HBM_PEAK_GBPS, 4),
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode step: k_decode_v, k_decode_mid, k_decode_u over all linears (one graph launch)",
+            "kernel": "decode step: k_decode_v, k_decode_mid, k_decode_u over all linears (three direct launches)",
             "achieved": round(r["gbps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(r["gbps"] / HBM_PEAK_GBPS, 4),
             "traffic": read_traffic("lb_decode.hip", args.workload),
             "algorithmic_bytes_per_launch": int(r["bytes"]),
             "kernel_ms_mean": round(r["kern_ms"], 5),
         },
+        "graph_replay_us_per_step": round(r["graph_ms"] * 1e3, 2),
     }
+    fn = lambda: r["stack"].forward(r["xs"], r["ys"], regime=lb.REGIME_DECODE, use_graph=False)
+    if not args.no_context:
+        out["decode_replays"] = {"n": 50, "warm_us": replay_stats(fn, torch, 50),
+                                 "cold_us": replay_stats(fn, torch, 50, cold_mb=512), "cold_scratch_mb": 512}
     if not args.no_prefill and args.layers is None:
         try:
             p = run_prefill(args, lb, torch, "cfg3-prefill")
@@ -266,9 +450,24 @@ def main():
             log(f"prefill: {p['ms_per_step']:.2f} ms/step, {p['tflops']:.0f} TFLOP/s")
         except lb.LittleBitError as e:
             out["prefill"] = {"error": str(e)}
+    del r["stack"], r["lins"], r["xs"], r["ys"], fn
+    torch.cuda.empty_cache()
+    if not args.no_context and args.layers is None:
+        import synth
+        ctx = achievable_peaks(torch)
+        ctx["decode_frac_of_probe_read"] = round(r["gbps"] / ctx["probe_read_gbps"], 4)
+        if "prefill" in out and "tflops" in out["prefill"]:
+            ctx["prefill_frac_of_bf16_gemm"] = round(out["prefill"]["tflops"] / ctx["bf16_gemm_8192_tflops"], 4)
+        out["achievable_peaks"] = ctx
+        wl_pre_name, T_pre, _ = WORKLOADS["cfg3-prefill"]
+        wl_pre = synth.WORKLOADS[wl_pre_name]
+        cmp_ = dense_comparators(torch, wl, r["ranks_of"], wl_pre, [ranks_for(wl_pre, s, lb) for s in wl_pre.mats], T_pre)
+        cmp_["speedup_vs_dense_bf16_decode"] = round(cmp_["dense_bf16_decode_us_per_token"] / us_per_token, 1)
+        cmp_["speedup_vs_decompress_then_compute"] = round(cmp_["decompress_then_compute_us_per_token"] / us_per_token, 1)
+        if "prefill" in out and "ms_per_step" in out["prefill"]:
+            cmp_["speedup_vs_dense_bf16_prefill"] = round(cmp_["dense_bf16_prefill_ms"] / out["prefill"]["ms_per_step"], 2)
+        out["comparators"] = cmp_
     if not args.no_cpu:
-        del r["stack"], r["lins"]
-        torch.cuda.empty_cache()
         out["cpu_baseline"] = cpu_baseline(wl, r["ranks_of"], T)
     print(json.dumps(out), flush=True)
 

@@ -30,7 +30,7 @@ EXPORTS = [
     "lb_packed_words_per_row", "lb_rank_for_bpw", "lb_pack_signs_host", "lb_pack_signs", "lb_unpack_signs",
     "lb_linear_create", "lb_linear_forward", "lb_linear_forward_ex", "lb_linear_info", "lb_linear_destroy",
     "lb_stack_create", "lb_stack_forward", "lb_stack_forward_ex", "lb_stack_destroy", "lb_status_string",
-    "lb_last_error",
+    "lb_last_error", "lb_probe_stream_read",
 ]
 
 
@@ -75,6 +75,7 @@ def lib():
         "lb_stack_destroy": (C.c_int, [vp]),
         "lb_status_string": (C.c_char_p, [C.c_int]),
         "lb_last_error": (C.c_char_p, []),
+        "lb_probe_stream_read": (C.c_int, [vp, i64, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -129,6 +130,12 @@ def unpack_signs(packed, rank: int, stream=None):
     out = torch.empty((rows, rank), dtype=torch.int8, device=packed.device)
     _check(lib().lb_unpack_signs(packed.data_ptr(), rows, rank, out.data_ptr(), _stream(stream)))
     return out
+
+
+def probe_stream_read(buf, stream=None) -> None:
+    """Enqueue lb_probe_stream_read over a device tensor (a measurement aid)."""
+    _check(lib().lb_probe_stream_read(C.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(),
+                                      _stream(stream)))
 
 
 def _io_of(t) -> int:
@@ -224,7 +231,10 @@ class Stack:
         _check(lib().lb_stack_create(arr, len(self.linears), C.byref(h)))
         self.handle = h
 
-    def forward(self, xs: Sequence, ys: Sequence, regime: int = REGIME_AUTO, use_graph: bool = True, stream=None):
+    def forward(self, xs: Sequence, ys: Sequence, regime: int = REGIME_AUTO, use_graph: Optional[bool] = None,
+                stream=None):
+        """use_graph None: the library's choice (lb_stack_forward); True / False:
+        capture into a HIP graph and replay / launch directly."""
         n = len(self.linears)
         if len(xs) != n or len(ys) != n:
             raise ValueError("need one x and one y per linear")
@@ -232,8 +242,13 @@ class Stack:
         io = _io_of(xs[0])
         xa = (C.c_void_p * n)(*[x.data_ptr() for x in xs])
         ya = (C.c_void_p * n)(*[y.data_ptr() for y in ys])
-        _check(lib().lb_stack_forward_ex(self.handle, xa, ya, tokens, io, regime, 1 if use_graph else 0,
-                                         _stream(stream)))
+        if use_graph is None and regime == REGIME_AUTO:
+            _check(lib().lb_stack_forward(self.handle, xa, ya, tokens, io, _stream(stream)))
+        else:
+            if use_graph is None:
+                use_graph = regime == REGIME_EXACT
+            _check(lib().lb_stack_forward_ex(self.handle, xa, ya, tokens, io, regime, 1 if use_graph else 0,
+                                             _stream(stream)))
         return ys
 
     __call__ = forward

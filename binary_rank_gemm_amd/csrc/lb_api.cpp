@@ -404,6 +404,14 @@ lb_status lb_pack_signs(const int8_t* signs, int64_t rows, int64_t rank, uint32_
   return LB_OK;
 }
 
+lb_status lb_probe_stream_read(const void* buf, int64_t bytes, void* stream) {
+  if (!buf) return fail(LB_ERR_INVALID_ARGUMENT, "null buffer");
+  if (bytes <= 0 || bytes % 16) return fail(LB_ERR_INVALID_ARGUMENT, "bytes must be a positive multiple of 16");
+  if (!aligned16(buf)) return fail(LB_ERR_ALIGNMENT, "buffer not 16-byte aligned");
+  HIP_TRY(launch_probe_stream_read(buf, bytes, reinterpret_cast<hipStream_t>(stream)));
+  return LB_OK;
+}
+
 lb_status lb_unpack_signs(const uint32_t* packed, int64_t rows, int64_t rank, int8_t* signs, void* stream) {
   if (!signs || !packed) return fail(LB_ERR_INVALID_ARGUMENT, "null pointer");
   if (rows <= 0 || rank <= 0) return fail(LB_ERR_INVALID_ARGUMENT, "rows and rank must be positive");
@@ -743,7 +751,10 @@ lb_status lb_stack_forward_ex(lb_stack S, const void* const* xs, void* const* ys
 
 lb_status lb_stack_forward(lb_stack S, const void* const* xs, void* const* ys, int64_t tokens, lb_dtype io,
                            void* stream) {
-  return lb_stack_forward_ex(S, xs, ys, tokens, io, LB_REGIME_AUTO, 1, stream);
+  // a graph only where launches are many (exact: two per linear); for the
+  // decode and prefill kernels a graph replay costs more than it saves
+  const lb_regime rg = pick_regime(tokens, io, LB_REGIME_AUTO);
+  return lb_stack_forward_ex(S, xs, ys, tokens, io, LB_REGIME_AUTO, rg == LB_REGIME_EXACT ? 1 : 0, stream);
 }
 
 lb_status lb_stack_destroy(lb_stack S) {

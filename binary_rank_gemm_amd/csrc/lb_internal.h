@@ -157,6 +157,8 @@ hipError_t launch_decode_u(const DecArgs& a, int nitems, hipStream_t st);
 // layouts of the decode U stage (built once per linear)
 hipError_t launch_decode_u_layout(const uint32_t* ucan0, const uint32_t* ucan1, int m, const int* W, const UGeom& g,
                                   uint8_t* udec, hipStream_t st);
+// calibration: one read-only streaming pass over a device buffer
+hipError_t launch_probe_stream_read(const void* buf, int64_t bytes, hipStream_t st);
 hipError_t launch_decode_h_layout(const uint16_t* h0, const uint16_t* h1, int m, int nq, uint16_t* hq,
                                   hipStream_t st);
 

@@ -150,15 +150,17 @@ lb_status lb_stack_create(const lb_linear* linears, int32_t count, lb_stack* out
 /* Runs every linear i of the stack: ys[i] = xs[i] W_i^T, `tokens` rows each
  * (xs and ys are host arrays of `count` device pointers).  Entries are
  * independent: the library runs them concurrently, so no ys[i] may alias any
- * xs[j] or another ys[k].  The launch sequence is captured once into a HIP
- * graph and replayed on `stream`; it is re-captured when the pointers,
- * tokens, io or regime change.  Calls on one stack must be ordered on one
- * stream (they share the stack's scratch memory and graph). */
+ * xs[j] or another ys[k].  The decode and prefill kernels (a few launches
+ * per step) go directly onto `stream`; the exact fp32 kernels (two launches
+ * per linear) are captured once into a HIP graph and replayed, re-captured
+ * when the pointers, tokens, io or regime change.  Calls on one stack must be
+ * ordered on one stream (they share the stack's scratch memory and graph). */
 lb_status lb_stack_forward(lb_stack S, const void* const* xs, void* const* ys, int64_t tokens,
                            lb_dtype io, void* stream);
 
-/* As lb_stack_forward with an explicit regime and graph use (use_graph = 0
- * launches the same kernels directly, without a graph). */
+/* As lb_stack_forward with an explicit regime and graph use (use_graph = 1
+ * captures the launches of any regime into a HIP graph and replays it;
+ * use_graph = 0 launches the same kernels directly). */
 lb_status lb_stack_forward_ex(lb_stack S, const void* const* xs, void* const* ys, int64_t tokens,
                               lb_dtype io, lb_regime regime, int32_t use_graph, void* stream);
 
@@ -170,6 +172,15 @@ const char* lb_status_string(lb_status s);
 
 /* Thread-local description of this thread's last failure ("" if none). */
 const char* lb_last_error(void);
+
+/* Measurement aid, not part of the method: enqueues on `stream` one
+ * read-only streaming pass over `bytes` bytes of device memory at `buf`
+ * (16-byte loads, grid-stride), so that a caller timing it with events gets
+ * the HBM read bandwidth plain loads reach on this GPU.  buf must be 16-byte
+ * aligned and bytes a positive multiple of 16 (LB_ERR_ALIGNMENT /
+ * LB_ERR_INVALID_ARGUMENT otherwise).  Reads only; writes nothing the caller
+ * can see. */
+lb_status lb_probe_stream_read(const void* buf, int64_t bytes, void* stream);
 
 #ifdef __cplusplus
 }

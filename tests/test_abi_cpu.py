@@ -110,6 +110,9 @@ def test_argument_validation_before_any_device_work():
     assert L.lb_pack_signs(None, 1, 1, dummy, None) == lb._binding.INVALID_ARGUMENT
     assert L.lb_unpack_signs(dummy, 0, 1, dummy, None) == lb._binding.INVALID_ARGUMENT
     assert L.lb_packed_words_per_row(0) == 0 and L.lb_packed_words_per_row(32) == 1
+    assert L.lb_probe_stream_read(None, 16, None) == lb._binding.INVALID_ARGUMENT
+    assert L.lb_probe_stream_read(dummy, 0, None) == lb._binding.INVALID_ARGUMENT
+    assert L.lb_probe_stream_read(dummy, 24, None) == lb._binding.INVALID_ARGUMENT
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
