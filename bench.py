@@ -348,6 +348,39 @@ def run_decode(args, lb, torch):
                 gbps=gbps, stack=S, lins=lins, xs=xs, ys=ys)
 
 
+def run_chained(r, lb, torch, steps=20, warmup=5):
+    """The same linears listed in a model's real order and chained through
+    their buffers (per layer: q, k, v read the layer input; o reads q's
+    output; gate and up read o's; down reads gate's; the next layer reads
+    down's), so the stack runs level after level: per-token latency of a real
+    model's linears at batch 1, where the independent stack is a bandwidth
+    figure.  Outputs of k, v and up are not consumed (attention and the MLP's
+    elementwise product are not part of the method)."""
+    wl, T, lins = r["wl"], r["T"], r["lins"]
+    d_model = wl.mats[0].n
+    x0 = torch.randn(T, d_model, device="cuda").to(torch.bfloat16)
+    ys = [torch.empty((T, lins[i].d_out), dtype=torch.bfloat16, device="cuda") for i in range(len(lins))]
+    xs = []
+    names = [s.name for s in wl.mats]
+    qi, oi, gi, di = names.index("q"), names.index("o"), names.index("gate"), names.index("down")
+    for l in range(wl.layers):
+        b = 7 * l
+        inp = x0 if l == 0 else ys[b - 7 + di]
+        src = {"q": inp, "k": inp, "v": inp, "o": ys[b + qi], "gate": ys[b + oi], "up": ys[b + oi],
+               "down": ys[b + gi]}
+        xs += [src[nm] for nm in names]
+    S = lb.Stack(lins)
+    out = {}
+    for lab, g in (("direct", False), ("graph", True)):
+        fn = lambda: S.forward(xs, ys, regime=lb.REGIME_DECODE, use_graph=g)
+        _, ms = time_steps(fn, steps, warmup, torch)
+        out[f"us_per_token_{lab}"] = round(ms * 1e3 / T, 1)
+    out["levels"] = 4 * wl.layers
+    out["workload"] = f"{wl.name}: {wl.count} linears chained in model order, batch {T}"
+    S.close()
+    return out
+
+
 def run_prefill(args, lb, torch, workload):
     import synth
     wl_name, T, _ = WORKLOADS[workload]
@@ -443,6 +476,9 @@ def main():
     if not args.no_context:
         out["decode_replays"] = {"n": 50, "warm_us": replay_stats(fn, torch, 50),
                                  "cold_us": replay_stats(fn, torch, 50, cold_mb=512), "cold_scratch_mb": 512}
+        if args.layers is None:
+            out["chained_decode"] = run_chained(r, lb, torch)
+            log(f"chained decode: {out['chained_decode']}")
     if not args.no_prefill and args.layers is None:
         try:
             p = run_prefill(args, lb, torch, "cfg3-prefill")

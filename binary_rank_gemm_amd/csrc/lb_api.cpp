@@ -143,18 +143,36 @@ struct DecodeImage {
   std::vector<std::array<const uint32_t*, 2>> vdec;
 };
 
+// Entries of a stack that run together: a level of mutually independent
+// entries (all of them when no entry reads or writes another's output).
+struct StackGroup {
+  std::vector<int> idx;                     // entries of the stack, in order
+  std::vector<lb_linear> lins;
+  std::vector<const PrefillLayer*> pre;
+  DecodeImage view;                         // the stack image's layouts of these entries (buf unused)
+  DecodePlan plan;
+  PrefillPlan pplan;
+  const void** xs_d = nullptr;              // device copies of the entries' pointers
+  void** ys_d = nullptr;
+  std::vector<const void*> xs_h;
+  std::vector<void*> ys_h;
+  void release() {
+    if (xs_d) (void)hipFree(xs_d);
+    if (ys_d) (void)hipFree(ys_d);
+    xs_d = nullptr;
+    ys_d = nullptr;
+    plan.release();
+    prefill_plan_release(pplan);
+  }
+};
+
 struct lb_stack_s {
   int device = 0;
   std::vector<lb_linear> linears;
   DecodeImage dimg;
-  std::vector<const PrefillLayer*> pre;
-  DecodePlan plan;
-  PrefillPlan pplan;
+  std::vector<StackGroup> groups;           // decode / prefill launch groups, run in order
   Scratch zexact;
-  // device copies of the caller's pointer arrays
-  const void** xs_d = nullptr;
-  void** ys_d = nullptr;
-  std::vector<const void*> xs_h;
+  std::vector<const void*> xs_h;            // the caller's pointers of the current plans
   std::vector<void*> ys_h;
   // captured graph and what it was captured for
   hipGraph_t graph = nullptr;
@@ -219,6 +237,19 @@ lb_status build_decode_plan(DecodePlan& P, const lb_linear* L, int count, int T,
   size_t work_bytes = 0;
   std::vector<size_t> img_off(count), cv_off(count);
   int slots = 0;
+  // Item sizes: about 192 KB of sign words per item when the launch has
+  // plenty of work; a launch with little (one level of a chained stack) is
+  // cut finer, aiming at ~1024 items, so that its latency is that of a small
+  // item rather than of a few large ones.
+  double vtotal = 0, utotal = 0;
+  for (int e = 0; e < count; ++e) {
+    const int nkc = (int)((L[e]->n + kChunk - 1) / kChunk);
+    for (int p = 0; p < L[e]->np; ++p) vtotal += (double)nkc * L[e]->paths[p].nct * 256.0;
+    utotal += (double)L[e]->ug.nq * (L[e]->ug.qbytes + 256.0);
+  }
+  constexpr double kMinItemBytes = 16 * 1024;
+  const double vtarget = std::min<double>(kDecodeVItemBytes, std::max(kMinItemBytes, vtotal / 1024));
+  const double utarget = std::min<double>(kDecodeUItemBytes, std::max(kMinItemBytes, utotal / 1024));
   for (int e = 0; e < count; ++e) {
     const lb_linear l = L[e];
     DecEntry& E = P.entries_h[e];
@@ -239,7 +270,7 @@ lb_status build_decode_plan(DecodePlan& P, const lb_linear* L, int count, int T,
       const int gt = (nct + groups - 1) / groups;
       const double chunk_bytes = gt * 256.0;
       const int max_split = std::max(1, E.nkc / kWavesPerGroup);
-      const int nsplit = std::max(1, std::min(max_split, (int)std::lround(E.nkc * chunk_bytes / kDecodeVItemBytes)));
+      const int nsplit = std::max(1, std::min(max_split, (int)std::lround(E.nkc * chunk_bytes / vtarget)));
       ml.push_back(MItem{e, p, slots, groups, nsplit, gt, 0, 0});
       for (int g = 0; g < groups; ++g) {
         const int tile0 = g * gt, nt = std::min(gt, nct - tile0);
@@ -257,7 +288,7 @@ lb_status build_decode_plan(DecodePlan& P, const lb_linear* L, int count, int T,
     work_bytes += align256(2 * 16 * sizeof(float));
     const double qbytes = E.ug.qbytes + 256.0;
     const int qw = std::max(1, std::min(decode_u_qw_max(bucket),
-                                        (int)std::lround(kDecodeUItemBytes / (kWavesPerGroup * qbytes))));
+                                        (int)std::lround(utarget / (kWavesPerGroup * qbytes))));
     for (int q0 = 0; q0 < E.ug.nq; q0 += kWavesPerGroup * qw) {
       const int nq = std::min(kWavesPerGroup * qw, E.ug.nq - q0);
       // a short run (small entries, the last run) is spread over all four waves
@@ -629,10 +660,7 @@ lb_status lb_stack_create(const lb_linear* linears, int32_t count, lb_stack* out
   if (!S) return fail(LB_ERR_OUT_OF_MEMORY, "host allocation failed");
   S->device = linears[0]->device;
   S->linears.assign(linears, linears + count);
-  for (int i = 0; i < count; ++i) S->pre.push_back(&linears[i]->pre);
-  hipError_t e = hipMalloc(&S->xs_d, count * sizeof(void*));
-  if (e == hipSuccess) e = hipMalloc(&S->ys_d, count * sizeof(void*));
-  if (e == hipSuccess) e = hipStreamCreateWithFlags(&S->cap_stream, hipStreamNonBlocking);
+  hipError_t e = hipStreamCreateWithFlags(&S->cap_stream, hipStreamNonBlocking);
   if (e == hipSuccess) e = build_decode_image(S->dimg, S->linears);
   if (e != hipSuccess) {
     lb_stack_destroy(S);
@@ -647,10 +675,18 @@ namespace {
 // Enqueues the stack's kernels on `st` (no graph).
 lb_status stack_launch(lb_stack S, lb_regime rg, int64_t tokens, lb_dtype io, hipStream_t st) {
   const int count = (int)S->linears.size();
-  if (rg == LB_REGIME_DECODE)
-    return run_decode(S->plan, S->linears.data(), count, S->xs_d, S->ys_d, nullptr, nullptr, tokens, st, &S->dimg);
+  if (rg == LB_REGIME_DECODE) {
+    for (StackGroup& G : S->groups) {
+      lb_status s = run_decode(G.plan, G.lins.data(), (int)G.lins.size(), G.xs_d, G.ys_d, nullptr, nullptr, tokens, st,
+                               &G.view);
+      if (s != LB_OK) return s;
+    }
+    return LB_OK;
+  }
   if (rg == LB_REGIME_PREFILL) {
-    HIP_TRY(prefill_run(S->pplan, S->pre.data(), count, S->xs_h.data(), S->ys_h.data(), (int)tokens, st, false));
+    for (StackGroup& G : S->groups)
+      HIP_TRY(prefill_run(G.pplan, G.pre.data(), (int)G.lins.size(), G.xs_h.data(), G.ys_h.data(), (int)tokens, st,
+                          false));
     return LB_OK;
   }
   // exact: one pair of kernels per linear, sharing one z' scratch laid out per entry
@@ -667,20 +703,84 @@ lb_status stack_launch(lb_stack S, lb_regime rg, int64_t tokens, lb_dtype io, hi
   return LB_OK;
 }
 
-// Prepares everything a launch sequence needs outside of any graph capture.
-lb_status stack_prepare(lb_stack S, lb_regime rg, int64_t tokens) {
-  const int count = (int)S->linears.size();
-  if (rg == LB_REGIME_DECODE) {
-    const int T = (int)std::min<int64_t>(tokens, kDecodeMaxTokens);
-    lb_status s = build_decode_plan(S->plan, S->linears.data(), count, T, &S->dimg);
-    if (s != LB_OK) return s;
-    if (tokens > kDecodeMaxTokens && tokens % kDecodeMaxTokens) {
-      // a ragged last slice uses another plan shape: keep direct launches for it
-      return LB_OK;
+// Levels of the stack's entries: entry j runs after every earlier entry i
+// whose output it reads (y_i overlaps x_j), whose output it also writes
+// (y_i overlaps y_j) or whose input it overwrites (y_j overlaps x_i);
+// level[j] = 1 + the highest such level[i], 0 if none.  An entry whose y
+// overlaps its own x is refused (-1 in bad).
+std::vector<int> stack_levels(const std::vector<lb_linear>& lins, const std::vector<const void*>& xs,
+                              const std::vector<void*>& ys, int64_t tokens, lb_dtype io, int* bad) {
+  const int count = (int)lins.size();
+  *bad = -1;
+  const uint64_t es = io == LB_FP32 ? 4 : 2;
+  auto range = [&](const void* p, int64_t cols) {
+    const uint64_t a = reinterpret_cast<uintptr_t>(p);
+    return std::make_pair(a, a + (uint64_t)tokens * (uint64_t)cols * es);
+  };
+  auto overlap = [](std::pair<uint64_t, uint64_t> u, std::pair<uint64_t, uint64_t> v) {
+    return u.first < v.second && v.first < u.second;
+  };
+  std::vector<int> level(count, 0);
+  for (int j = 0; j < count; ++j) {
+    const auto xj = range(xs[j], lins[j]->n), yj = range(ys[j], lins[j]->m);
+    if (overlap(xj, yj) && *bad < 0) *bad = j;
+    for (int i = 0; i < j; ++i) {
+      const auto xi = range(xs[i], lins[i]->n), yi = range(ys[i], lins[i]->m);
+      if (overlap(yi, xj) || overlap(yi, yj) || overlap(yj, xi)) level[j] = std::max(level[j], level[i] + 1);
     }
+  }
+  return level;
+}
+
+// Splits the stack into launch groups by level (one group when the entries
+// are independent) and copies each group's pointers to the device.
+lb_status stack_groups(lb_stack S, int64_t tokens, lb_dtype io) {
+  const int count = (int)S->linears.size();
+  int bad = -1;
+  const std::vector<int> level = stack_levels(S->linears, S->xs_h, S->ys_h, tokens, io, &bad);
+  if (bad >= 0) return fail(LB_ERR_INVALID_ARGUMENT, "entry %d: y overlaps its own x", bad);
+  const int nlev = 1 + *std::max_element(level.begin(), level.end());
+  for (StackGroup& G : S->groups) G.release();
+  S->groups.clear();
+  S->groups.resize(nlev);
+  for (int i = 0; i < count; ++i) S->groups[level[i]].idx.push_back(i);
+  for (StackGroup& G : S->groups) {
+    const int n = (int)G.idx.size();
+    for (int i : G.idx) {
+      G.lins.push_back(S->linears[i]);
+      G.pre.push_back(&S->linears[i]->pre);
+      G.view.udec.push_back(S->dimg.udec[i]);
+      G.view.hq.push_back(S->dimg.hq[i]);
+      G.view.vdec.push_back(S->dimg.vdec[i]);
+      G.xs_h.push_back(S->xs_h[i]);
+      G.ys_h.push_back(S->ys_h[i]);
+    }
+    HIP_TRY(hipMalloc(&G.xs_d, n * sizeof(void*)));
+    HIP_TRY(hipMalloc(&G.ys_d, n * sizeof(void*)));
+    HIP_TRY(hipMemcpy(G.xs_d, G.xs_h.data(), n * sizeof(void*), hipMemcpyHostToDevice));
+    HIP_TRY(hipMemcpy(G.ys_d, G.ys_h.data(), n * sizeof(void*), hipMemcpyHostToDevice));
+  }
+  return LB_OK;
+}
+
+// Prepares everything a launch sequence needs outside of any graph capture.
+lb_status stack_prepare(lb_stack S, lb_regime rg, int64_t tokens, lb_dtype io) {
+  if (rg == LB_REGIME_DECODE) {
+    lb_status s = stack_groups(S, tokens, io);
+    if (s != LB_OK) return s;
+    const int T = (int)std::min<int64_t>(tokens, kDecodeMaxTokens);
+    for (StackGroup& G : S->groups) {
+      s = build_decode_plan(G.plan, G.lins.data(), (int)G.lins.size(), T, &G.view);
+      if (s != LB_OK) return s;
+    }
+    // (a ragged last slice of a long decode uses another plan shape: those
+    // runs launch directly and rebuild the plan per slice)
   } else if (rg == LB_REGIME_PREFILL) {
     if (!prefill_available()) return fail(LB_ERR_UNSUPPORTED, "the prefill kernels are not available in this build");
-    HIP_TRY(prefill_prepare(S->pplan, S->pre.data(), count, (int)tokens, S->xs_h.data(), S->ys_h.data()));
+    lb_status s = stack_groups(S, tokens, io);
+    if (s != LB_OK) return s;
+    for (StackGroup& G : S->groups)
+      HIP_TRY(prefill_prepare(G.pplan, G.pre.data(), (int)G.lins.size(), (int)tokens, G.xs_h.data(), G.ys_h.data()));
   } else {
     size_t want = 0;
     for (lb_linear L : S->linears) {
@@ -717,9 +817,7 @@ lb_status lb_stack_forward_ex(lb_stack S, const void* const* xs, void* const* ys
     HIP_TRY(hipStreamSynchronize(st));
     S->xs_h.assign(xs, xs + count);
     S->ys_h.assign(ys, ys + count);
-    HIP_TRY(hipMemcpy(S->xs_d, S->xs_h.data(), count * sizeof(void*), hipMemcpyHostToDevice));
-    HIP_TRY(hipMemcpy(S->ys_d, S->ys_h.data(), count * sizeof(void*), hipMemcpyHostToDevice));
-    s = stack_prepare(S, rg, tokens);
+    s = stack_prepare(S, rg, tokens, io);
     if (s != LB_OK) return s;
     if (S->exec) HIP_TRY(hipGraphExecDestroy(S->exec));
     if (S->graph) HIP_TRY(hipGraphDestroy(S->graph));
@@ -762,10 +860,7 @@ lb_status lb_stack_destroy(lb_stack S) {
   if (S->exec) (void)hipGraphExecDestroy(S->exec);
   if (S->graph) (void)hipGraphDestroy(S->graph);
   if (S->cap_stream) (void)hipStreamDestroy(S->cap_stream);
-  if (S->xs_d) (void)hipFree(S->xs_d);
-  if (S->ys_d) (void)hipFree(S->ys_d);
-  S->plan.release();
-  prefill_plan_release(S->pplan);
+  for (StackGroup& G : S->groups) G.release();
   S->zexact.release();
   S->dimg.buf.release();
   delete S;

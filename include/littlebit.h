@@ -147,14 +147,19 @@ lb_status lb_linear_destroy(lb_linear L);
  * the same device. */
 lb_status lb_stack_create(const lb_linear* linears, int32_t count, lb_stack* out);
 
-/* Runs every linear i of the stack: ys[i] = xs[i] W_i^T, `tokens` rows each
- * (xs and ys are host arrays of `count` device pointers).  Entries are
- * independent: the library runs them concurrently, so no ys[i] may alias any
- * xs[j] or another ys[k].  The decode and prefill kernels (a few launches
- * per step) go directly onto `stream`; the exact fp32 kernels (two launches
- * per linear) are captured once into a HIP graph and replayed, re-captured
- * when the pointers, tokens, io or regime change.  Calls on one stack must be
- * ordered on one stream (they share the stack's scratch memory and graph). */
+/* Runs every linear i of the stack, in order: ys[i] = xs[i] W_i^T, `tokens`
+ * rows each (xs and ys are host arrays of `count` device pointers).  Entries
+ * may be chained through their buffers: when ys[i] overlaps xs[j] or ys[j] of
+ * a later entry j, or ys[j] overlaps xs[i], entry j runs after entry i (so a
+ * model's linears can be listed in their real order, each reading an earlier
+ * one's output).  The stack is split into levels of mutually independent
+ * entries; each level's entries run together (one launch per stage), levels
+ * one after another.  An entry's y must not overlap its own x
+ * (LB_ERR_INVALID_ARGUMENT).  The decode and prefill kernels go directly onto
+ * `stream`; the exact fp32 kernels (two launches per linear) are captured once
+ * into a HIP graph and replayed.  Plans and graphs are rebuilt when the
+ * pointers, tokens, io or regime change.  Calls on one stack must be ordered
+ * on one stream (they share the stack's scratch memory and graph). */
 lb_status lb_stack_forward(lb_stack S, const void* const* xs, void* const* ys, int64_t tokens,
                            lb_dtype io, void* stream);
 

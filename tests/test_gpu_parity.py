@@ -252,8 +252,11 @@ def test_stack_decode_graph_eager_single_agree(T):
         single = lins[i].forward(xd[i], regime=lb.REGIME_DECODE)
         torch.cuda.synchronize()
         assert torch.equal(ys_g[i].view(torch.int16), ys_e[i].view(torch.int16)), f"graph != eager, entry {i}"
-        assert torch.equal(ys_g[i].view(torch.int16), single.view(torch.int16)), f"stack != single, entry {i}"
-        assert_bf16_close(to_f64(ys_g[i]), oracle.forward(x_f64(xs[i]), paths[i], m, n), f"stack entry {i}")
+        # a single forward is a smaller launch, cut into smaller items: its
+        # partial sums are grouped differently, so it is held to the oracle
+        ref = oracle.forward(x_f64(xs[i]), paths[i], m, n)
+        assert_bf16_close(to_f64(ys_g[i]), ref, f"stack entry {i}")
+        assert_bf16_close(to_f64(single), ref, f"single entry {i}")
     # replay the captured graph several times with eager work in between
     ref = [y.clone() for y in ys_g]
     for rep in range(3):
@@ -265,6 +268,79 @@ def test_stack_decode_graph_eager_single_agree(T):
         del junk
         for i in range(len(ys_g)):
             assert torch.equal(ys_g[i].view(torch.int16), ref[i].view(torch.int16)), f"replay {rep} entry {i}"
+
+
+# A model's linears in their real order, chained through their buffers: per
+# layer q, k, v read the layer input; o reads q's output; gate and up read o's
+# output; down reads gate's output; the next layer's q, k, v read down's
+# output.  (m, n) per linear at model width D and MLP width F.
+CHAIN_D, CHAIN_F = 256, 704
+CHAIN_LAYER = [(CHAIN_D, CHAIN_D, [16, 12]), (CHAIN_D // 4, CHAIN_D, [9, 9]), (CHAIN_D // 4, CHAIN_D, [9, 9]),
+               (CHAIN_D, CHAIN_D, [16, 12]), (CHAIN_F, CHAIN_D, [33, 20]), (CHAIN_F, CHAIN_D, [33, 20]),
+               (CHAIN_D, CHAIN_F, [33, 20])]
+
+
+def chained_stack(key, layers, T, io):
+    shapes = CHAIN_LAYER * layers
+    lins, paths = [], []
+    for i, (m, n, ranks) in enumerate(shapes):
+        p = seeded_paths((key, i, 0), m, n, ranks)
+        paths.append(p)
+        lins.append(build(m, n, p))
+    dt = torch.bfloat16 if io == "bf16" else torch.float32
+    x0 = x_tensor(synth.activations((key, 99, T), T, CHAIN_D, io=io))
+    ys = [torch.empty((T, m), dtype=dt, device="cuda") for m, _, _ in shapes]
+    xs = []
+    for l in range(layers):
+        b = 7 * l
+        inp = x0 if l == 0 else ys[b - 1]
+        xs += [inp, inp, inp, ys[b], ys[b + 3], ys[b + 3], ys[b + 4]]
+    return shapes, lins, paths, xs, ys
+
+
+@pytest.mark.parametrize("regime,T,io", [(lb.REGIME_DECODE, 1, "bf16"), (lb.REGIME_DECODE, 16, "bf16"),
+                                         (lb.REGIME_DECODE, 40, "bf16"), (lb.REGIME_PREFILL, 200, "bf16"),
+                                         (lb.REGIME_EXACT, 3, "fp32")])
+def test_stack_chained_in_model_order(regime, T, io):
+    """Each entry sees its producer's finished output: every link matches the
+    oracle applied to the input the entry actually read, graph and direct
+    launches agree bit for bit, and single forwards run one after another
+    match the oracle link by link too (bit for bit with the stack where the
+    plan does not depend on the launch's size: prefill and exact)."""
+    log(f"chained stack regime={regime} T={T} io={io}")
+    layers = 2
+    shapes, lins, paths, xs, ys = chained_stack(31, layers, T, io)
+    S = lb.Stack(lins)
+    close = assert_bf16_close if io == "bf16" else assert_fp32_close
+    bits = torch.int16 if io == "bf16" else torch.int32
+    runs = []
+    for use_graph in (False, True):
+        for y in ys:
+            y.zero_()
+        S.forward(xs, ys, regime=regime, use_graph=use_graph)
+        torch.cuda.synchronize()
+        for i, (m, n, _) in enumerate(shapes):
+            close(to_f64(ys[i]), oracle.forward(to_f64(xs[i]), paths[i], m, n), f"chained entry {i} graph={use_graph}")
+        runs.append([y.clone() for y in ys])
+    for i in range(len(shapes)):
+        assert torch.equal(runs[0][i].view(bits), runs[1][i].view(bits)), f"graph != direct, entry {i}"
+    for y in ys:
+        y.zero_()
+    for i, (m, n, _) in enumerate(shapes):
+        lins[i].forward(xs[i], ys[i], regime=regime)
+        torch.cuda.synchronize()
+        close(to_f64(ys[i]), oracle.forward(to_f64(xs[i]), paths[i], m, n), f"single link {i}")
+        if regime != lb.REGIME_DECODE:
+            assert torch.equal(runs[0][i].view(bits), ys[i].view(bits)), f"stack != singles, entry {i}"
+
+
+def test_stack_refuses_output_over_own_input():
+    m = n = 256
+    p = seeded_paths((32, 0, 0), m, n, [16])
+    S = lb.Stack([build(m, n, p)])
+    x = x_tensor(synth.activations((32, 1, 4), 4, n, io="bf16"))
+    with pytest.raises(lb.LittleBitError, match="overlaps its own x"):
+        S.forward([x], [x], regime=lb.REGIME_DECODE)
 
 
 def test_stack_exact_fp32_matches_single():
