@@ -567,22 +567,42 @@ __global__ void __launch_bounds__(kThreads) k_decode_mid(DecArgs a) {
     const int t = u / nblk, blk = u % nblk, tb = t / 8, tt = t % 8;
     const int jj = 32 * blk + 2 * sub;             // latents jj, jj + 1
     const ConvLane LK(((jj % kChunk) / 32) * 16 + sub);
-    float v[2];
+    // the partial sums of both latents over the splits, added in split order;
+    // the loads of up to kB splits go out together
+    constexpr int kB = 8;
+    const LB_GLOBAL float* sp[2];
+    int off[2];
+    bool in[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      const int j = jj + q;
-      v[q] = 0.f;
-      if (j < r) {
-        const int tile = j / 16, col = j % 16, g = tile / it.gtiles, tl = tile - g * it.gtiles;
-        const LB_GLOBAL float* sp = part + (int64_t)(it.slot0 + g * it.nsplit) * SF;
-        float d = 0.f, c = 0.f;
-        for (int s = 0; s < it.nsplit; ++s) {
-          d += sp[(int64_t)s * SF + (tl * TM + t) * 16 + col];
-          c += sp[(int64_t)s * SF + CT * TM * 16 + t];
-        }
-        v[q] = (d + c) * f16f(lsc[j]) * LK.fcls;
-      }
+      const int j = jj + q, tile = j / 16, col = j % 16, g = tile / it.gtiles, tl = tile - g * it.gtiles;
+      in[q] = j < r;
+      sp[q] = part + (int64_t)(it.slot0 + g * it.nsplit) * SF;
+      off[q] = (tl * TM + t) * 16 + col;
     }
+    float d[2] = {0.f, 0.f}, c[2] = {0.f, 0.f};
+    for (int s0 = 0; s0 < it.nsplit; s0 += kB) {
+      float dv[2][kB], cv[2][kB];
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int i = 0; i < kB; ++i)
+          if (in[q] && s0 + i < it.nsplit) {
+            dv[q][i] = sp[q][(int64_t)(s0 + i) * SF + off[q]];
+            cv[q][i] = sp[q][(int64_t)(s0 + i) * SF + CT * TM * 16 + t];
+          }
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int i = 0; i < kB; ++i)
+          if (in[q] && s0 + i < it.nsplit) {
+            d[q] += dv[q][i];
+            c[q] += cv[q][i];
+          }
+    }
+    float v[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) v[q] = in[q] ? (d[q] + c[q]) * f16f(lsc[jj + q]) * LK.fcls : 0.f;
     uint8_t* ab = E.aimg + ((int64_t)(ufirst + jj / kChunk) * TB + tb) * kABytes;
     const float cc = row16_sum(convert_pair(LK, v[0], v[1], tt, gp(ab)));
     if (sub == 0) cblk[u] = cc;
@@ -606,7 +626,7 @@ struct UShape {
   static constexpr int TB = (TM + 7) / 8;
   static constexpr int KQQ = TM == 1 ? 1 : 2;          // token slots per lane and block
   static constexpr int KST = TM > 8 ? 2 : 1;           // output stores per quad (8 tokens x 64 rows each)
-  static constexpr int NMAX = TB == 1 ? 8 : 4;         // most units with operands held in registers
+  static constexpr int NMAX = TB == 1 ? 8 : 6;         // most units with operands held in registers
   static constexpr int QW = decode_u_qw_max(TM);       // most quads per wave
   static constexpr int STG = QW * TM * 128;            // staging bytes per wave
   static constexpr size_t lds = (size_t)kWaves * (kRingBytes + STG);
