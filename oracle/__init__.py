@@ -16,3 +16,4 @@ from .littlebit_oracle import (  # noqa: F401
     unpack_signs,
     words_per_row,
 )
+from . import dual_svid  # noqa: F401

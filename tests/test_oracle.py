@@ -347,3 +347,92 @@ def test_forward_rows_is_the_same_definition():
     x = oracle.decode_bf16(bf16bits(rng.choice(DYADIC, size=(3, n))))
     rows = [0, 7, 40, 13]
     assert np.array_equal(oracle.forward_rows(x, paths, m, n, rows), oracle.forward(x, paths, m, n)[:, rows])
+
+
+# ----------------------------------------------------------------------------
+# Dual-SVID initialisation (oracle.dual_svid)
+# ----------------------------------------------------------------------------
+
+def _hadamard_weight(m, n, sigmas):
+    """W = Hm[:, :r] diag(s) Hn[:, :r]^T with orthonormal Hadamard columns:
+    its truncated SVD factors have entries of one magnitude per column, so
+    |U'| and |V'| are exactly rank 1."""
+    from scipy.linalg import hadamard
+    r = len(sigmas)
+    Hm = hadamard(m)[:, :r] / np.sqrt(m)
+    Hn = hadamard(n)[:, :r] / np.sqrt(n)
+    return Hm @ np.diag(sigmas) @ Hn.T
+
+
+def test_dual_svid_exact_when_magnitudes_are_rank_one():
+    # pinned by construction: Dual-SVID then reproduces the truncated SVD exactly
+    D = oracle.dual_svid
+    W = _hadamard_weight(64, 32, [9.0, 5.0, 3.0, 2.0, 1.5])
+    f = D.dual_svid(W, 5)
+    assert np.abs(D.path_weight(f) - W).max() <= 1e-12 * np.abs(W).max()
+    # a lower rank gives the rank-r truncation (Eckart-Young), still exactly
+    f3 = D.dual_svid(W, 3)
+    W3 = _hadamard_weight(64, 32, [9.0, 5.0, 3.0])
+    assert np.abs(D.path_weight(f3) - W3).max() <= 1e-12 * np.abs(W).max()
+
+
+def test_truncated_factors_are_the_best_rank_r_approximation():
+    # Eckart-Young: the squared Frobenius error is the sum of the dropped squared singular values
+    rng = np.random.default_rng(21)
+    W = rng.standard_normal((30, 20))
+    s = np.linalg.svd(W, compute_uv=False)
+    for r in (1, 4, 19):
+        Up, Vp = oracle.dual_svid.truncated_factors(W, r)
+        err = np.linalg.norm(W - Up @ Vp.T) ** 2
+        assert abs(err - np.sum(s[r:] ** 2)) <= 1e-9 * np.sum(s ** 2)
+        # the even split: both factors carry the same column norms (sqrt of sigma)
+        assert np.allclose(np.linalg.norm(Up, axis=0), np.sqrt(s[:r]))
+        assert np.allclose(np.linalg.norm(Vp, axis=0), np.sqrt(s[:r]))
+
+
+def test_rank1_matches_power_iteration():
+    # an independent algorithm: power iteration on M^T M for the top singular pair
+    rng = np.random.default_rng(22)
+    M = np.abs(rng.standard_normal((40, 12))) + 0.1
+    a, b = oracle.dual_svid.rank1(M)
+    v = np.ones(M.shape[1])
+    for _ in range(500):
+        v = M.T @ (M @ v)
+        v /= np.linalg.norm(v)
+    u = M @ v
+    sigma = np.linalg.norm(u)
+    u /= sigma
+    assert np.allclose(np.outer(a, b), sigma * np.outer(u, v), rtol=0, atol=1e-10 * sigma)
+    assert a.sum() >= 0 and b.sum() >= 0
+    # an exactly rank-1 nonnegative matrix is reproduced
+    p, q = rng.uniform(0.5, 2, 40), rng.uniform(0.5, 2, 12)
+    a, b = oracle.dual_svid.rank1(np.outer(p, q))
+    assert np.allclose(np.outer(a, b), np.outer(p, q), rtol=1e-12)
+
+
+def test_dual_svid_sign_of_zero_and_stored_form():
+    D = oracle.dual_svid
+    rng = np.random.default_rng(23)
+    W = rng.standard_normal((16, 40))
+    W[5, :] = 0.0                          # a zero row of W gets a zero row scale
+    f = D.dual_svid(W, 6)
+    assert abs(f["h"][5]) <= 1e-12 * np.abs(f["h"]).max()
+    assert list(D.sign_pm1(np.array([0.0, -0.0, 1e-300, -1e-300, -2.0]))) == [1, 1, 1, -1, -1]
+    assert set(np.unique(f["U"])) <= {-1, 1} and set(np.unique(f["V"])) <= {-1, 1}
+    p = D.stored_path(f)
+    back = oracle.decode_path(p, 16, 40)
+    assert np.array_equal(back["U"], f["U"].astype(np.float64))
+    assert np.array_equal(back["V"], f["V"].astype(np.float64))
+    for k in ("h", "g", "l"):
+        assert np.array_equal(back[k], f[k].astype(np.float16).astype(np.float64))
+
+
+def test_residual_path_reduces_the_error():
+    # the pages report the two-path initial approximation beating one path; on
+    # a random matrix the residual path must at least lower the error
+    rng = np.random.default_rng(24)
+    W = rng.standard_normal((96, 64))
+    paths = oracle.dual_svid.init_paths(W, [12, 12])
+    e1 = np.linalg.norm(W - oracle.reconstruct_w(paths[:1], 96, 64))
+    e2 = np.linalg.norm(W - oracle.reconstruct_w(paths, 96, 64))
+    assert e2 < e1 < np.linalg.norm(W)
