@@ -17,6 +17,7 @@ from ._binding import (  # noqa: F401
     LittleBitError,
     Stack,
     lib,
+    init_dual_svid,
     pack_signs,
     pack_signs_host,
     packed_words_per_row,

@@ -30,11 +30,16 @@ EXPORTS = [
     "lb_packed_words_per_row", "lb_rank_for_bpw", "lb_pack_signs_host", "lb_pack_signs", "lb_unpack_signs",
     "lb_linear_create", "lb_linear_forward", "lb_linear_forward_ex", "lb_linear_info", "lb_linear_destroy",
     "lb_stack_create", "lb_stack_forward", "lb_stack_forward_ex", "lb_stack_destroy", "lb_status_string",
-    "lb_last_error", "lb_probe_stream_read",
+    "lb_last_error", "lb_probe_stream_read", "lb_init_dual_svid",
 ]
 
 
 class LbPath(C.Structure):
+    _fields_ = [("rank", C.c_int64), ("u_packed", C.c_void_p), ("v_packed", C.c_void_p),
+                ("h", C.c_void_p), ("g", C.c_void_p), ("l", C.c_void_p)]
+
+
+class LbPathInit(C.Structure):
     _fields_ = [("rank", C.c_int64), ("u_packed", C.c_void_p), ("v_packed", C.c_void_p),
                 ("h", C.c_void_p), ("g", C.c_void_p), ("l", C.c_void_p)]
 
@@ -76,6 +81,7 @@ def lib():
         "lb_status_string": (C.c_char_p, [C.c_int]),
         "lb_last_error": (C.c_char_p, []),
         "lb_probe_stream_read": (C.c_int, [vp, i64, vp]),
+        "lb_init_dual_svid": (C.c_int, [vp, i64, i64, vp, i32, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -130,6 +136,30 @@ def unpack_signs(packed, rank: int, stream=None):
     out = torch.empty((rows, rank), dtype=torch.int8, device=packed.device)
     _check(lib().lb_unpack_signs(packed.data_ptr(), rows, rank, out.data_ptr(), _stream(stream)))
     return out
+
+
+def init_dual_svid(W, ranks: Sequence[int], stream=None) -> List[Dict]:
+    """Dual-SVID initialisation of a layer from a dense fp32 device tensor W
+    [d_out, d_in] (lb_init_dual_svid): one dict per path of device tensors u
+    (int32 [d_out, words]), v (int32 [d_in, words]), h, g, l (int16 fp16 bits),
+    ready for Linear(d_out, d_in, paths)."""
+    import torch
+    if W.dim() != 2 or W.dtype != torch.float32 or not W.is_contiguous():
+        raise ValueError("W must be a contiguous float32 [d_out, d_in] tensor")
+    m, n = W.shape
+    paths, outs = [], []
+    for r in ranks:
+        w = packed_words_per_row(r)
+        p = dict(rank=int(r), u=torch.empty((m, w), dtype=torch.int32, device=W.device),
+                 v=torch.empty((n, w), dtype=torch.int32, device=W.device),
+                 h=torch.empty(m, dtype=torch.int16, device=W.device), g=torch.empty(n, dtype=torch.int16, device=W.device),
+                 l=torch.empty(int(r), dtype=torch.int16, device=W.device))
+        paths.append(p)
+        outs.append(LbPathInit(int(r), p["u"].data_ptr(), p["v"].data_ptr(), p["h"].data_ptr(), p["g"].data_ptr(),
+                               p["l"].data_ptr()))
+    arr = (LbPathInit * len(outs))(*outs)
+    _check(lib().lb_init_dual_svid(C.c_void_p(W.data_ptr()), m, n, arr, len(outs), _stream(stream)))
+    return paths
 
 
 def probe_stream_read(buf, stream=None) -> None:

@@ -435,6 +435,33 @@ lb_status lb_pack_signs(const int8_t* signs, int64_t rows, int64_t rank, uint32_
   return LB_OK;
 }
 
+lb_status lb_init_dual_svid(const float* W, int64_t d_out, int64_t d_in, const lb_path_init* paths, int32_t n_paths,
+                            void* stream) {
+  if (!W || !paths) return fail(LB_ERR_INVALID_ARGUMENT, "null pointer");
+  if (n_paths != 1 && n_paths != 2) return fail(LB_ERR_INVALID_ARGUMENT, "n_paths must be 1 or 2 (got %d)", n_paths);
+  if (d_out <= 0 || d_in <= 0) return fail(LB_ERR_INVALID_ARGUMENT, "d_out and d_in must be positive");
+  if (d_out > LB_MAX_DIM || d_in > LB_MAX_DIM) return fail(LB_ERR_UNSUPPORTED, "dimension exceeds %d", LB_MAX_DIM);
+  int64_t ranks[2] = {0, 0};
+  InitPathOut out[2] = {};
+  for (int p = 0; p < n_paths; ++p) {
+    const lb_path_init& P = paths[p];
+    if (P.rank < 1 || P.rank > std::min<int64_t>(std::min(d_out, d_in), LB_MAX_RANK))
+      return fail(LB_ERR_INVALID_ARGUMENT, "path %d: rank must be in 1..min(d_out, d_in, %d)", p, LB_MAX_RANK);
+    if (!P.u_packed || !P.v_packed || !P.h || !P.g || !P.l)
+      return fail(LB_ERR_INVALID_ARGUMENT, "path %d: null output pointer", p);
+    ranks[p] = P.rank;
+    out[p] = InitPathOut{P.u_packed, P.v_packed, P.h, P.g, P.l};
+  }
+  int rocstatus = 0;
+  const hipError_t e = dual_svid_init(W, d_out, d_in, ranks, n_paths, out, reinterpret_cast<hipStream_t>(stream),
+                                      &rocstatus);
+  if (e != hipSuccess) {
+    if (rocstatus) return fail(LB_ERR_HIP, "lb_init_dual_svid: rocBLAS/rocSOLVER status %d", rocstatus);
+    return hip_fail(e, "lb_init_dual_svid");
+  }
+  return LB_OK;
+}
+
 lb_status lb_probe_stream_read(const void* buf, int64_t bytes, void* stream) {
   if (!buf) return fail(LB_ERR_INVALID_ARGUMENT, "null buffer");
   if (bytes <= 0 || bytes % 16) return fail(LB_ERR_INVALID_ARGUMENT, "bytes must be a positive multiple of 16");

@@ -157,6 +157,19 @@ hipError_t launch_decode_u(const DecArgs& a, int nitems, hipStream_t st);
 // layouts of the decode U stage (built once per linear)
 hipError_t launch_decode_u_layout(const uint32_t* ucan0, const uint32_t* ucan1, int m, const int* W, const UGeom& g,
                                   uint8_t* udec, hipStream_t st);
+// Dual-SVID initialisation: per path, caller-owned device outputs in the
+// interchange form of lb_linear_create's inputs
+struct InitPathOut {
+  uint32_t* u_packed;
+  uint32_t* v_packed;
+  uint16_t* h;
+  uint16_t* g;
+  uint16_t* l;
+};
+// W row-major [m][n] fp32 on the device; synchronous on st.  rocstatus: the
+// rocBLAS / rocSOLVER status when one of their calls failed, else 0.
+hipError_t dual_svid_init(const float* W, int64_t m, int64_t n, const int64_t* ranks, int np, const InitPathOut* out,
+                          hipStream_t st, int* rocstatus);
 // calibration: one read-only streaming pass over a device buffer
 hipError_t launch_probe_stream_read(const void* buf, int64_t bytes, hipStream_t st);
 hipError_t launch_decode_h_layout(const uint16_t* h0, const uint16_t* h1, int m, int nq, uint16_t* hq,

@@ -178,6 +178,34 @@ const char* lb_status_string(lb_status s);
 /* Thread-local description of this thread's last failure ("" if none). */
 const char* lb_last_error(void);
 
+/* One path's outputs of lb_init_dual_svid: caller-owned device buffers in the
+ * form lb_linear_create reads (lb_path). */
+typedef struct {
+  int64_t   rank;          /* r_p, 1 <= r_p <= min(d_out, d_in, LB_MAX_RANK)        */
+  uint32_t* u_packed;      /* device, [d_out][ceil(r/32)] words, canonical packing  */
+  uint32_t* v_packed;      /* device, [d_in ][ceil(r/32)] words                     */
+  uint16_t* h;             /* device, fp16 bits, [d_out]                            */
+  uint16_t* g;             /* device, fp16 bits, [d_in]                             */
+  uint16_t* l;             /* device, fp16 bits, [rank]                             */
+} lb_path_init;
+
+/* Dual-SVID initialisation ("LittleBit: Ultra Low-Bit Quantization via Latent
+ * Factorization", paper notes, sections "Key design / Dual-SVID
+ * initialisation" and "Residual compensation") of an n_paths-path layer from a
+ * dense weight W (device, fp32, row-major [d_out][d_in]).  Path p starts from
+ * what the earlier stored paths leave of W: a truncated rank-r_p SVD gives
+ * U', V' (singular values split evenly); U_sign = sign(U'), V_sign = sign(V')
+ * (sign(0) = +1); the top singular pair of |U'| gives h and one latent factor,
+ * that of |V'| gives g and the other, and l is their product.  Scales are
+ * rounded to fp16 (nearest even), and the next path starts from W minus the
+ * paths as stored.  fp64 arithmetic (rocSOLVER's partial SVD, rocBLAS);
+ * allocates working memory of about 2 d_out d_in doubles; returns after the
+ * work on `stream` has completed.  Errors: null pointers, n_paths not 1 or 2,
+ * or a rank outside 1..min(d_out, d_in, LB_MAX_RANK) -> LB_ERR_INVALID_ARGUMENT;
+ * solver or HIP failures -> LB_ERR_HIP (outputs then undefined). */
+lb_status lb_init_dual_svid(const float* W, int64_t d_out, int64_t d_in, const lb_path_init* paths,
+                            int32_t n_paths, void* stream);
+
 /* Measurement aid, not part of the method: enqueues on `stream` one
  * read-only streaming pass over `bytes` bytes of device memory at `buf`
  * (16-byte loads, grid-stride), so that a caller timing it with events gets

@@ -113,6 +113,14 @@ def test_argument_validation_before_any_device_work():
     assert L.lb_probe_stream_read(None, 16, None) == lb._binding.INVALID_ARGUMENT
     assert L.lb_probe_stream_read(dummy, 0, None) == lb._binding.INVALID_ARGUMENT
     assert L.lb_probe_stream_read(dummy, 24, None) == lb._binding.INVALID_ARGUMENT
+    outs = (lb._binding.LbPathInit * 1)(lb._binding.LbPathInit(4, dummy, dummy, dummy, dummy, dummy))
+    assert L.lb_init_dual_svid(None, 8, 8, outs, 1, None) == lb._binding.INVALID_ARGUMENT
+    assert L.lb_init_dual_svid(dummy, 8, 8, None, 1, None) == lb._binding.INVALID_ARGUMENT
+    assert L.lb_init_dual_svid(dummy, 8, 8, outs, 3, None) == lb._binding.INVALID_ARGUMENT
+    bad = (lb._binding.LbPathInit * 1)(lb._binding.LbPathInit(9, dummy, dummy, dummy, dummy, dummy))
+    assert L.lb_init_dual_svid(dummy, 8, 8, bad, 1, None) == lb._binding.INVALID_ARGUMENT   # rank > min(m, n)
+    nul = (lb._binding.LbPathInit * 1)(lb._binding.LbPathInit(4, dummy, None, dummy, dummy, dummy))
+    assert L.lb_init_dual_svid(dummy, 8, 8, nul, 1, None) == lb._binding.INVALID_ARGUMENT
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
