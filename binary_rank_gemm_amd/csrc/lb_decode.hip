@@ -450,7 +450,7 @@ __device__ __attribute__((always_inline)) inline void v_plain(const DecArgs& a, 
 }
 
 template <int TM>
-__global__ void __launch_bounds__(kThreads, 3) k_decode_v(DecArgs a) {
+__global__ void __launch_bounds__(kThreads, TM >= 16 ? 2 : 3) k_decode_v(DecArgs a) {
   using S = VShape<TM>;
   constexpr int TB = S::TB, CT = S::CT;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];

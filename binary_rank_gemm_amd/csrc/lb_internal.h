@@ -125,9 +125,11 @@ constexpr int kDecodeMaxTokens = 16;
 __host__ __device__ inline constexpr int decode_bucket(int T) {
   return T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : T <= 8 ? 8 : 16;
 }
-// Column tiles of one V item, and the floats of one partial slot:
-// [tile][token][16 columns] sums, then 16 correction sums.
-__host__ __device__ inline constexpr int decode_v_tiles(int bucket) { return bucket >= 16 ? 12 : 20; }
+// Column tiles of one V item (20 at every bucket: at 16 tokens the V
+// workgroups then hold more registers and two fit a CU, but a 205-rank path
+// stays one column group, so x is read once per path), and the floats of one
+// partial slot: [tile][token][16 columns] sums, then 16 correction sums.
+__host__ __device__ inline constexpr int decode_v_tiles(int bucket) { return 20; }
 __host__ __device__ inline constexpr int decode_slot_floats(int bucket) {
   return decode_v_tiles(bucket) * 16 * bucket + 16;
 }
