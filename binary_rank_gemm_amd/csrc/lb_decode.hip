@@ -156,6 +156,9 @@ struct ConvLane {
   }
 };
 
+typedef short short2v __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
+
 // Converts this lane's two values (already multiplied by the class factor) of
 // token slot tt into the A image `ab` at the lane's K position; the 16 lanes of
 // a DPP row hold one 32-element block.  Returns the lane's contribution to C.
@@ -165,12 +168,15 @@ __device__ inline float convert_pair(const ConvLane& L, float t0, float t1, int 
   int ex;
   frexpf(mx, &ex);
   int E = ex - 8;                       // max / 2^E in [128, 256)
-  E = E < -123 ? -123 : (E > 127 ? 127 : E);
-  float u0 = ldexpf(t0, -E), u1 = ldexpf(t1, -E);
-  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(u0, u1, 0, false);
-  float h0 = __builtin_amdgcn_cvt_f32_fp8(hi, 0), h1 = __builtin_amdgcn_cvt_f32_fp8(hi, 1);
-  int lo = __builtin_amdgcn_cvt_pk_fp8_f32((u0 - h0) * 16.f, (u1 - h1) * 16.f, 0, false);
-  float l0 = __builtin_amdgcn_cvt_f32_fp8(lo, 0), l1 = __builtin_amdgcn_cvt_f32_fp8(lo, 1);
+  E = E < -122 ? -122 : (E > 127 ? 127 : E);
+  // the scaled conversions divide by their scale going to fp8 and multiply by
+  // it coming back (powers of two: exact), so H = hi 2^E, L = lo 2^(E - 4)
+  const float sc = __builtin_bit_cast(float, (E + 127) << 23), sl = __builtin_bit_cast(float, (E + 123) << 23);
+  const short2v zero2 = {0, 0};
+  const int hi = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(zero2, t0, t1, sc, false)) & 0xffff;
+  const float2v H = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi, sc, false);
+  const int lo = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(zero2, t0 - H[0], t1 - H[1], sl, false)) & 0xffff;
+  const float2v Lq = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(lo, sl, false);
   const int mhi = 2 * tt, mlo = 2 * tt + 1;
   using U16 = typename std::conditional<std::is_same<Ptr, uint8_t*>::value, uint16_t, LB_GLOBAL uint16_t>::type;
   *reinterpret_cast<U16*>(ab + img_off(mhi, L.gdst, L.edst)) = (uint16_t)hi;
@@ -180,7 +186,7 @@ __device__ inline float convert_pair(const ConvLane& L, float t0, float t1, int 
     ab[2048 + mlo * 4 + L.kb] = (uint8_t)(E + 127 - 4);
   }
   // quantised value of t (A / class factor), summed over the three {0, beta} classes
-  return ldexpf((h0 + h1) + (l0 + l1) * 0.0625f, E) * L.finv;
+  return ((H[0] + H[1]) + (Lq[0] + Lq[1])) * L.finv;
 }
 
 // Reads lane (mr, gr)'s A operand and scale from an A image (LDS or global).
