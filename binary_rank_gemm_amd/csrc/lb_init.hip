@@ -112,13 +112,16 @@ double f16_to_f64(uint16_t h) {
   return (h & 0x8000) ? -v : v;
 }
 
-struct Dev {
-  double* p = nullptr;
-  ~Dev() {
+template <class T>
+struct DevT {
+  T* p = nullptr;
+  ~DevT() {
     if (p) (void)hipFree(p);
   }
-  hipError_t alloc(size_t count) { return hipMalloc(&p, std::max<size_t>(count, 1) * sizeof(double)); }
+  hipError_t alloc(size_t count) { return hipMalloc(&p, std::max<size_t>(count, 1) * sizeof(T)); }
 };
+using Dev = DevT<double>;
+using DevI = DevT<rocblas_int>;
 
 #define LB_ROC(expr)                                                   \
   do {                                                                 \
@@ -138,29 +141,26 @@ struct Dev {
 // b (cols), sigma; signs chosen so that sum(a) + sum(b) >= 0
 hipError_t rank1(rocblas_handle H, double* X, int64_t rows, int cols, std::vector<double>& a, std::vector<double>& b,
                  double& sigma, rocblas_status& status, hipStream_t st) {
-  Dev S, U, Vt, E;
+  Dev S, U, Vt;
+  DevI nsv, info, ifail;
   LB_HIPR(S.alloc(std::min<int64_t>(rows, cols)));
   LB_HIPR(U.alloc(rows));
   LB_HIPR(Vt.alloc(cols));
-  rocblas_int *nsv = nullptr, *ifail = nullptr, *info = nullptr;
-  LB_HIPR(hipMalloc(&nsv, sizeof(rocblas_int)));
-  LB_HIPR(hipMalloc(&info, sizeof(rocblas_int)));
-  LB_HIPR(hipMalloc(&ifail, std::max<int64_t>(std::min<int64_t>(rows, cols), 1) * sizeof(rocblas_int)));
+  LB_HIPR(nsv.alloc(1));
+  LB_HIPR(info.alloc(1));
+  LB_HIPR(ifail.alloc(std::min<int64_t>(rows, cols)));
   const rocblas_status rs = rocsolver_dgesvdx(H, rocblas_svect_singular, rocblas_svect_singular, rocblas_srange_index,
-                                              (rocblas_int)rows, cols, X, (rocblas_int)rows, 0.0, 0.0, 1, 1, nsv, S.p, U.p,
-                                              (rocblas_int)rows, Vt.p, 1, ifail, info);
+                                              (rocblas_int)rows, cols, X, (rocblas_int)rows, 0.0, 0.0, 1, 1, nsv.p, S.p,
+                                              U.p, (rocblas_int)rows, Vt.p, 1, ifail.p, info.p);
   rocblas_int inf = 0;
   hipError_t e = hipSuccess;
-  if (rs == rocblas_status_success) e = hipMemcpyAsync(&inf, info, sizeof(inf), hipMemcpyDeviceToHost, st);
+  if (rs == rocblas_status_success) e = hipMemcpyAsync(&inf, info.p, sizeof(inf), hipMemcpyDeviceToHost, st);
   a.resize(rows);
   b.resize(cols);
   if (rs == rocblas_status_success && e == hipSuccess) e = hipMemcpyAsync(&sigma, S.p, sizeof(double), hipMemcpyDeviceToHost, st);
   if (rs == rocblas_status_success && e == hipSuccess) e = hipMemcpyAsync(a.data(), U.p, rows * sizeof(double), hipMemcpyDeviceToHost, st);
   if (rs == rocblas_status_success && e == hipSuccess) e = hipMemcpyAsync(b.data(), Vt.p, cols * sizeof(double), hipMemcpyDeviceToHost, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
-  (void)hipFree(nsv);
-  (void)hipFree(info);
-  (void)hipFree(ifail);
   if (rs != rocblas_status_success) {
     status = rs;
     return hipErrorUnknown;
@@ -209,21 +209,18 @@ hipError_t dual_svid_init(const float* W, int64_t m, int64_t n, const int64_t* r
       LB_HIPR(Vp.alloc(n * r));
       LB_HIPR(T1.alloc(m * r));
       LB_HIPR(T2.alloc(n * r));
-      rocblas_int *nsv = nullptr, *ifail = nullptr, *info = nullptr;
-      LB_HIPR(hipMalloc(&nsv, sizeof(rocblas_int)));
-      LB_HIPR(hipMalloc(&info, sizeof(rocblas_int)));
-      LB_HIPR(hipMalloc(&ifail, std::min(m, n) * sizeof(rocblas_int)));
+      DevI nsv, info, ifail;
+      LB_HIPR(nsv.alloc(1));
+      LB_HIPR(info.alloc(1));
+      LB_HIPR(ifail.alloc(std::min(m, n)));
       const rocblas_status rs =
           rocsolver_dgesvdx(H, rocblas_svect_singular, rocblas_svect_singular, rocblas_srange_index, (rocblas_int)m,
-                            (rocblas_int)n, R.p, (rocblas_int)m, 0.0, 0.0, 1, r, nsv, S.p, U.p, (rocblas_int)m, Vt.p, r,
-                            ifail, info);
+                            (rocblas_int)n, R.p, (rocblas_int)m, 0.0, 0.0, 1, r, nsv.p, S.p, U.p, (rocblas_int)m, Vt.p, r,
+                            ifail.p, info.p);
       rocblas_int inf = 0;
-      hipError_t e = rs == rocblas_status_success ? hipMemcpyAsync(&inf, info, sizeof(inf), hipMemcpyDeviceToHost, st)
+      hipError_t e = rs == rocblas_status_success ? hipMemcpyAsync(&inf, info.p, sizeof(inf), hipMemcpyDeviceToHost, st)
                                                   : hipSuccess;
       if (e == hipSuccess) e = hipStreamSynchronize(st);
-      (void)hipFree(nsv);
-      (void)hipFree(info);
-      (void)hipFree(ifail);
       if (rs != rocblas_status_success) {
         status = rs;
         return hipErrorUnknown;
