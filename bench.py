@@ -36,13 +36,13 @@ METRIC = "decode µs/token + HBM GB/s on layer stack; prefill TFLOP/s vs MFMA pe
 
 WORKLOADS = {
     # name: (synth workload, tokens, regime)
-    "cfg5-decode": ("llama2-70b-0.1bpw", 1, "decode"),
-    "cfg5-decode8": ("llama2-70b-0.1bpw", 8, "decode"),
-    "cfg5-decode64": ("llama2-70b-0.1bpw", 64, "decode"),
-    "cfg2-decode": ("llama2-7b-0.1bpw", 1, "decode"),
-    "cfg4-decode": ("llama3-8b-0.3bpw", 16, "decode"),
-    "cfg3-prefill": ("llama2-13b-0.55bpw", 2048, "prefill"),
-    "cfg4-prefill": ("llama3-8b-0.3bpw", 2048, "prefill"),
+    "llama2-70b-decode-t1": ("llama2-70b-0.1bpw", 1, "decode"),
+    "llama2-70b-decode-t8": ("llama2-70b-0.1bpw", 8, "decode"),
+    "llama2-70b-decode-t64": ("llama2-70b-0.1bpw", 64, "decode"),
+    "llama2-7b-decode-t1": ("llama2-7b-0.1bpw", 1, "decode"),
+    "llama3-8b-decode-t16": ("llama3-8b-0.3bpw", 16, "decode"),
+    "llama2-13b-prefill-t2048": ("llama2-13b-0.55bpw", 2048, "prefill"),
+    "llama3-8b-prefill-t2048": ("llama3-8b-0.3bpw", 2048, "prefill"),
 }
 
 
@@ -404,7 +404,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     # the GPU's clocks take some tens of milliseconds of load to settle
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", default="cfg5-decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="llama2-70b-decode-t1", choices=sorted(WORKLOADS))
     ap.add_argument("--layers", type=int, default=None, help="limit the stack to this many layers (not for reports)")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-only", action="store_true", help="time only the prefill stack (for profiling)")
@@ -436,7 +436,7 @@ def main():
         log(f"copy probe: {nb} bytes read + {nb} bytes written")
 
     if args.prefill_only:
-        p = run_prefill(args, lb, torch, "cfg3-prefill")
+        p = run_prefill(args, lb, torch, "llama2-13b-prefill-t2048")
         log(f"prefill: {p['ms_per_step']:.2f} ms/step, {p['tflops']:.0f} TFLOP/s")
         print(json.dumps({"prefill": p}), flush=True)
         return
@@ -481,7 +481,7 @@ def main():
             log(f"chained decode: {out['chained_decode']}")
     if not args.no_prefill and args.layers is None:
         try:
-            p = run_prefill(args, lb, torch, "cfg3-prefill")
+            p = run_prefill(args, lb, torch, "llama2-13b-prefill-t2048")
             out["prefill"] = p
             log(f"prefill: {p['ms_per_step']:.2f} ms/step, {p['tflops']:.0f} TFLOP/s")
         except lb.LittleBitError as e:
@@ -495,7 +495,7 @@ def main():
         if "prefill" in out and "tflops" in out["prefill"]:
             ctx["prefill_frac_of_bf16_gemm"] = round(out["prefill"]["tflops"] / ctx["bf16_gemm_8192_tflops"], 4)
         out["achievable_peaks"] = ctx
-        wl_pre_name, T_pre, _ = WORKLOADS["cfg3-prefill"]
+        wl_pre_name, T_pre, _ = WORKLOADS["llama2-13b-prefill-t2048"]
         wl_pre = synth.WORKLOADS[wl_pre_name]
         cmp_ = dense_comparators(torch, wl, r["ranks_of"], wl_pre, [ranks_for(wl_pre, s, lb) for s in wl_pre.mats], T_pre)
         cmp_["speedup_vs_dense_bf16_decode"] = round(cmp_["dense_bf16_decode_us_per_token"] / us_per_token, 1)

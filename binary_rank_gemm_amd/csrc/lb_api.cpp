@@ -632,6 +632,8 @@ lb_status lb_linear_destroy(lb_linear L) {
   return LB_OK;
 }
 
+}  // extern "C"
+
 namespace {
 
 // Copies the decode layouts of the stack's linears into one allocation (see
@@ -675,6 +677,8 @@ hipError_t build_decode_image(DecodeImage& D, const std::vector<lb_linear>& lins
 
 }  // namespace
 
+extern "C" {
+
 lb_status lb_stack_create(const lb_linear* linears, int32_t count, lb_stack* out) {
   if (!out || !linears) return fail(LB_ERR_INVALID_ARGUMENT, "null pointer");
   if (count <= 0) return fail(LB_ERR_INVALID_ARGUMENT, "count must be positive");
@@ -696,6 +700,8 @@ lb_status lb_stack_create(const lb_linear* linears, int32_t count, lb_stack* out
   *out = S;
   return LB_OK;
 }
+
+}  // extern "C"
 
 namespace {
 
@@ -821,6 +827,8 @@ lb_status stack_prepare(lb_stack S, lb_regime rg, int64_t tokens, lb_dtype io) {
 }
 
 }  // namespace
+
+extern "C" {
 
 lb_status lb_stack_forward_ex(lb_stack S, const void* const* xs, void* const* ys, int64_t tokens, lb_dtype io,
                               lb_regime regime, int32_t use_graph, void* stream) {
