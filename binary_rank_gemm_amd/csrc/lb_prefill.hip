@@ -179,7 +179,16 @@ using Int = std::integral_constant<int, N>;
 constexpr int kPreBufs = 4;                              // LDS buffers of the K-block pipeline
 
 typedef __attribute__((address_space(3))) void lds_void;
-typedef const __attribute__((address_space(1))) void gbl_void;
+
+// Buffer resource over plain byte offsets (no range check in practice: the
+// record count is the largest allowed).  The loads into LDS go through buffer
+// instructions rather than global ones: the compiler treats a pending global
+// load into LDS as touching both memory and LDS and then waits for every
+// outstanding LDS read wherever it needs one, which exposes the latency of
+// the reads just issued for the next step.
+__device__ inline __amdgpu_buffer_rsrc_t byte_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
+}
 
 // Waits until at most VM vector-memory operations of this wave are
 // outstanding and all of its LDS reads have returned, then the workgroup
@@ -249,16 +258,21 @@ __device__ __forceinline__ void prefill_tile(const PreArgs& a, const PreItem& it
 
   // ---- block loads: rows past T are clamped onto row T - 1 (a row of A only
   // reaches the same output row, which is not stored)
+  // A: byte offsets inside the tile's row stripe; B: the wave's B tile; |g|
   const LB_GLOBAL uint16_t* asrc[kAI];
+  int aoffb[kAI];
 #pragma unroll
   for (int i = 0; i < kAI; ++i) {
     const int s = 64 * (kWaves * i + wave) + lane;
-    asrc[i] = gp(A) + (int64_t)min(m0 + a_slot_row(s), T - 1) * lda + a_slot_chunk(s) * 8;
+    const int r = min(m0 + a_slot_row(s), T - 1) - m0;
+    asrc[i] = gp(A) + (int64_t)(m0 + r) * lda + a_slot_chunk(s) * 8;
+    aoffb[i] = (r * lda + a_slot_chunk(s) * 8) * 2;
   }
+  const __amdgpu_buffer_rsrc_t rsA = byte_rsrc(A + (int64_t)m0 * lda);
   const int btile = min(2 * it.nt + (wave & 1), ntiles - 1);
-  const LB_GLOBAL u32x4* bsrc = reinterpret_cast<const LB_GLOBAL u32x4*>(gp(Bw)) + (int64_t)btile * kbn * 64 + lane;
-  const LB_GLOBAL uint32_t* gsrc =
-      reinterpret_cast<const LB_GLOBAL uint32_t*>(gp(L.gabs) + (int64_t)(lane >> 5) * L.kb1 * kPreBK + l32 * 2);
+  const __amdgpu_buffer_rsrc_t rsB = byte_rsrc(Bw + (int64_t)btile * kbn * 64 * 4);
+  const __amdgpu_buffer_rsrc_t rsG = byte_rsrc(L.gabs);
+  const int goffb = ((lane >> 5) * L.kb1 * kPreBK + l32 * 2) * 2;
   // Issues block kb into LDS buffer buf.  Full blocks of 16-byte aligned rows
   // go straight to LDS (the B / |g| load first, so that a wait for "all but
   // the last kAI" covers it); a ragged or unaligned block goes through
@@ -267,13 +281,13 @@ __device__ __forceinline__ void prefill_tile(const PreArgs& a, const PreItem& it
     uint8_t* base = lds + buf * kBuf;
     const int k0 = kb * kPreBK;
     if (wave < 2)
-      __builtin_amdgcn_global_load_lds((gbl_void*)(bsrc + (int64_t)kb * 64), (lds_void*)(base + kBufA + wave * 1024), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_void*)(base + kBufA + wave * 1024), 16, (kb * 64 + lane) * 16, 0, 0, 0);
     else if (MODE == 1 && wave == 2)
-      __builtin_amdgcn_global_load_lds((gbl_void*)(gsrc + k0 / 2), (lds_void*)(base + kBufA + kBufB), 4, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsG, (lds_void*)(base + kBufA + kBufB), 4, goffb + k0 * 2, 0, 0, 0);
     if (vec_ok && k0 + kPreBK <= K) {
 #pragma unroll
       for (int i = 0; i < kAI; ++i)
-        __builtin_amdgcn_global_load_lds((gbl_void*)(asrc[i] + k0), (lds_void*)(base + (kWaves * i + wave) * 1024), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_void*)(base + (kWaves * i + wave) * 1024), 16, aoffb[i] + k0 * 2, 0, 0, 0);
     } else {
 #pragma unroll
       for (int i = 0; i < kAI; ++i) {
@@ -363,11 +377,17 @@ __device__ __forceinline__ void prefill_tile(const PreArgs& a, const PreItem& it
     vm_wait_barrier<0>();
   }
   u32x4 af[2][MB], bf[2][NB];
+  // GEMM1 magnitudes are read two K steps ahead (slot s & 1 holds step s's),
+  // so that expanding the next step's B operand waits for no LDS read of
+  // this step
+  u32x4 gq[2][2] = {};
   read_a(0, 0, af[0]);
   u32x4 bw = read_b(0);
   {
     const u32x4 g0 = MODE == 1 ? read_g(0, 0, bpath[0]) : u32x4{};
     const u32x4 g1 = (MODE == 1 && STR) ? read_g(0, 0, !bpath[0]) : u32x4{};
+    if (MODE == 1) gq[1][0] = read_g(0, 1, bpath[0]);
+    if (MODE == 1 && STR) gq[1][1] = read_g(0, 1, !bpath[0]);
     make_b(bw[0], g0, g1, kpath(0, 0), bf[0]);
   }
 
@@ -379,10 +399,12 @@ __device__ __forceinline__ void prefill_tile(const PreArgs& a, const PreItem& it
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int rb = ks < 3 ? cur : nxt, rks = (ks + 1) & 3;
+      const int gb = ks < 2 ? cur : nxt, gks = (ks + 2) & 3;
       read_a(rb, rks, af[(ks + 1) & 1]);
       const uint32_t dn = ks < 3 ? bw[ks + 1] : bwn[0];
-      const u32x4 g0 = MODE == 1 ? read_g(rb, rks, bpath[0]) : u32x4{};
-      const u32x4 g1 = (MODE == 1 && STR) ? read_g(rb, rks, !bpath[0]) : u32x4{};
+      const u32x4 g0 = gq[(ks + 1) & 1][0], g1 = gq[(ks + 1) & 1][1];
+      if (MODE == 1) gq[ks & 1][0] = read_g(gb, gks, bpath[0]);
+      if (MODE == 1 && STR) gq[ks & 1][1] = read_g(gb, gks, !bpath[0]);
       // the LDS reads of step ks + 1 go out before this step's MFMAs (the
       // scheduler would otherwise sink them next to their use and expose
       // their latency at every step)
