@@ -5,6 +5,7 @@ does all of the arithmetic; this package only marshals arguments.
 """
 from ._binding import (  # noqa: F401
     BF16,
+    BF16_FP32,
     EXPORTS,
     FP32,
     PREFILL_MIN_TOKENS,

@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblittlebit.so")
 
 OK, INVALID_ARGUMENT, INVALID_SIGN, ALIGNMENT, UNSUPPORTED, OUT_OF_MEMORY, HIP_ERROR = range(7)
-BF16, FP32 = 0, 1
+BF16, FP32, BF16_FP32 = 0, 1, 2   # lb_dtype: element types of (x, y)
 REGIME_AUTO, REGIME_EXACT, REGIME_DECODE, REGIME_PREFILL = 0, 1, 2, 3
 PREFILL_MIN_TOKENS = 128
 
@@ -168,13 +168,17 @@ def probe_stream_read(buf, stream=None) -> None:
                                       _stream(stream)))
 
 
-def _io_of(t) -> int:
+def _io_of(x, y) -> int:
+    """lb_dtype of an (x, y) pair: both bf16, both fp32, or bf16 x with fp32 y."""
     import torch
-    if t.dtype == torch.bfloat16:
+    pair = (x.dtype, y.dtype)
+    if pair == (torch.bfloat16, torch.bfloat16):
         return BF16
-    if t.dtype == torch.float32:
+    if pair == (torch.float32, torch.float32):
         return FP32
-    raise TypeError(f"x and y must be bfloat16 or float32, got {t.dtype}")
+    if pair == (torch.bfloat16, torch.float32):
+        return BF16_FP32
+    raise TypeError(f"x / y must be bf16 / bf16, fp32 / fp32 or bf16 / fp32, got {x.dtype} / {y.dtype}")
 
 
 class Linear:
@@ -225,15 +229,19 @@ class Linear:
         return dict(d_out=m.value, d_in=n.value, n_paths=npaths.value, ranks=list(ranks)[:npaths.value],
                     device_bytes=dev.value)
 
-    def forward(self, x, y=None, regime: int = REGIME_AUTO, stream=None):
+    def forward(self, x, y=None, regime: int = REGIME_AUTO, stream=None, out_dtype=None):
+        """y = x W^T.  y (allocated when None, of out_dtype or x's dtype) sets
+        the output type: bf16 x may write bf16 or fp32 y."""
         import torch
         if x.dim() != 2 or x.shape[1] != self.d_in:
             raise ValueError(f"x must be [tokens, {self.d_in}]")
         if not x.is_contiguous():
             raise ValueError("x must be contiguous")
         if y is None:
-            y = torch.empty((x.shape[0], self.d_out), dtype=x.dtype, device=x.device)
-        _check(lib().lb_linear_forward_ex(self.handle, x.data_ptr(), y.data_ptr(), x.shape[0], _io_of(x), regime,
+            y = torch.empty((x.shape[0], self.d_out), dtype=out_dtype or x.dtype, device=x.device)
+        if y.dim() != 2 or tuple(y.shape) != (x.shape[0], self.d_out) or not y.is_contiguous():
+            raise ValueError(f"y must be a contiguous [{x.shape[0]}, {self.d_out}] tensor")
+        _check(lib().lb_linear_forward_ex(self.handle, x.data_ptr(), y.data_ptr(), x.shape[0], _io_of(x, y), regime,
                                           _stream(stream)))
         return y
 
@@ -269,7 +277,9 @@ class Stack:
         if len(xs) != n or len(ys) != n:
             raise ValueError("need one x and one y per linear")
         tokens = xs[0].shape[0]
-        io = _io_of(xs[0])
+        io = _io_of(xs[0], ys[0])
+        if any(_io_of(x, y) != io for x, y in zip(xs, ys)):
+            raise TypeError("every entry of a stack forward must have the same x / y element types")
         xa = (C.c_void_p * n)(*[x.data_ptr() for x in xs])
         ya = (C.c_void_p * n)(*[y.data_ptr() for y in ys])
         if use_graph is None and regime == REGIME_AUTO:

@@ -318,7 +318,8 @@ lb_status build_decode_plan(DecodePlan& P, const lb_linear* L, int count, int T,
 
 // Launches the three decode kernels over token slices of at most kDecodeMaxTokens.
 lb_status run_decode(DecodePlan& P, const lb_linear* L, int count, const void* const* xs_d, void* const* ys_d,
-                     const void* x0, void* y0, int64_t tokens, hipStream_t st, const DecodeImage* img = nullptr) {
+                     const void* x0, void* y0, int64_t tokens, int yf32, hipStream_t st,
+                     const DecodeImage* img = nullptr) {
   for (int64_t t0 = 0; t0 < tokens; t0 += kDecodeMaxTokens) {
     const int T = (int)std::min<int64_t>(kDecodeMaxTokens, tokens - t0);
     if (P.T != T && P.T != -1) HIP_TRY(hipStreamSynchronize(st));  // the plan is rewritten below
@@ -332,6 +333,7 @@ lb_status run_decode(DecodePlan& P, const lb_linear* L, int count, const void* c
     a.y0 = y0;
     a.T = T;
     a.t0 = (int)t0;
+    a.yf32 = yf32;
     a.vitems = P.vitems_d;
     a.mitems = P.mitems_d;
     a.uitems = P.uitems_d;
@@ -346,12 +348,17 @@ lb_status run_decode(DecodePlan& P, const lb_linear* L, int count, const void* c
 lb_status check_io(int64_t tokens, lb_dtype io, lb_regime regime) {
   if (tokens <= 0) return fail(LB_ERR_INVALID_ARGUMENT, "tokens must be positive (got %lld)", (long long)tokens);
   if (tokens > LB_MAX_TOKENS) return fail(LB_ERR_UNSUPPORTED, "tokens %lld exceeds %d", (long long)tokens, LB_MAX_TOKENS);
-  if (io != LB_BF16 && io != LB_FP32) return fail(LB_ERR_INVALID_ARGUMENT, "io must be LB_BF16 or LB_FP32");
+  if (io != LB_BF16 && io != LB_FP32 && io != LB_BF16_FP32)
+    return fail(LB_ERR_INVALID_ARGUMENT, "io must be LB_BF16, LB_FP32 or LB_BF16_FP32");
   if (regime < LB_REGIME_AUTO || regime > LB_REGIME_PREFILL) return fail(LB_ERR_INVALID_ARGUMENT, "unknown regime");
   if (io == LB_FP32 && (regime == LB_REGIME_DECODE || regime == LB_REGIME_PREFILL))
-    return fail(LB_ERR_UNSUPPORTED, "the decode and prefill kernels take bf16 I/O; fp32 I/O runs the exact kernels");
+    return fail(LB_ERR_UNSUPPORTED, "the decode and prefill kernels read bf16 x; fp32 x runs the exact kernels");
   return LB_OK;
 }
+
+// element types of x and y
+inline int x_is_fp32(lb_dtype io) { return io == LB_FP32 ? 1 : 0; }
+inline int y_is_fp32(lb_dtype io) { return io == LB_BF16 ? 0 : 1; }
 
 lb_regime pick_regime(int64_t tokens, lb_dtype io, lb_regime regime) {
   if (regime != LB_REGIME_AUTO) return regime;
@@ -605,7 +612,7 @@ lb_status lb_linear_forward_ex(lb_linear L, const void* x, void* y, int64_t toke
       HIP_TRY(hipStreamSynchronize(st));
       HIP_TRY(L->zexact.ensure(want));
     }
-    HIP_TRY(launch_exact(L->paths, L->np, (int)L->m, (int)L->n, x, y, (int)tokens, io == LB_FP32,
+    HIP_TRY(launch_exact(L->paths, L->np, (int)L->m, (int)L->n, x, y, (int)tokens, x_is_fp32(io), y_is_fp32(io),
                          reinterpret_cast<float*>(L->zexact.ptr), rpad, st));
     return LB_OK;
   }
@@ -613,13 +620,13 @@ lb_status lb_linear_forward_ex(lb_linear L, const void* x, void* y, int64_t toke
     const int T = (int)std::min<int64_t>(tokens, kDecodeMaxTokens);
     if (L->plan.T != T) HIP_TRY(hipStreamSynchronize(st));
     lb_linear one[1] = {L};
-    return run_decode(L->plan, one, 1, nullptr, nullptr, x, y, tokens, st);
+    return run_decode(L->plan, one, 1, nullptr, nullptr, x, y, tokens, y_is_fp32(io), st);
   }
   if (!prefill_available()) return fail(LB_ERR_UNSUPPORTED, "the prefill kernels are not available in this build");
   const PrefillLayer* one[1] = {&L->pre};
   const void* xs[1] = {x};
   void* ys[1] = {y};
-  HIP_TRY(prefill_run(L->pplan, one, 1, xs, ys, (int)tokens, st, /*single=*/true));
+  HIP_TRY(prefill_run(L->pplan, one, 1, xs, ys, (int)tokens, y_is_fp32(io), st, /*single=*/true));
   return LB_OK;
 }
 
@@ -710,16 +717,16 @@ lb_status stack_launch(lb_stack S, lb_regime rg, int64_t tokens, lb_dtype io, hi
   const int count = (int)S->linears.size();
   if (rg == LB_REGIME_DECODE) {
     for (StackGroup& G : S->groups) {
-      lb_status s = run_decode(G.plan, G.lins.data(), (int)G.lins.size(), G.xs_d, G.ys_d, nullptr, nullptr, tokens, st,
-                               &G.view);
+      lb_status s = run_decode(G.plan, G.lins.data(), (int)G.lins.size(), G.xs_d, G.ys_d, nullptr, nullptr, tokens,
+                               y_is_fp32(io), st, &G.view);
       if (s != LB_OK) return s;
     }
     return LB_OK;
   }
   if (rg == LB_REGIME_PREFILL) {
     for (StackGroup& G : S->groups)
-      HIP_TRY(prefill_run(G.pplan, G.pre.data(), (int)G.lins.size(), G.xs_h.data(), G.ys_h.data(), (int)tokens, st,
-                          false));
+      HIP_TRY(prefill_run(G.pplan, G.pre.data(), (int)G.lins.size(), G.xs_h.data(), G.ys_h.data(), (int)tokens,
+                          y_is_fp32(io), st, false));
     return LB_OK;
   }
   // exact: one pair of kernels per linear, sharing one z' scratch laid out per entry
@@ -729,8 +736,8 @@ lb_status stack_launch(lb_stack S, lb_regime rg, int64_t tokens, lb_dtype io, hi
     int rpad = 0;
     for (int p = 0; p < L->np; ++p) rpad = std::max(rpad, L->paths[p].r);
     rpad = (rpad + 15) / 16 * 16;
-    HIP_TRY(launch_exact(L->paths, L->np, (int)L->m, (int)L->n, S->xs_h[i], S->ys_h[i], (int)tokens, io == LB_FP32,
-                         reinterpret_cast<float*>(S->zexact.ptr) + off, rpad, st));
+    HIP_TRY(launch_exact(L->paths, L->np, (int)L->m, (int)L->n, S->xs_h[i], S->ys_h[i], (int)tokens, x_is_fp32(io),
+                         y_is_fp32(io), reinterpret_cast<float*>(S->zexact.ptr) + off, rpad, st));
     off += (size_t)L->np * tokens * rpad;
   }
   return LB_OK;
@@ -745,8 +752,8 @@ std::vector<int> stack_levels(const std::vector<lb_linear>& lins, const std::vec
                               const std::vector<void*>& ys, int64_t tokens, lb_dtype io, int* bad) {
   const int count = (int)lins.size();
   *bad = -1;
-  const uint64_t es = io == LB_FP32 ? 4 : 2;
-  auto range = [&](const void* p, int64_t cols) {
+  const uint64_t xes = x_is_fp32(io) ? 4 : 2, yes = y_is_fp32(io) ? 4 : 2;   // element bytes of x, y
+  auto range = [&](const void* p, int64_t cols, uint64_t es) {
     const uint64_t a = reinterpret_cast<uintptr_t>(p);
     return std::make_pair(a, a + (uint64_t)tokens * (uint64_t)cols * es);
   };
@@ -755,10 +762,10 @@ std::vector<int> stack_levels(const std::vector<lb_linear>& lins, const std::vec
   };
   std::vector<int> level(count, 0);
   for (int j = 0; j < count; ++j) {
-    const auto xj = range(xs[j], lins[j]->n), yj = range(ys[j], lins[j]->m);
+    const auto xj = range(xs[j], lins[j]->n, xes), yj = range(ys[j], lins[j]->m, yes);
     if (overlap(xj, yj) && *bad < 0) *bad = j;
     for (int i = 0; i < j; ++i) {
-      const auto xi = range(xs[i], lins[i]->n), yi = range(ys[i], lins[i]->m);
+      const auto xi = range(xs[i], lins[i]->n, xes), yi = range(ys[i], lins[i]->m, yes);
       if (overlap(yi, xj) || overlap(yi, yj) || overlap(yj, xi)) level[j] = std::max(level[j], level[i] + 1);
     }
   }

@@ -642,8 +642,9 @@ struct UShape {
 template <int TM>
 struct UCtx {
   static constexpr int TB = UShape<TM>::TB;
-  int m, T, np, nu0;
-  LB_GLOBAL uint16_t* y;
+  int m, T, np, nu0, yf32;
+  LB_GLOBAL uint16_t* y;                           // bf16 y at this launch's first token
+  LB_GLOBAL float* yf;                             // the same as fp32 (yf32)
   float cv[2][TB][2];                              // U correction sums of the lane's tokens
 };
 
@@ -676,16 +677,22 @@ __device__ __attribute__((always_inline)) inline void u_store_plain(const UCtx<T
 #pragma unroll
       for (int qq = 0; qq < UShape<TM>::KQQ; ++qq) {
         const int t = tb * 8 + 2 * gr + qq, i = 64 * q + 16 * rt + mr;
-        if (t < C.T && i < C.m) C.y[(int64_t)t * C.m + i] = bf16_bits(part[rt][tb][qq]);
+        if (t < C.T && i < C.m) {
+          if (C.yf32) C.yf[(int64_t)t * C.m + i] = part[rt][tb][qq];
+          else C.y[(int64_t)t * C.m + i] = bf16_bits(part[rt][tb][qq]);
+        }
       }
   vm_wait<0>();
 }
 
-// One quad's outputs into the wave's staging area: [token][64 rows] bf16.
+// One quad's outputs into the wave's staging area: [token][64 rows] bf16,
+// or fp32 (twice the bytes per quad) when y is fp32.
 template <int TM>
-__device__ __attribute__((always_inline)) inline void u_stage(const float (&part)[4][UShape<TM>::TB][2], uint8_t* stq) {
+__device__ __attribute__((always_inline)) inline void u_stage(const float (&part)[4][UShape<TM>::TB][2], uint8_t* stq,
+                                                             int yf32) {
   const int lane = threadIdx.x & 63, mr = lane & 15, gr = lane >> 4;
   uint16_t* s16 = reinterpret_cast<uint16_t*>(stq);
+  float* s32 = reinterpret_cast<float*>(stq);
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -693,7 +700,10 @@ __device__ __attribute__((always_inline)) inline void u_stage(const float (&part
 #pragma unroll
       for (int qq = 0; qq < UShape<TM>::KQQ; ++qq) {
         const int t = tb * 8 + 2 * gr + qq;
-        if (t < TM) s16[t * 64 + rt * 16 + mr] = bf16_bits(part[rt][tb][qq]);
+        if (t < TM) {
+          if (yf32) s32[t * 64 + rt * 16 + mr] = part[rt][tb][qq];
+          else s16[t * 64 + rt * 16 + mr] = bf16_bits(part[rt][tb][qq]);
+        }
       }
 }
 
@@ -704,6 +714,18 @@ template <int TM>
 __device__ __attribute__((always_inline)) inline void u_flush(const UCtx<TM>& C, int qa, int nst, const uint8_t* stg) {
   const int lane = threadIdx.x & 63;
   wave_lds_fence();
+  if (C.yf32) {
+    // fp32: 256 bytes per token and quad, lane l: token 4 k + l / 16, rows 4 (l % 16) .. + 3
+    for (int j = 0; j < nst; ++j) {
+#pragma unroll
+      for (int k = 0; k < (TM + 3) / 4; ++k) {
+        const int t = min(4 * k + (lane >> 4), C.T - 1);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + (j * TM + t) * 256 + (lane & 15) * 16);
+        *reinterpret_cast<LB_GLOBAL u32x4*>(C.yf + (int64_t)t * C.m + 64 * (qa + j) + (lane & 15) * 4) = v;
+      }
+    }
+    return;
+  }
   for (int j = 0; j < nst; ++j) {
 #pragma unroll
     for (int k = 0; k < UShape<TM>::KST; ++k) {
@@ -760,7 +782,8 @@ __device__ __attribute__((always_inline)) inline void u_stream(const DecArgs& a,
   vm_wait<kRing - 1>();
 
   // quads whose 64 rows are whole (and 16-byte aligned in y) are staged
-  const int nst = (C.m & 7) == 0 ? max(0, min(qb, C.m / 64) - qa) : 0;
+  // (as many as the staging area holds: half as many when y is fp32)
+  const int nst = (C.m & 7) == 0 ? min(max(0, min(qb, C.m / 64) - qa), C.yf32 ? S::QW / 2 : S::QW) : 0;
   int s = 0;
   for (int q = qa; q < qb; ++q) {
     v4f acc[4][TB];
@@ -804,7 +827,7 @@ __device__ __attribute__((always_inline)) inline void u_stream(const DecArgs& a,
     });
     if (C.np > 1) u_fold<TB>(acc, h[1], C.cv[1], part, false);
     else u_fold<TB>(acc, h[0], C.cv[0], part, true);
-    if (q - qa < nst) u_stage<TM>(part, stg + (q - qa) * TM * 128);
+    if (q - qa < nst) u_stage<TM>(part, stg + (q - qa) * TM * (C.yf32 ? 256 : 128), C.yf32);
     else u_store_plain<TM>(C, q, part);
   }
   vm_wait<0>();                                    // no direct-to-LDS load may still be in flight
@@ -861,7 +884,8 @@ __device__ __attribute__((always_inline)) inline void u_plain(const DecArgs& a, 
   }
 }
 
-template <int TM>
+// YF: y is fp32 (a separate instantiation, so the bf16 kernel carries none of it)
+template <int TM, bool YF>
 __global__ void __launch_bounds__(kThreads, TM >= 16 ? 2 : 3) k_decode_u(DecArgs a) {
   using S = UShape<TM>;
   constexpr int TB = S::TB;
@@ -878,7 +902,9 @@ __global__ void __launch_bounds__(kThreads, TM >= 16 ? 2 : 3) k_decode_u(DecArgs
   C.np = Eg.np;
   C.nu0 = Eg.ug.nu0;
   void* yv = a.xs ? cp(a.ys)[it.entry] : a.y0;
+  C.yf32 = YF;
   C.y = gp(reinterpret_cast<uint16_t*>(yv)) + (int64_t)a.t0 * C.m;
+  C.yf = gp(reinterpret_cast<float*>(yv)) + (int64_t)a.t0 * C.m;
   const LB_GLOBAL float* cval = gp(Eg.cval);
 #pragma unroll
   for (int p = 0; p < 2; ++p)
@@ -925,15 +951,21 @@ hipError_t launch_decode_mid(const DecArgs& a, int nitems, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <bool YF>
+static void launch_u(const DecArgs& a, int nitems, hipStream_t st) {
+  switch (decode_bucket(a.T)) {
+    case 1: hipLaunchKernelGGL((k_decode_u<1, YF>), dim3(nitems), dim3(kThreads), UShape<1>::lds, st, a); break;
+    case 2: hipLaunchKernelGGL((k_decode_u<2, YF>), dim3(nitems), dim3(kThreads), UShape<2>::lds, st, a); break;
+    case 4: hipLaunchKernelGGL((k_decode_u<4, YF>), dim3(nitems), dim3(kThreads), UShape<4>::lds, st, a); break;
+    case 8: hipLaunchKernelGGL((k_decode_u<8, YF>), dim3(nitems), dim3(kThreads), UShape<8>::lds, st, a); break;
+    default: hipLaunchKernelGGL((k_decode_u<16, YF>), dim3(nitems), dim3(kThreads), UShape<16>::lds, st, a); break;
+  }
+}
+
 hipError_t launch_decode_u(const DecArgs& a, int nitems, hipStream_t st) {
   if (nitems <= 0) return hipSuccess;
-  switch (decode_bucket(a.T)) {
-    case 1: hipLaunchKernelGGL(k_decode_u<1>, dim3(nitems), dim3(kThreads), UShape<1>::lds, st, a); break;
-    case 2: hipLaunchKernelGGL(k_decode_u<2>, dim3(nitems), dim3(kThreads), UShape<2>::lds, st, a); break;
-    case 4: hipLaunchKernelGGL(k_decode_u<4>, dim3(nitems), dim3(kThreads), UShape<4>::lds, st, a); break;
-    case 8: hipLaunchKernelGGL(k_decode_u<8>, dim3(nitems), dim3(kThreads), UShape<8>::lds, st, a); break;
-    default: hipLaunchKernelGGL(k_decode_u<16>, dim3(nitems), dim3(kThreads), UShape<16>::lds, st, a); break;
-  }
+  if (a.yf32) launch_u<true>(a, nitems, st);
+  else launch_u<false>(a, nitems, st);
   return hipGetLastError();
 }
 

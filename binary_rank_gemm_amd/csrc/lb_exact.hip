@@ -1,4 +1,5 @@
-// fp32 forward of one linear with plain vector arithmetic (the fp32-I/O path).
+// fp32 forward of one linear with plain vector arithmetic (the fp32-I/O path;
+// it also serves bf16 x with bf16 or fp32 y).
 //
 // It follows the factorised order of the paper notes ("LittleBit", section
 // "Key design"): per path t = x o g, z = t V, z' = z o l, then
@@ -13,8 +14,8 @@ namespace lb {
 
 namespace {
 
-__device__ inline float ld_act(const void* x, int64_t idx, int io_fp32) {
-  if (io_fp32) return reinterpret_cast<const float*>(x)[idx];
+__device__ inline float ld_act(const void* x, int64_t idx, int x_fp32) {
+  if (x_fp32) return reinterpret_cast<const float*>(x)[idx];
   uint32_t b = (uint32_t)reinterpret_cast<const uint16_t*>(x)[idx] << 16;
   return __uint_as_float(b);
 }
@@ -33,7 +34,7 @@ struct ExactArgs {
   const void* x;
   void* y;
   float* zbuf;
-  int np, m, n, T, rpad, io_fp32, t0;
+  int np, m, n, T, rpad, x_fp32, y_fp32, t0;
 };
 
 // grid (ceil(r_max/64), np, T), block 256: lane -> latent column j, wave -> row phase.
@@ -49,7 +50,7 @@ __global__ void __launch_bounds__(256) k_exact_z(ExactArgs a) {
     int cnt = 0;
     const int64_t xo = (int64_t)t * a.n;
     for (int k = wave; k < a.n; k += 4) {
-      float tv = ld_act(a.x, xo + k, a.io_fp32) * f16(P.g, k);
+      float tv = ld_act(a.x, xo + k, a.x_fp32) * f16(P.g, k);
       uint32_t bit = (P.v_can[(int64_t)k * P.W + (j >> 5)] >> (j & 31)) & 1u;
       blk += bit ? -tv : tv;
       if (++cnt == 64) { acc += blk; blk = 0.f; cnt = 0; }
@@ -92,17 +93,18 @@ __global__ void __launch_bounds__(256) k_exact_y(ExactArgs a) {
     y += s * f16(P.h, i);
   }
   const int64_t yo = (int64_t)t * a.m + i;
-  if (a.io_fp32) reinterpret_cast<float*>(a.y)[yo] = y;
+  if (a.y_fp32) reinterpret_cast<float*>(a.y)[yo] = y;
   else reinterpret_cast<uint16_t*>(a.y)[yo] = f32_to_bf16_rne(y);
 }
 
 }  // namespace
 
 hipError_t launch_exact(const PathDev* p, int np, int m, int n, const void* x, void* y, int T,
-                        int io_fp32, float* zbuf, int rpad, hipStream_t st) {
+                        int x_fp32, int y_fp32, float* zbuf, int rpad, hipStream_t st) {
   ExactArgs a{};
   for (int i = 0; i < np; ++i) a.p[i] = p[i];
-  a.x = x; a.y = y; a.zbuf = zbuf; a.np = np; a.m = m; a.n = n; a.T = T; a.rpad = rpad; a.io_fp32 = io_fp32;
+  a.x = x; a.y = y; a.zbuf = zbuf; a.np = np; a.m = m; a.n = n; a.T = T; a.rpad = rpad; a.x_fp32 = x_fp32;
+  a.y_fp32 = y_fp32;
   int rmax = 0;
   for (int i = 0; i < np; ++i) rmax = rmax > p[i].r ? rmax : p[i].r;
   const int kMaxY = 65535;  // grid y/z extent limit: tokens go in slices

@@ -117,6 +117,7 @@ struct DecArgs {
   const UItem* uitems;
   float* part;             // V-stage partial sums, decode_slot_floats(bucket) per slot
   int T, t0;               // tokens in this launch and the offset of its first token
+  int yf32;                // y is fp32 (else bf16)
 };
 
 // Tokens one decode launch handles (token blocks of 8, at most 2 blocks).
@@ -150,7 +151,7 @@ hipError_t launch_retile_v_decode(const uint32_t* vcan, int n, int r, uint32_t* 
 
 // fp32 exact path: z' then y, one linear
 hipError_t launch_exact(const PathDev* p, int np, int m, int n, const void* x, void* y, int T,
-                        int io_fp32, float* zbuf, int rpad, hipStream_t st);
+                        int x_fp32, int y_fp32, float* zbuf, int rpad, hipStream_t st);
 
 // decode path: V stage, mid stage, U stage, one workgroup per work item
 hipError_t launch_decode_v(const DecArgs& a, int nitems, hipStream_t st);

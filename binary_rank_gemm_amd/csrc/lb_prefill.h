@@ -66,7 +66,7 @@ hipError_t prefill_prepare(PrefillPlan& P, const PrefillLayer* const* layers, in
 // arguments (the plan is rebuilt here when T changes); otherwise the plan
 // must have been prepared for these pointers and T.
 hipError_t prefill_run(PrefillPlan& P, const PrefillLayer* const* layers, int count, const void* const* xs,
-                       void* const* ys, int T, hipStream_t st, bool single);
+                       void* const* ys, int T, int yf32, hipStream_t st, bool single);
 void prefill_plan_release(PrefillPlan& P);
 
 }  // namespace lb

@@ -156,6 +156,7 @@ struct PreArgs {
   const void* x0;   // when non-null: entry 0's input / output (single-linear forwards)
   void* y0;
   int T;
+  int yf32;         // GEMM2 writes fp32 y (else bf16)
 };
 
 __device__ inline v16f mfma32(const u32x4& a, const u32x4& b, v16f c) {
@@ -428,6 +429,34 @@ __device__ __forceinline__ void prefill_tile(const PreArgs& a, const PreItem& it
   // every wave is past the loop's last barrier, which waited for all LDS
   // reads) and writes whole 512-byte row segments; otherwise each run goes
   // straight out.
+  if (MODE == 2 && a.yf32) {
+    // fp32 y: each run of four adjacent columns is one 16-byte store
+    float* Cf = reinterpret_cast<float*>(first ? a.y0 : Eg.y);
+    const bool vec4 = (ldc & 3) == 0;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int cb = n0 + wcol + 32 * b + 4 * kg;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int row = m0 + wm * MB * 32 + mb * 32 + l32;
+        if (row >= T) continue;
+        LB_GLOBAL float* cp = gp(Cf) + (int64_t)row * ldc;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int col = cb + 8 * j;
+          const f4 v = {acc[mb][b][4 * j], acc[mb][b][4 * j + 1], acc[mb][b][4 * j + 2], acc[mb][b][4 * j + 3]};
+          if (vec4 && col + 3 < N) {
+            *reinterpret_cast<LB_GLOBAL f4*>(cp + col) = v;
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (col + i < N) cp[col + i] = v[i];
+          }
+        }
+      }
+    }
+    return;
+  }
   const bool c_stage = (ldc & 7) == 0;
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
@@ -692,8 +721,9 @@ hipError_t prefill_prepare(PrefillPlan& P, const PrefillLayer* const* layers, in
 }
 
 hipError_t prefill_run(PrefillPlan& P, const PrefillLayer* const* layers, int count, const void* const* xs,
-                       void* const* ys, int T, hipStream_t st, bool single) {
+                       void* const* ys, int T, int yf32, hipStream_t st, bool single) {
   PreArgs a{};
+  a.yf32 = yf32;
   if (single) {
     // single-linear forwards: the plan holds no pointers, they travel as kernel arguments
     if (P.T != T || P.count != 1) {

@@ -54,14 +54,19 @@ typedef enum {
   LB_ERR_HIP = 6               /* a HIP runtime call failed                   */
 } lb_status;
 
-typedef enum { LB_BF16 = 0, LB_FP32 = 1 } lb_dtype; /* element type of x and y */
+/* Element types of x and y.  LB_BF16_FP32 reads bf16 x and writes fp32 y:
+ * the kernels' fp32 results are stored without the final rounding to bf16
+ * (for callers that keep an fp32 residual stream). */
+typedef enum { LB_BF16 = 0, LB_FP32 = 1, LB_BF16_FP32 = 2 } lb_dtype;
 
 /* Which kernels run a forward.  AUTO picks by tokens and dtype:
  *   fp32 I/O            -> EXACT  (fp32 vector arithmetic end to end);
- *   bf16, tokens <  LB_PREFILL_MIN_TOKENS -> DECODE (fused fp8 x fp4 MFMA pass);
- *   bf16, tokens >= LB_PREFILL_MIN_TOKENS -> PREFILL (bf16 MFMA GEMMs).
+ *   bf16 x (y bf16 or fp32), tokens <  LB_PREFILL_MIN_TOKENS -> DECODE
+ *                          (fused fp8 x fp4 MFMA pass);
+ *   bf16 x (y bf16 or fp32), tokens >= LB_PREFILL_MIN_TOKENS -> PREFILL
+ *                          (bf16 MFMA GEMMs).
  * Forcing a regime is for tests and measurements; every regime accepts every
- * token count.  DECODE and PREFILL require bf16 I/O. */
+ * token count.  DECODE and PREFILL require bf16 x (LB_BF16 or LB_BF16_FP32). */
 typedef enum { LB_REGIME_AUTO = 0, LB_REGIME_EXACT = 1, LB_REGIME_DECODE = 2,
                LB_REGIME_PREFILL = 3 } lb_regime;
 
@@ -123,8 +128,8 @@ lb_status lb_unpack_signs(const uint32_t* packed, int64_t rows, int64_t rank, in
 lb_status lb_linear_create(int64_t d_out, int64_t d_in, const lb_path* paths, int32_t n_paths,
                            void* stream, lb_linear* out);
 
-/* y = x W^T for `tokens` rows.  x and y are device pointers (bf16 or fp32 per
- * `io`), borrowed until the stream work completes.  Runs the kernels of
+/* y = x W^T for `tokens` rows.  x and y are device pointers (element types
+ * per `io`), borrowed until the stream work completes.  Runs the kernels of
  * LB_REGIME_AUTO.  Concurrent forwards of the same linear must be ordered on
  * one stream (they share the linear's scratch memory). */
 lb_status lb_linear_forward(lb_linear L, const void* x, void* y, int64_t tokens, lb_dtype io, void* stream);

@@ -123,6 +123,18 @@ def test_argument_validation_before_any_device_work():
     assert L.lb_init_dual_svid(dummy, 8, 8, nul, 1, None) == lb._binding.INVALID_ARGUMENT
 
 
+def test_binding_io_types():
+    """The binding's lb_dtype of an (x, y) pair; other pairs are refused."""
+    torch = pytest.importorskip("torch")
+    b, f = torch.zeros(1, dtype=torch.bfloat16), torch.zeros(1, dtype=torch.float32)
+    io = lb._binding._io_of
+    assert (io(b, b), io(f, f), io(b, f)) == (lb.BF16, lb.FP32, lb.BF16_FP32) == (0, 1, 2)
+    with pytest.raises(TypeError):
+        io(f, b)
+    with pytest.raises(TypeError):
+        io(b, torch.zeros(1, dtype=torch.float16))
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     import importlib
     b = importlib.import_module("binary_rank_gemm_amd._binding")

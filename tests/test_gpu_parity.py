@@ -220,6 +220,59 @@ def test_forward_errors():
 
 
 # ----------------------------------------------------------------------------
+# bf16 x, fp32 y (LB_BF16_FP32)
+# ----------------------------------------------------------------------------
+
+MIXED_CASES = [  # (regime, m, n, ranks, T)
+    (lb.REGIME_DECODE, 777, 2100, [319, 5], 1),
+    (lb.REGIME_DECODE, 513, 257, [33, 31], 9),
+    (lb.REGIME_DECODE, 1024, 640, [102, 90], 16),
+    (lb.REGIME_DECODE, 130, 200, [40], 17),        # two decode launches; rows not whole quads
+    (lb.REGIME_PREFILL, 600, 520, [70, 50], 200),
+    (lb.REGIME_PREFILL, 258, 300, [33], 130),      # ragged rows of y (not a multiple of 4 columns)
+    (lb.REGIME_EXACT, 300, 257, [31, 9], 3),
+]
+
+
+@pytest.mark.parametrize("regime,m,n,ranks,T", MIXED_CASES)
+def test_bf16_in_fp32_out(regime, m, n, ranks, T):
+    """fp32 y from bf16 x: against the oracle, and rounding the fp32 result to
+    bf16 (nearest even) gives the bf16-output forward bit for bit (the same
+    sums, stored before the last rounding)."""
+    log(f"bf16->fp32 regime={regime} m={m} n={n} ranks={ranks} T={T}")
+    paths = seeded_paths((31, m, n), m, n, ranks)
+    x = x_tensor(synth.activations((31, T, n), T, n))
+    lin = build(m, n, paths)
+    yf = lin.forward(x, regime=regime, out_dtype=torch.float32)
+    yb = lin.forward(x, regime=regime)
+    torch.cuda.synchronize()
+    assert yf.dtype == torch.float32 and yb.dtype == torch.bfloat16
+    ref = oracle.forward(to_f64(x), paths, m, n)
+    if regime == lb.REGIME_EXACT:
+        assert_fp32_close(to_f64(yf), ref, "exact bf16->fp32")
+    else:
+        s = assert_bf16_close(to_f64(yf), ref, "bf16->fp32")
+        log(f"  E_rms={s['erms']:.2e} E_max/rms={s['emax_rel_rms']:.2e}")
+    assert torch.equal(yf.to(torch.bfloat16).view(torch.int16), yb.view(torch.int16))
+
+
+@pytest.mark.parametrize("regime,T", [(lb.REGIME_DECODE, 4), (lb.REGIME_PREFILL, 256)])
+def test_stack_bf16_in_fp32_out(regime, T):
+    shapes = [(256, 512, [16, 16]), (1024, 300, [33, 20]), (96, 96, [5])]
+    lins, paths, xs = make_stack(32, shapes, T)
+    xt = [x_tensor(x) for x in xs]
+    ys = [torch.empty((T, m), dtype=torch.float32, device="cuda") for (m, _, _) in shapes]
+    S = lb.Stack(lins)
+    S.forward(xt, ys, regime=regime, use_graph=False)
+    torch.cuda.synchronize()
+    for (m, n, _), p, x, y in zip(shapes, paths, xs, ys):
+        assert_bf16_close(to_f64(y), oracle.forward(x_f64(x), p, m, n), f"stack bf16->fp32 {m}x{n}")
+    with pytest.raises(TypeError):
+        S.forward(xt, [y.to(torch.bfloat16) if i == 0 else y for i, y in enumerate(ys)], regime=regime)
+    S.close()
+
+
+# ----------------------------------------------------------------------------
 # stacks
 # ----------------------------------------------------------------------------
 
