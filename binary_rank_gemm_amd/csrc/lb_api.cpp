@@ -316,15 +316,19 @@ lb_status build_decode_plan(DecodePlan& P, const lb_linear* L, int count, int T,
   return LB_OK;
 }
 
-// Launches the three decode kernels over token slices of at most kDecodeMaxTokens.
+// Launches the three decode kernels over token slices of at most
+// kDecodeMaxTokens.  Every slice of one forward runs on one plan, built for
+// the first slice's token count (a shorter last slice runs the same kernels
+// on fewer tokens), so a ragged token count never rebuilds the plan.
 lb_status run_decode(DecodePlan& P, const lb_linear* L, int count, const void* const* xs_d, void* const* ys_d,
                      const void* x0, void* y0, int64_t tokens, int yf32, hipStream_t st,
                      const DecodeImage* img = nullptr) {
+  const int Tplan = (int)std::min<int64_t>(kDecodeMaxTokens, tokens);
+  if (P.T != Tplan && P.T != -1) HIP_TRY(hipStreamSynchronize(st));  // the plan is rewritten below
+  lb_status s = build_decode_plan(P, L, count, Tplan, img);
+  if (s != LB_OK) return s;
   for (int64_t t0 = 0; t0 < tokens; t0 += kDecodeMaxTokens) {
     const int T = (int)std::min<int64_t>(kDecodeMaxTokens, tokens - t0);
-    if (P.T != T && P.T != -1) HIP_TRY(hipStreamSynchronize(st));  // the plan is rewritten below
-    lb_status s = build_decode_plan(P, L, count, T, img);
-    if (s != LB_OK) return s;
     DecArgs a{};
     a.entries = P.entries_d;
     a.xs = xs_d;
@@ -333,6 +337,7 @@ lb_status run_decode(DecodePlan& P, const lb_linear* L, int count, const void* c
     a.y0 = y0;
     a.T = T;
     a.t0 = (int)t0;
+    a.bucket = decode_bucket(Tplan);
     a.yf32 = yf32;
     a.vitems = P.vitems_d;
     a.mitems = P.mitems_d;

@@ -929,7 +929,7 @@ __global__ void __launch_bounds__(kThreads, TM >= 16 ? 2 : 3) k_decode_u(DecArgs
 
 hipError_t launch_decode_v(const DecArgs& a, int nitems, hipStream_t st) {
   if (nitems <= 0) return hipSuccess;
-  switch (decode_bucket(a.T)) {
+  switch (a.bucket) {
     case 1: hipLaunchKernelGGL(k_decode_v<1>, dim3(nitems), dim3(kThreads), VShape<1>::lds, st, a); break;
     case 2: hipLaunchKernelGGL(k_decode_v<2>, dim3(nitems), dim3(kThreads), VShape<2>::lds, st, a); break;
     case 4: hipLaunchKernelGGL(k_decode_v<4>, dim3(nitems), dim3(kThreads), VShape<4>::lds, st, a); break;
@@ -941,7 +941,7 @@ hipError_t launch_decode_v(const DecArgs& a, int nitems, hipStream_t st) {
 
 hipError_t launch_decode_mid(const DecArgs& a, int nitems, hipStream_t st) {
   if (nitems <= 0) return hipSuccess;
-  switch (decode_bucket(a.T)) {
+  switch (a.bucket) {
     case 1: hipLaunchKernelGGL(k_decode_mid<1>, dim3(nitems), dim3(kThreads), 0, st, a); break;
     case 2: hipLaunchKernelGGL(k_decode_mid<2>, dim3(nitems), dim3(kThreads), 0, st, a); break;
     case 4: hipLaunchKernelGGL(k_decode_mid<4>, dim3(nitems), dim3(kThreads), 0, st, a); break;
@@ -953,7 +953,7 @@ hipError_t launch_decode_mid(const DecArgs& a, int nitems, hipStream_t st) {
 
 template <bool YF>
 static void launch_u(const DecArgs& a, int nitems, hipStream_t st) {
-  switch (decode_bucket(a.T)) {
+  switch (a.bucket) {
     case 1: hipLaunchKernelGGL((k_decode_u<1, YF>), dim3(nitems), dim3(kThreads), UShape<1>::lds, st, a); break;
     case 2: hipLaunchKernelGGL((k_decode_u<2, YF>), dim3(nitems), dim3(kThreads), UShape<2>::lds, st, a); break;
     case 4: hipLaunchKernelGGL((k_decode_u<4, YF>), dim3(nitems), dim3(kThreads), UShape<4>::lds, st, a); break;

@@ -117,6 +117,7 @@ struct DecArgs {
   const UItem* uitems;
   float* part;             // V-stage partial sums, decode_slot_floats(bucket) per slot
   int T, t0;               // tokens in this launch and the offset of its first token
+  int bucket;              // token bucket the plan was built for (T <= bucket): selects the kernels
   int yf32;                // y is fp32 (else bf16)
 };
 
