@@ -336,10 +336,12 @@ def run_decode(args, lb, torch):
         wl = dataclasses.replace(wl, layers=min(args.layers, wl.layers))
     S = lb.Stack(lins)
     # direct launches of the decode kernels: on this ROCm a HIP graph replay
-    # adds ~13 us of its own per replay (timed below and reported beside)
-    fn = lambda: S.forward(xs, ys, regime=lb.REGIME_DECODE, use_graph=False)
+    # adds a few us of its own per replay (timed below and reported beside).
+    # The stack is bound to its buffers once, so each step is one C-ABI call
+    # with no per-call marshalling of the 560 pointers.
+    fn = S.bind(xs, ys, regime=lb.REGIME_DECODE, use_graph=False).forward
     wall, kern_ms = time_steps(fn, args.steps, args.warmup, torch)
-    fn_g = lambda: S.forward(xs, ys, regime=lb.REGIME_DECODE, use_graph=True)
+    fn_g = S.bind(xs, ys, regime=lb.REGIME_DECODE, use_graph=True).forward
     _, graph_ms = time_steps(fn_g, args.steps, args.warmup, torch)
     byts, flops = algorithmic(wl, ranks_of, T)
     ms = wall * 1e3 / args.steps
@@ -372,7 +374,7 @@ def run_chained(r, lb, torch, steps=20, warmup=5):
     S = lb.Stack(lins)
     out = {}
     for lab, g in (("direct", False), ("graph", True)):
-        fn = lambda: S.forward(xs, ys, regime=lb.REGIME_DECODE, use_graph=g)
+        fn = S.bind(xs, ys, regime=lb.REGIME_DECODE, use_graph=g).forward
         _, ms = time_steps(fn, steps, warmup, torch)
         out[f"us_per_token_{lab}"] = round(ms * 1e3 / T, 1)
     out["levels"] = 4 * wl.layers
@@ -390,7 +392,7 @@ def run_prefill(args, lb, torch, workload):
     if args.layers:
         wl = dataclasses.replace(wl, layers=min(args.layers, wl.layers))
     S = lb.Stack(lins)
-    fn = lambda: S.forward(xs, ys, regime=lb.REGIME_PREFILL, use_graph=True)
+    fn = S.bind(xs, ys, regime=lb.REGIME_PREFILL, use_graph=True).forward
     wall, kern_ms = time_steps(fn, max(2, args.steps // 10), max(1, args.warmup // 5), torch)
     byts, flops = algorithmic(wl, ranks_of, T)
     return dict(workload=f"{wl.name} prefill, {wl.count} linears, {T} tokens", tokens=T, ms_per_step=kern_ms,
@@ -472,7 +474,7 @@ def main():
         },
         "graph_replay_us_per_step": round(r["graph_ms"] * 1e3, 2),
     }
-    fn = lambda: r["stack"].forward(r["xs"], r["ys"], regime=lb.REGIME_DECODE, use_graph=False)
+    fn = r["stack"].bind(r["xs"], r["ys"], regime=lb.REGIME_DECODE, use_graph=False).forward
     if not args.no_context:
         out["decode_replays"] = {"n": 50, "warm_us": replay_stats(fn, torch, 50),
                                  "cold_us": replay_stats(fn, torch, 50, cold_mb=512), "cold_scratch_mb": 512}

@@ -16,6 +16,7 @@ from ._binding import (  # noqa: F401
     LbPath,
     Linear,
     LittleBitError,
+    BoundStack,
     Stack,
     lib,
     init_dual_svid,

@@ -276,20 +276,16 @@ class Stack:
         n = len(self.linears)
         if len(xs) != n or len(ys) != n:
             raise ValueError("need one x and one y per linear")
-        tokens = xs[0].shape[0]
-        io = _io_of(xs[0], ys[0])
-        if any(_io_of(x, y) != io for x, y in zip(xs, ys)):
-            raise TypeError("every entry of a stack forward must have the same x / y element types")
-        xa = (C.c_void_p * n)(*[x.data_ptr() for x in xs])
-        ya = (C.c_void_p * n)(*[y.data_ptr() for y in ys])
-        if use_graph is None and regime == REGIME_AUTO:
-            _check(lib().lb_stack_forward(self.handle, xa, ya, tokens, io, _stream(stream)))
-        else:
-            if use_graph is None:
-                use_graph = regime == REGIME_EXACT
-            _check(lib().lb_stack_forward_ex(self.handle, xa, ya, tokens, io, regime, 1 if use_graph else 0,
-                                             _stream(stream)))
+        self.bind(xs, ys, regime, use_graph, stream).forward()
         return ys
+
+    def bind(self, xs: Sequence, ys: Sequence, regime: int = REGIME_AUTO, use_graph: Optional[bool] = None,
+             stream=None) -> "BoundStack":
+        """The stack with its inputs, outputs, regime and stream fixed: the
+        returned object's forward() passes the same pointer arrays each call
+        (the per-call marshalling of hundreds of pointers otherwise costs more
+        host time than a decode step takes on the GPU)."""
+        return BoundStack(self, xs, ys, regime, use_graph, stream)
 
     __call__ = forward
 
@@ -303,3 +299,35 @@ class Stack:
             self.close()
         except Exception:
             pass
+
+
+class BoundStack:
+    """A Stack bound to fixed xs / ys (see Stack.bind).  It keeps references to
+    the tensors, so their memory stays valid while it lives."""
+
+    def __init__(self, stack: "Stack", xs: Sequence, ys: Sequence, regime: int, use_graph: Optional[bool], stream):
+        n = len(stack.linears)
+        if len(xs) != n or len(ys) != n:
+            raise ValueError("need one x and one y per linear")
+        pairs = {(x.dtype, y.dtype) for x, y in zip(xs, ys)}
+        if len(pairs) != 1:
+            raise TypeError("every entry of a stack forward must have the same x / y element types")
+        self.stack, self.xs, self.ys = stack, list(xs), list(ys)
+        self.tokens = xs[0].shape[0]
+        self.io = _io_of(xs[0], ys[0])
+        self.xa = (C.c_void_p * n)(*[x.data_ptr() for x in xs])
+        self.ya = (C.c_void_p * n)(*[y.data_ptr() for y in ys])
+        self.regime = regime
+        self.auto = use_graph is None and regime == REGIME_AUTO
+        self.graph = 1 if (regime == REGIME_EXACT if use_graph is None else use_graph) else 0
+        self.stream = _stream(stream)
+
+    def forward(self):
+        if self.auto:
+            _check(lib().lb_stack_forward(self.stack.handle, self.xa, self.ya, self.tokens, self.io, self.stream))
+        else:
+            _check(lib().lb_stack_forward_ex(self.stack.handle, self.xa, self.ya, self.tokens, self.io, self.regime,
+                                             self.graph, self.stream))
+        return self.ys
+
+    __call__ = forward

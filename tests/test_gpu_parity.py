@@ -219,6 +219,28 @@ def test_forward_errors():
     assert info["d_out"] == m and info["d_in"] == n and info["ranks"] == [8, 8] and info["device_bytes"] > 0
 
 
+def test_bound_stack_matches_forward():
+    """Stack.bind fixes the pointer arrays once; its forward() runs the same
+    launches as Stack.forward."""
+    shapes = [(256, 512, [16, 16]), (1024, 300, [33, 20])]
+    lins, paths, xs = make_stack(34, shapes, 3)
+    xt = [x_tensor(x) for x in xs]
+    ya = [torch.empty((3, m), dtype=torch.bfloat16, device="cuda") for (m, _, _) in shapes]
+    yb = [torch.empty_like(y) for y in ya]
+    S = lb.Stack(lins)
+    S.forward(xt, ya, regime=lb.REGIME_DECODE, use_graph=False)
+    bound = S.bind(xt, yb, regime=lb.REGIME_DECODE, use_graph=False)
+    for _ in range(2):
+        bound.forward()
+    torch.cuda.synchronize()
+    for a, b in zip(ya, yb):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    with pytest.raises(TypeError):
+        S.bind(xt, [ya[0].float(), ya[1]])
+    del bound
+    S.close()
+
+
 # ----------------------------------------------------------------------------
 # bf16 x, fp32 y (LB_BF16_FP32)
 # ----------------------------------------------------------------------------
