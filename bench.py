@@ -418,7 +418,7 @@ def main():
                          "reference for the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this build has no multi-GPU path)",
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the library has no multi-GPU path)",
               file=sys.stderr)
         sys.exit(2)
     import torch

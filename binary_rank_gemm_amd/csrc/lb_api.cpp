@@ -627,7 +627,7 @@ lb_status lb_linear_forward_ex(lb_linear L, const void* x, void* y, int64_t toke
     lb_linear one[1] = {L};
     return run_decode(L->plan, one, 1, nullptr, nullptr, x, y, tokens, y_is_fp32(io), st);
   }
-  if (!prefill_available()) return fail(LB_ERR_UNSUPPORTED, "the prefill kernels are not available in this build");
+  if (!prefill_available()) return fail(LB_ERR_UNSUPPORTED, "the prefill kernels are not available in this library");
   const PrefillLayer* one[1] = {&L->pre};
   const void* xs[1] = {x};
   void* ys[1] = {y};
@@ -821,7 +821,7 @@ lb_status stack_prepare(lb_stack S, lb_regime rg, int64_t tokens, lb_dtype io) {
     // (a ragged last slice of a long decode uses another plan shape: those
     // runs launch directly and rebuild the plan per slice)
   } else if (rg == LB_REGIME_PREFILL) {
-    if (!prefill_available()) return fail(LB_ERR_UNSUPPORTED, "the prefill kernels are not available in this build");
+    if (!prefill_available()) return fail(LB_ERR_UNSUPPORTED, "the prefill kernels are not available in this library");
     lb_status s = stack_groups(S, tokens, io);
     if (s != LB_OK) return s;
     for (StackGroup& G : S->groups)

@@ -18,7 +18,7 @@ What it computes (sources are the pages' titles and sections):
 * Same page, section "Residual compensation": the layer's weight is the sum of
   the primary path and a residual path of the same form with its own factors.
 * Same page, "overall framework", and the aibk.xyz article's section on how to
-  judge an ultra-low-bit scheme (its first point, on how bpp is counted): bits per
+  assess an ultra-low-bit scheme (its first point, on how bpp is counted): bits per
   weight is the factorised storage averaged over the original weights.
 
 Readings where the pages are silent (each is listed in the design notes):

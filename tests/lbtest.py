@@ -10,7 +10,7 @@ import numpy as np
 import oracle
 import synth
 
-# bf16 I/O acceptance (reading of the benchmark spec's bound; rounding the exact
+# bf16 I/O acceptance (our reading of the 1e-2 accuracy bound; rounding the exact
 # result to bf16 alone exceeds 1e-2 * rms when max|y| / rms(y) > ~2.6):
 #   (i)  rms(y - y_ref) <= 1e-2 * rms(y_ref)
 #   (ii) max|y - y_ref| <= 1e-2 * rms(y_ref) + 2^-7 * max|y_ref|
