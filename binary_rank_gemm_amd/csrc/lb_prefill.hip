@@ -640,19 +640,24 @@ bool prefill_available() { return true; }
 
 namespace {
 
-// Tiles of one (entry, row stripe) go to one XCD (workgroup b runs on XCD b % 8),
-// stripes balanced over the XCDs by tile count.
-std::vector<PreItem> xcd_order(const std::vector<std::vector<PreItem>>& stripes) {
+// Tiles of one (entry, row stripe) go to one XCD (workgroup b runs on XCD b % 8).
+// Stripes are balanced over the XCDs by work (tiles x K blocks per tile),
+// heaviest first, so each XCD's list starts with its longest tiles and the
+// launch ends on short ones.
+std::vector<PreItem> xcd_order(const std::vector<std::vector<PreItem>>& stripes, const std::vector<double>& kblocks) {
   constexpr int kXcd = 8;
   std::vector<int> order(stripes.size());
   for (size_t i = 0; i < order.size(); ++i) order[i] = (int)i;
-  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return stripes[a].size() > stripes[b].size(); });
+  auto work = [&](int s) { return (double)stripes[s].size() * kblocks[s]; };
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return work(a) > work(b); });
   std::vector<std::vector<PreItem>> per(kXcd);
+  std::vector<double> load(kXcd, 0.0);
   for (int s : order) {
     int best = 0;
     for (int x = 1; x < kXcd; ++x)
-      if (per[x].size() < per[best].size()) best = x;
+      if (load[x] < load[best]) best = x;
     per[best].insert(per[best].end(), stripes[s].begin(), stripes[s].end());
+    load[best] += work(s);
   }
   size_t len = 0;
   for (auto& v : per) len = std::max(len, v.size());
@@ -668,6 +673,7 @@ hipError_t prefill_prepare(PrefillPlan& P, const PrefillLayer* const* layers, in
                            const void* const* xs, void* const* ys) {
   const int mts = (T + kPreBM - 1) / kPreBM;
   std::vector<std::vector<PreItem>> s1, s2;
+  std::vector<double> k1, k2;   // K blocks per tile of each stripe
   size_t zoff = 0;
   std::vector<size_t> zoffs(count);
   P.entries_h.assign(count, PreEntry{});
@@ -683,9 +689,11 @@ hipError_t prefill_prepare(PrefillPlan& P, const PrefillLayer* const* layers, in
       for (int nt = 0; nt < nt2; ++nt) b.push_back(PreItem{e, mt, nt, 0});
       s1.push_back(a);
       s2.push_back(b);
+      k1.push_back(L.kb1);
+      k2.push_back(L.kb2);
     }
   }
-  std::vector<PreItem> i1 = xcd_order(s1), i2 = xcd_order(s2);
+  std::vector<PreItem> i1 = xcd_order(s1, k1), i2 = xcd_order(s2, k2);
   if (zoff > P.zbytes) {
     if (P.zbuf) {
       hipError_t e = hipFree(P.zbuf);
