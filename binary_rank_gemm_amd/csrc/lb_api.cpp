@@ -609,10 +609,10 @@ lb_status lb_linear_forward_ex(lb_linear L, const void* x, void* y, int64_t toke
   if (L->last_stream != st && L->last_stream) HIP_TRY(hipStreamSynchronize(L->last_stream));
   L->last_stream = st;
   if (rg == LB_REGIME_EXACT) {
-    int rpad = 0;
-    for (int p = 0; p < L->np; ++p) rpad = std::max(rpad, L->paths[p].r);
-    rpad = (rpad + 15) / 16 * 16;
-    const size_t want = (size_t)L->np * tokens * rpad * sizeof(float);
+    int rmax = 0;
+    for (int p = 0; p < L->np; ++p) rmax = std::max(rmax, L->paths[p].r);
+    const int rpad = (rmax + 15) / 16 * 16;
+    const size_t want = exact_scratch_floats(rmax, L->np, tokens, (int)L->n, rpad) * sizeof(float);
     if (want > L->zexact.bytes) {
       HIP_TRY(hipStreamSynchronize(st));
       HIP_TRY(L->zexact.ensure(want));
@@ -738,12 +738,12 @@ lb_status stack_launch(lb_stack S, lb_regime rg, int64_t tokens, lb_dtype io, hi
   size_t off = 0;
   for (int i = 0; i < count; ++i) {
     lb_linear L = S->linears[i];
-    int rpad = 0;
-    for (int p = 0; p < L->np; ++p) rpad = std::max(rpad, L->paths[p].r);
-    rpad = (rpad + 15) / 16 * 16;
+    int rmax = 0;
+    for (int p = 0; p < L->np; ++p) rmax = std::max(rmax, L->paths[p].r);
+    const int rpad = (rmax + 15) / 16 * 16;
     HIP_TRY(launch_exact(L->paths, L->np, (int)L->m, (int)L->n, S->xs_h[i], S->ys_h[i], (int)tokens, x_is_fp32(io),
                          y_is_fp32(io), reinterpret_cast<float*>(S->zexact.ptr) + off, rpad, st));
-    off += (size_t)L->np * tokens * rpad;
+    off += exact_scratch_floats(rmax, L->np, tokens, (int)L->n, rpad);
   }
   return LB_OK;
 }
@@ -829,9 +829,9 @@ lb_status stack_prepare(lb_stack S, lb_regime rg, int64_t tokens, lb_dtype io) {
   } else {
     size_t want = 0;
     for (lb_linear L : S->linears) {
-      int rpad = 0;
-      for (int p = 0; p < L->np; ++p) rpad = std::max(rpad, L->paths[p].r);
-      want += (size_t)L->np * tokens * ((rpad + 15) / 16 * 16);
+      int rmax = 0;
+      for (int p = 0; p < L->np; ++p) rmax = std::max(rmax, L->paths[p].r);
+      want += exact_scratch_floats(rmax, L->np, tokens, (int)L->n, (rmax + 15) / 16 * 16);
     }
     HIP_TRY(S->zexact.ensure(std::max<size_t>(want, 1) * sizeof(float)));
   }

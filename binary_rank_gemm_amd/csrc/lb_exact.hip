@@ -34,22 +34,27 @@ struct ExactArgs {
   const void* x;
   void* y;
   float* zbuf;
-  int np, m, n, T, rpad, x_fp32, y_fp32, t0;
+  int np, m, n, T, rpad, x_fp32, y_fp32, t0, splits;
 };
 
-// grid (ceil(r_max/64), np, T), block 256: lane -> latent column j, wave -> row phase.
+// grid (ceil(r_max/64), np, tokens x splits), block 256: lane -> latent
+// column j, wave -> row phase; split s sums rows [n s / S, n (s + 1) / S)
+// (S > 1 only when tokens are few: more workgroups for the same work).
+// Writes the split's sum of (x o g) V for column j; l is applied when the
+// splits are added, in split order, by k_exact_y.
 __global__ void __launch_bounds__(256) k_exact_z(ExactArgs a) {
-  const int p = blockIdx.y, t = a.t0 + (int)blockIdx.z;
+  const int p = blockIdx.y, t = a.t0 + (int)blockIdx.z / a.splits, sp = (int)blockIdx.z % a.splits;
   const PathDev P = a.p[p];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = blockIdx.x * 64 + lane;
+  const int k0 = (int)((int64_t)a.n * sp / a.splits), k1 = (int)((int64_t)a.n * (sp + 1) / a.splits);
   __shared__ float part[4][64];
   float acc = 0.f;
   if (j < P.r) {
     float blk = 0.f;
     int cnt = 0;
     const int64_t xo = (int64_t)t * a.n;
-    for (int k = wave; k < a.n; k += 4) {
+    for (int k = k0 + wave; k < k1; k += 4) {
       float tv = ld_act(a.x, xo + k, a.x_fp32) * f16(P.g, k);
       uint32_t bit = (P.v_can[(int64_t)k * P.W + (j >> 5)] >> (j & 31)) & 1u;
       blk += bit ? -tv : tv;
@@ -60,8 +65,8 @@ __global__ void __launch_bounds__(256) k_exact_z(ExactArgs a) {
   part[wave][lane] = acc;
   __syncthreads();
   if (wave == 0 && j < P.r) {
-    float z = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
-    a.zbuf[((int64_t)p * a.T + t) * a.rpad + j] = z * f16(P.l, j);
+    const float z = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
+    a.zbuf[(((int64_t)sp * a.np + p) * a.T + t) * a.rpad + j] = z;
   }
 }
 
@@ -71,8 +76,11 @@ __global__ void __launch_bounds__(256) k_exact_y(ExactArgs a) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   extern __shared__ float zs[];  // [np][rpad]
   for (int p = 0; p < a.np; ++p)
-    for (int j = threadIdx.x; j < a.p[p].r; j += 256)
-      zs[p * a.rpad + j] = a.zbuf[((int64_t)p * a.T + t) * a.rpad + j];
+    for (int j = threadIdx.x; j < a.p[p].r; j += 256) {
+      float z = 0.f;
+      for (int sp = 0; sp < a.splits; ++sp) z += a.zbuf[(((int64_t)sp * a.np + p) * a.T + t) * a.rpad + j];
+      zs[p * a.rpad + j] = z * f16(a.p[p].l, j);
+    }
   __syncthreads();
   if (i >= a.m) return;
   float y = 0.f;
@@ -107,11 +115,13 @@ hipError_t launch_exact(const PathDev* p, int np, int m, int n, const void* x, v
   a.y_fp32 = y_fp32;
   int rmax = 0;
   for (int i = 0; i < np; ++i) rmax = rmax > p[i].r ? rmax : p[i].r;
+  a.splits = exact_splits(rmax, np, T, n);
   const int kMaxY = 65535;  // grid y/z extent limit: tokens go in slices
-  for (int t0 = 0; t0 < T; t0 += kMaxY) {
+  const int kMaxZ = kMaxY / a.splits;
+  for (int t0 = 0; t0 < T; t0 += kMaxZ) {
     a.t0 = t0;
-    int tn = T - t0 < kMaxY ? T - t0 : kMaxY;
-    hipLaunchKernelGGL(k_exact_z, dim3((rmax + 63) / 64, np, tn), dim3(256), 0, st, a);
+    int tn = T - t0 < kMaxZ ? T - t0 : kMaxZ;
+    hipLaunchKernelGGL(k_exact_z, dim3((rmax + 63) / 64, np, tn * a.splits), dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -151,6 +151,20 @@ hipError_t launch_unpack_signs(const uint32_t* w, int64_t rows, int64_t rank, in
 hipError_t launch_retile_v_decode(const uint32_t* vcan, int n, int r, uint32_t* vdec, hipStream_t st);
 
 // fp32 exact path: z' then y, one linear
+// K splits of the exact path's z stage: when tokens are few, the rows of V
+// are cut into up to 64 ranges (at least 256 rows each) so the launch has
+// about 512 workgroups.
+inline int exact_splits(int rmax, int np, int64_t T, int n) {
+  const int64_t blocks = (int64_t)((rmax + 63) / 64) * np * T;
+  if (blocks >= 512) return 1;
+  const int64_t want = (512 + blocks - 1) / blocks;
+  const int64_t most = n / 256 < 1 ? 1 : (n / 256 > 64 ? 64 : n / 256);
+  return (int)(want < most ? want : most);
+}
+// Floats of z scratch the exact path needs for one linear: splits x np x T x rpad.
+inline size_t exact_scratch_floats(int rmax, int np, int64_t T, int n, int rpad) {
+  return (size_t)exact_splits(rmax, np, T, n) * np * T * rpad;
+}
 hipError_t launch_exact(const PathDev* p, int np, int m, int n, const void* x, void* y, int T,
                         int x_fp32, int y_fp32, float* zbuf, int rpad, hipStream_t st);
 
