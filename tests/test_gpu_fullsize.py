@@ -78,3 +78,39 @@ def test_full_size_layers_sampled(name, T, regime, layers):
         st = assert_bf16_close(got, ref, f"{name} layer {l} {s.name} T={T}")
         log(f"  layer {l} {s.name:5s} {s.m}x{s.n} r={p[0]['rank']}: E_rms {st['erms']:.2e} "
             f"E_max/rms {st['emax_rel_rms']:.2e}")
+
+
+def test_full_70b_stack_decode_as_benchmarked():
+    """The whole Llama-2-70B-shaped stack (80 layers, 560 linears) at batch 1,
+    run exactly as the benchmark times it: one stack, bound to its buffers,
+    three direct launches per step (so the work items are those of the
+    timed configuration, not of a smaller stack).  Sampled output channels of
+    three layers' linears are checked against the oracle."""
+    wl = synth.WORKLOADS["llama2-70b-0.1bpw"]
+    T = 1
+    rk = [ranks(wl, s) for s in wl.mats]
+    lins, xs, ys, keep = [], [], [], {}
+    check_layers = (0, 40, 79)
+    for l in range(wl.layers):
+        for j, s in enumerate(wl.mats):
+            p = synth.layer_tensors(wl.wid, l, j, s.m, s.n, rk[j])
+            x = synth.layer_activations(wl, l, j, s.n, T, io="bf16")
+            lins.append(lb.Linear.from_numpy(s.m, s.n, p))
+            xs.append(x_tensor(x))
+            ys.append(torch.empty((T, s.m), dtype=torch.bfloat16, device="cuda"))
+            if l in check_layers:
+                keep[len(lins) - 1] = (l, s, p, x)
+    log(f"70B stack: {len(lins)} linears")
+    S = lb.Stack(lins)
+    step = S.bind(xs, ys, regime=lb.REGIME_DECODE, use_graph=False)
+    for _ in range(3):
+        step.forward()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5601)
+    for i, (l, s, p, x) in keep.items():
+        rows = np.sort(rng.choice(s.m, size=min(SAMPLE_ROWS, s.m), replace=False))
+        ref = oracle.forward_rows(x_f64(x), p, s.m, s.n, rows)
+        st = assert_bf16_close(to_f64(ys[i])[:, rows], ref, f"70B stack layer {l} {s.name}")
+        log(f"  layer {l} {s.name:5s}: E_rms {st['erms']:.2e} E_max/rms {st['emax_rel_rms']:.2e}")
+    del step
+    S.close()
