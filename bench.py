@@ -438,7 +438,9 @@ def main():
         log(f"copy probe: {nb} bytes read + {nb} bytes written")
 
     if args.prefill_only:
-        p = run_prefill(args, lb, torch, "llama2-13b-prefill-t2048")
+        # a prefill workload named by --workload, else the 13B stack at 2048 tokens
+        wk = args.workload if WORKLOADS[args.workload][2] == "prefill" else "llama2-13b-prefill-t2048"
+        p = run_prefill(args, lb, torch, wk)
         log(f"prefill: {p['ms_per_step']:.2f} ms/step, {p['tflops']:.0f} TFLOP/s")
         print(json.dumps({"prefill": p}), flush=True)
         return
