@@ -238,9 +238,13 @@ lb_status build_decode_plan(DecodePlan& P, const lb_linear* L, int count, int T,
   std::vector<size_t> img_off(count), cv_off(count);
   int slots = 0;
   // Item sizes: about 192 KB of sign words per item when the launch has
-  // plenty of work; a launch with little (one level of a chained stack) is
-  // cut finer, aiming at ~1024 items, so that its latency is that of a small
-  // item rather than of a few large ones.
+  // plenty of work; a launch with less is cut into about one item per
+  // workgroup slot of the GPU (CUs x workgroups per CU), so that it runs as
+  // one wave of items and its latency is that of one item (16 KB at least).
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, L[0]->device) != hipSuccess || cus <= 0)
+    cus = 256;
+  const double slots_per_launch = (double)cus * (bucket >= 16 ? 2 : 3);
   double vtotal = 0, utotal = 0;
   for (int e = 0; e < count; ++e) {
     const int nkc = (int)((L[e]->n + kChunk - 1) / kChunk);
@@ -248,8 +252,8 @@ lb_status build_decode_plan(DecodePlan& P, const lb_linear* L, int count, int T,
     utotal += (double)L[e]->ug.nq * (L[e]->ug.qbytes + 256.0);
   }
   constexpr double kMinItemBytes = 16 * 1024;
-  const double vtarget = std::min<double>(kDecodeVItemBytes, std::max(kMinItemBytes, vtotal / 1024));
-  const double utarget = std::min<double>(kDecodeUItemBytes, std::max(kMinItemBytes, utotal / 1024));
+  const double vtarget = std::min<double>(kDecodeVItemBytes, std::max(kMinItemBytes, vtotal / slots_per_launch));
+  const double utarget = std::min<double>(kDecodeUItemBytes, std::max(kMinItemBytes, utotal / slots_per_launch));
   for (int e = 0; e < count; ++e) {
     const lb_linear l = L[e];
     DecEntry& E = P.entries_h[e];
