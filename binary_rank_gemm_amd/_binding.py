@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(HERE, "liblittlebit.so")
 OK, INVALID_ARGUMENT, INVALID_SIGN, ALIGNMENT, UNSUPPORTED, OUT_OF_MEMORY, HIP_ERROR = range(7)
 BF16, FP32, BF16_FP32 = 0, 1, 2   # lb_dtype: element types of (x, y)
 REGIME_AUTO, REGIME_EXACT, REGIME_DECODE, REGIME_PREFILL = 0, 1, 2, 3
-PREFILL_MIN_TOKENS = 128
+PREFILL_MIN_TOKENS = 64   # LB_PREFILL_MIN_TOKENS
 
 STATUS_NAMES = {OK: "LB_OK", INVALID_ARGUMENT: "LB_ERR_INVALID_ARGUMENT", INVALID_SIGN: "LB_ERR_INVALID_SIGN",
                 ALIGNMENT: "LB_ERR_ALIGNMENT", UNSUPPORTED: "LB_ERR_UNSUPPORTED",

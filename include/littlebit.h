@@ -70,7 +70,11 @@ typedef enum { LB_BF16 = 0, LB_FP32 = 1, LB_BF16_FP32 = 2 } lb_dtype;
 typedef enum { LB_REGIME_AUTO = 0, LB_REGIME_EXACT = 1, LB_REGIME_DECODE = 2,
                LB_REGIME_PREFILL = 3 } lb_regime;
 
-#define LB_PREFILL_MIN_TOKENS 128
+/* From this many tokens AUTO runs the prefill GEMMs (256-row tiles, so their
+ * time is flat below 256 tokens) instead of 16-token decode slices: the two
+ * cross near 50 tokens on a 0.55-bit-per-weight Llama-2-13B stack and near 90
+ * on a 0.1-bit-per-weight Llama-2-70B stack. */
+#define LB_PREFILL_MIN_TOKENS 64
 
 /* Limits (LB_ERR_UNSUPPORTED beyond them). */
 #define LB_MAX_DIM    (1 << 20)   /* d_in, d_out                */

@@ -123,6 +123,11 @@ def test_argument_validation_before_any_device_work():
     assert L.lb_init_dual_svid(dummy, 8, 8, nul, 1, None) == lb._binding.INVALID_ARGUMENT
 
 
+def test_binding_constants_match_header():
+    hdr = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "littlebit.h")).read()
+    assert int(re.search(r"#define LB_PREFILL_MIN_TOKENS (\d+)", hdr).group(1)) == lb.PREFILL_MIN_TOKENS
+
+
 def test_binding_io_types():
     """The binding's lb_dtype of an (x, y) pair; other pairs are refused."""
     torch = pytest.importorskip("torch")
