@@ -47,8 +47,8 @@ struct PrefillPlan {
   int T = -1;
   int count = 0;
   PreEntry* entries_d = nullptr;
-  PreItem* items_d = nullptr;       // GEMM1 items, then GEMM2 items
-  int n1 = 0, n2 = 0;
+  PreItem* items_d = nullptr;       // GEMM1 items (full row stripes, then the partial one), then GEMM2's
+  int n1 = 0, n1p = 0, n2 = 0, n2p = 0;
   void* zbuf = nullptr;
   size_t zbytes = 0;
   std::vector<PreEntry> entries_h;

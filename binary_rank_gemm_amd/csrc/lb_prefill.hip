@@ -215,8 +215,10 @@ __device__ inline int a_slot_chunk(int s) { return (s & 7) ^ ((s >> 3) & 7); }
 // Wave layout of the 256 x 256 workgroup tile: WM x WN waves, each owning
 // (256 / WM) x (256 / WN) outputs as MB x NB blocks of 32 x 32.  STR (GEMM1
 // only): some wave's columns cross from the primary path into the residual
-// one, so |g| is chosen per column block.
-template <int MODE, int WM, int WN, bool STR>
+// one, so |g| is chosen per column block.  PART: the tile's rows run past the
+// last token (the last row stripe when T is not a multiple of 256); each wave
+// then reads and multiplies only its 32-row blocks that hold tokens.
+template <int MODE, int WM, int WN, bool STR, bool PART>
 __device__ __forceinline__ void prefill_tile(const PreArgs& a, const PreItem& it) {
   constexpr int kWaves = WM * WN, kNT = 64 * kWaves;
   constexpr int MB = kPreBM / WM / 32, NB = kPreBN / WN / 32;
@@ -249,6 +251,12 @@ __device__ __forceinline__ void prefill_tile(const PreArgs& a, const PreItem& it
   const int m0 = it.mt * kPreBM, n0 = it.nt * kPreBN;
   const int l32 = lane & 31, kg = lane >> 5;
   const int wcol = wn * (NB * 32);                       // first column of this wave in the tile
+  // row blocks of this wave that hold tokens (all of them unless PART)
+  int mba = MB;
+  if constexpr (PART) {
+    const int live = T - (m0 + wm * MB * 32);
+    mba = __builtin_amdgcn_readfirstlane(live <= 0 ? 0 : min(MB, (live + 31) / 32));
+  }
   const int bb0 = (wcol & (kPreWN - 1)) / 32;            // first 32-column block inside its B tile
   const bool vec_ok = (lda & 7) == 0;
   const int nkb = (K + kPreBK - 1) / kPreBK;
@@ -310,7 +318,8 @@ __device__ __forceinline__ void prefill_tile(const PreArgs& a, const PreItem& it
   auto read_a = [&](int buf, int ks, u32x4* af) {
     const uint8_t* Ab = lds + buf * kBuf + aoff[ks];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) af[mb] = *reinterpret_cast<const u32x4*>(Ab + mb * 32 * 128);
+    for (int mb = 0; mb < MB; ++mb)
+      if (!PART || mb < mba) af[mb] = *reinterpret_cast<const u32x4*>(Ab + mb * 32 * 128);
   };
   const int bsel = wcol / kPreWN;                        // which of the two B tiles
   auto read_b = [&](int buf) { return reinterpret_cast<const u32x4*>(lds + buf * kBuf + kBufA)[bsel * 64 + lane]; };
@@ -414,7 +423,8 @@ __device__ __forceinline__ void prefill_tile(const PreArgs& a, const PreItem& it
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) acc[mb][b] = mfma32(bf[ks & 1][b], af[ks & 1][mb], acc[mb][b]);
+        for (int mb = 0; mb < MB; ++mb)
+          if (!PART || mb < mba) acc[mb][b] = mfma32(bf[ks & 1][b], af[ks & 1][mb], acc[mb][b]);
     }
     bw = bwn;
     if (more) vm_wait_barrier<kAI>();
@@ -528,15 +538,17 @@ __device__ __forceinline__ void prefill_tile(const PreArgs& a, const PreItem& it
 
 // One workgroup per tile; GEMM1 tiles where a wave's columns reach into both
 // paths take the body that picks |g| per column block.
-template <int MODE, int WM, int WN>
+// PART: a launch over the tiles of row stripes that run past the last token
+// (a separate launch, so the full tiles' kernel carries none of it).
+template <int MODE, int WM, int WN, bool PART>
 __global__ void __launch_bounds__(64 * WM * WN, 1) k_prefill(PreArgs a) {
   const PreItem it = a.items[blockIdx.x];
   if (it.entry < 0) return;
   if constexpr (MODE == 1) {
-    if (it.str) prefill_tile<1, WM, WN, true>(a, it);
-    else prefill_tile<1, WM, WN, false>(a, it);
+    if (it.str) prefill_tile<1, WM, WN, true, PART>(a, it);
+    else prefill_tile<1, WM, WN, false, PART>(a, it);
   } else {
-    prefill_tile<2, WM, WN, false>(a, it);
+    prefill_tile<2, WM, WN, false, PART>(a, it);
   }
 }
 
@@ -672,8 +684,8 @@ std::vector<PreItem> xcd_order(const std::vector<std::vector<PreItem>>& stripes,
 hipError_t prefill_prepare(PrefillPlan& P, const PrefillLayer* const* layers, int count, int T,
                            const void* const* xs, void* const* ys) {
   const int mts = (T + kPreBM - 1) / kPreBM;
-  std::vector<std::vector<PreItem>> s1, s2;
-  std::vector<double> k1, k2;   // K blocks per tile of each stripe
+  std::vector<std::vector<PreItem>> s1, s2, s1p, s2p;   // full row stripes, stripes past the last token
+  std::vector<double> k1, k2, k1p, k2p;                  // K blocks per tile of each stripe
   size_t zoff = 0;
   std::vector<size_t> zoffs(count);
   P.entries_h.assign(count, PreEntry{});
@@ -687,13 +699,15 @@ hipError_t prefill_prepare(PrefillPlan& P, const PrefillLayer* const* layers, in
       std::vector<PreItem> a, b;
       for (int nt = 0; nt < nt1; ++nt) a.push_back(PreItem{e, mt, nt, tile_straddles(L, nt) ? 1 : 0});
       for (int nt = 0; nt < nt2; ++nt) b.push_back(PreItem{e, mt, nt, 0});
-      s1.push_back(a);
-      s2.push_back(b);
-      k1.push_back(L.kb1);
-      k2.push_back(L.kb2);
+      const bool part = (mt + 1) * kPreBM > T;
+      (part ? s1p : s1).push_back(a);
+      (part ? s2p : s2).push_back(b);
+      (part ? k1p : k1).push_back(L.kb1);
+      (part ? k2p : k2).push_back(L.kb2);
     }
   }
   std::vector<PreItem> i1 = xcd_order(s1, k1), i2 = xcd_order(s2, k2);
+  std::vector<PreItem> i1p = xcd_order(s1p, k1p), i2p = xcd_order(s2p, k2p);
   if (zoff > P.zbytes) {
     if (P.zbuf) {
       hipError_t e = hipFree(P.zbuf);
@@ -715,14 +729,21 @@ hipError_t prefill_prepare(PrefillPlan& P, const PrefillLayer* const* layers, in
   P.entries_d = nullptr;
   P.items_d = nullptr;
   hipError_t e = hipMalloc(&P.entries_d, count * sizeof(PreEntry));
-  if (e == hipSuccess) e = hipMalloc(&P.items_d, (i1.size() + i2.size()) * sizeof(PreItem));
+  if (e == hipSuccess)
+    e = hipMalloc(&P.items_d, std::max<size_t>(1, i1.size() + i1p.size() + i2.size() + i2p.size()) * sizeof(PreItem));
   if (e == hipSuccess) e = hipMemcpy(P.entries_d, P.entries_h.data(), count * sizeof(PreEntry), hipMemcpyHostToDevice);
   if (e != hipSuccess) return e;
   std::vector<PreItem> all(i1);
+  all.insert(all.end(), i1p.begin(), i1p.end());
   all.insert(all.end(), i2.begin(), i2.end());
-  if ((e = hipMemcpy(P.items_d, all.data(), all.size() * sizeof(PreItem), hipMemcpyHostToDevice)) != hipSuccess) return e;
+  all.insert(all.end(), i2p.begin(), i2p.end());
+  if (!all.empty() &&
+      (e = hipMemcpy(P.items_d, all.data(), all.size() * sizeof(PreItem), hipMemcpyHostToDevice)) != hipSuccess)
+    return e;
   P.n1 = (int)i1.size();
+  P.n1p = (int)i1p.size();
   P.n2 = (int)i2.size();
+  P.n2p = (int)i2p.size();
   P.T = T;
   P.count = count;
   return hipSuccess;
@@ -749,12 +770,20 @@ hipError_t prefill_run(PrefillPlan& P, const PrefillLayer* const* layers, int co
   }
   a.entries = P.entries_d;
   a.T = T;
+  // GEMM1 over the full row stripes, then over the stripe past the last token;
+  // the same for GEMM2
   a.items = P.items_d;
-  if (P.n1 > 0) hipLaunchKernelGGL((k_prefill<1, kPreWM, kPreWNv>), dim3(P.n1), dim3(kThreads), kPreLds, st, a);
+  if (P.n1 > 0) hipLaunchKernelGGL((k_prefill<1, kPreWM, kPreWNv, false>), dim3(P.n1), dim3(kThreads), kPreLds, st, a);
+  a.items = P.items_d + P.n1;
+  if (P.n1p > 0) hipLaunchKernelGGL((k_prefill<1, kPreWM, kPreWNv, true>), dim3(P.n1p), dim3(kThreads), kPreLds, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  a.items = P.items_d + P.n1;
-  hipLaunchKernelGGL((k_prefill<2, kPreWM, kPreWNv>), dim3(P.n2), dim3(kThreads), kPreLds, st, a);
+  a.items = P.items_d + P.n1 + P.n1p;
+  if (P.n2 > 0) hipLaunchKernelGGL((k_prefill<2, kPreWM, kPreWNv, false>), dim3(P.n2), dim3(kThreads), kPreLds, st, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  a.items = P.items_d + P.n1 + P.n1p + P.n2;
+  if (P.n2p > 0) hipLaunchKernelGGL((k_prefill<2, kPreWM, kPreWNv, true>), dim3(P.n2p), dim3(kThreads), kPreLds, st, a);
   return hipGetLastError();
 }
 
