@@ -23,7 +23,6 @@ from ._binding import (  # noqa: F401
     pack_signs,
     pack_signs_host,
     packed_words_per_row,
-    probe_stream_read,
     rank_for_bpw,
     unpack_signs,
 )

@@ -25,12 +25,13 @@ STATUS_NAMES = {OK: "LB_OK", INVALID_ARGUMENT: "LB_ERR_INVALID_ARGUMENT", INVALI
                 ALIGNMENT: "LB_ERR_ALIGNMENT", UNSUPPORTED: "LB_ERR_UNSUPPORTED",
                 OUT_OF_MEMORY: "LB_ERR_OUT_OF_MEMORY", HIP_ERROR: "LB_ERR_HIP"}
 
-# every symbol include/littlebit.h declares
+# every symbol include/littlebit.h declares (the measurement probe of
+# include/littlebit_probe.h is bound in probe.py)
 EXPORTS = [
     "lb_packed_words_per_row", "lb_rank_for_bpw", "lb_pack_signs_host", "lb_pack_signs", "lb_unpack_signs",
     "lb_linear_create", "lb_linear_forward", "lb_linear_forward_ex", "lb_linear_info", "lb_linear_destroy",
     "lb_stack_create", "lb_stack_forward", "lb_stack_forward_ex", "lb_stack_destroy", "lb_status_string",
-    "lb_last_error", "lb_probe_stream_read", "lb_init_dual_svid",
+    "lb_last_error", "lb_init_dual_svid",
 ]
 
 
@@ -80,7 +81,6 @@ def lib():
         "lb_stack_destroy": (C.c_int, [vp]),
         "lb_status_string": (C.c_char_p, [C.c_int]),
         "lb_last_error": (C.c_char_p, []),
-        "lb_probe_stream_read": (C.c_int, [vp, i64, vp]),
         "lb_init_dual_svid": (C.c_int, [vp, i64, i64, vp, i32, vp]),
     }
     for name, (res, args) in sig.items():
@@ -162,12 +162,6 @@ def init_dual_svid(W, ranks: Sequence[int], stream=None) -> List[Dict]:
     return paths
 
 
-def probe_stream_read(buf, stream=None) -> None:
-    """Enqueue lb_probe_stream_read over a device tensor (a measurement aid)."""
-    _check(lib().lb_probe_stream_read(C.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(),
-                                      _stream(stream)))
-
-
 def _io_of(x, y) -> int:
     """lb_dtype of an (x, y) pair: both bf16, both fp32, or bf16 x with fp32 y."""
     import torch
@@ -237,10 +231,14 @@ class Linear:
             raise ValueError(f"x must be [tokens, {self.d_in}]")
         if not x.is_contiguous():
             raise ValueError("x must be contiguous")
+        if not x.is_cuda:
+            raise ValueError("x must be a device tensor")
         if y is None:
             y = torch.empty((x.shape[0], self.d_out), dtype=out_dtype or x.dtype, device=x.device)
         if y.dim() != 2 or tuple(y.shape) != (x.shape[0], self.d_out) or not y.is_contiguous():
             raise ValueError(f"y must be a contiguous [{x.shape[0]}, {self.d_out}] tensor")
+        if y.device != x.device:
+            raise ValueError("x and y must be on the same device")
         _check(lib().lb_linear_forward_ex(self.handle, x.data_ptr(), y.data_ptr(), x.shape[0], _io_of(x, y), regime,
                                           _stream(stream)))
         return y
@@ -312,8 +310,22 @@ class BoundStack:
         pairs = {(x.dtype, y.dtype) for x, y in zip(xs, ys)}
         if len(pairs) != 1:
             raise TypeError("every entry of a stack forward must have the same x / y element types")
+        tokens = int(xs[0].shape[0]) if xs[0].dim() == 2 else -1
+        dev = xs[0].device
+        # the library cannot see tensor shapes: a wrong-sized entry would be
+        # read and written out of bounds on the device, so check each one here
+        for i, (lin, x, y) in enumerate(zip(stack.linears, xs, ys)):
+            if x.dim() != 2 or tuple(x.shape) != (tokens, lin.d_in):
+                raise ValueError(f"entry {i}: x must be [{tokens}, {lin.d_in}], got {tuple(x.shape)}")
+            if y.dim() != 2 or tuple(y.shape) != (tokens, lin.d_out):
+                raise ValueError(f"entry {i}: y must be [{tokens}, {lin.d_out}], got {tuple(y.shape)}")
+            if not x.is_contiguous() or not y.is_contiguous():
+                raise ValueError(f"entry {i}: x and y must be contiguous")
+        for i, (x, y) in enumerate(zip(xs, ys)):
+            if not x.is_cuda or x.device != dev or y.device != dev:
+                raise ValueError(f"entry {i}: every x and y must be on the same device ({dev})")
         self.stack, self.xs, self.ys = stack, list(xs), list(ys)
-        self.tokens = xs[0].shape[0]
+        self.tokens = tokens
         self.io = _io_of(xs[0], ys[0])
         self.xa = (C.c_void_p * n)(*[x.data_ptr() for x in xs])
         self.ya = (C.c_void_p * n)(*[y.data_ptr() for y in ys])

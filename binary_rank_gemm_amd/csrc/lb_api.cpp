@@ -13,6 +13,7 @@
 
 #include "lb_internal.h"
 #include "lb_prefill.h"
+#include "littlebit_probe.h"
 
 using namespace lb;
 
@@ -229,6 +230,10 @@ hipError_t upload(Item** dst, const std::vector<Item>& v) {
 //   U items: runs of 4 qw quads, qw quads per wave, about kDecodeUItemBytes.
 lb_status build_decode_plan(DecodePlan& P, const lb_linear* L, int count, int T, const DecodeImage* img = nullptr) {
   if (P.T == T && P.count == count) return LB_OK;
+  // the buffers and tables below are freed and reallocated: until every step
+  // has succeeded the plan must not look valid for any token count
+  P.T = -1;
+  P.count = 0;
   const int bucket = decode_bucket(T), tb = (bucket + 7) / 8, ct_max = decode_v_tiles(bucket);
   P.entries_h.assign(count, DecEntry{});
   std::vector<std::pair<double, VItem>> vl;
@@ -866,14 +871,30 @@ lb_status lb_stack_forward_ex(lb_stack S, const void* const* xs, void* const* ys
     // everything below rewrites memory earlier launches read: wait for them
     if (S->last_stream) HIP_TRY(hipStreamSynchronize(S->last_stream));
     HIP_TRY(hipStreamSynchronize(st));
+    // The old plans and graph go first, and the stack records what it was
+    // prepared for only once the new plans exist: a failed call (an entry
+    // whose y overlaps its own x, an allocation failure) leaves a stack that
+    // matches no pointers, so a retry is checked again instead of replaying
+    // launches that write into the previous call's buffers.
+    S->g_tokens = -1;
+    S->g_io = -1;
+    S->g_regime = -1;
+    if (S->exec) (void)hipGraphExecDestroy(S->exec);
+    if (S->graph) (void)hipGraphDestroy(S->graph);
+    S->exec = nullptr;
+    S->graph = nullptr;
+    for (StackGroup& G : S->groups) G.release();
+    S->groups.clear();
     S->xs_h.assign(xs, xs + count);
     S->ys_h.assign(ys, ys + count);
     s = stack_prepare(S, rg, tokens, io);
-    if (s != LB_OK) return s;
-    if (S->exec) HIP_TRY(hipGraphExecDestroy(S->exec));
-    if (S->graph) HIP_TRY(hipGraphDestroy(S->graph));
-    S->exec = nullptr;
-    S->graph = nullptr;
+    if (s != LB_OK) {
+      for (StackGroup& G : S->groups) G.release();
+      S->groups.clear();
+      S->xs_h.clear();
+      S->ys_h.clear();
+      return s;
+    }
     S->g_tokens = tokens;
     S->g_io = (int)io;
     S->g_regime = (int)rg;

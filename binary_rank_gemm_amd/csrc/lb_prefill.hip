@@ -683,6 +683,10 @@ std::vector<PreItem> xcd_order(const std::vector<std::vector<PreItem>>& stripes,
 
 hipError_t prefill_prepare(PrefillPlan& P, const PrefillLayer* const* layers, int count, int T,
                            const void* const* xs, void* const* ys) {
+  // buffers and tables are rebuilt below: the plan is valid again only once
+  // all of it has succeeded
+  P.T = -1;
+  P.count = 0;
   const int mts = (T + kPreBM - 1) / kPreBM;
   std::vector<std::vector<PreItem>> s1, s2, s1p, s2p;   // full row stripes, stripes past the last token
   std::vector<double> k1, k2, k1p, k2p;                  // K blocks per tile of each stripe

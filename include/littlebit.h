@@ -215,15 +215,6 @@ typedef struct {
 lb_status lb_init_dual_svid(const float* W, int64_t d_out, int64_t d_in, const lb_path_init* paths,
                             int32_t n_paths, void* stream);
 
-/* Measurement aid, not part of the method: enqueues on `stream` one
- * read-only streaming pass over `bytes` bytes of device memory at `buf`
- * (16-byte loads, grid-stride), so that a caller timing it with events gets
- * the HBM read bandwidth plain loads reach on this GPU.  buf must be 16-byte
- * aligned and bytes a positive multiple of 16 (LB_ERR_ALIGNMENT /
- * LB_ERR_INVALID_ARGUMENT otherwise).  Reads only; writes nothing the caller
- * can see. */
-lb_status lb_probe_stream_read(const void* buf, int64_t bytes, void* stream);
-
 #ifdef __cplusplus
 }
 #endif

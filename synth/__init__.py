@@ -18,4 +18,6 @@ from .gen import (  # noqa: F401
     rng_for,
     scales_fp16_bits,
     sign_words,
+    signed_scales_fp16_bits,
+    wide_range_activations,
 )

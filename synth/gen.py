@@ -58,6 +58,34 @@ def scales_fp16_bits(key: Sequence[int], length: int, sigma: float = 0.5) -> np.
     return v.astype(np.float16).view(np.uint16)
 
 
+def signed_scales_fp16_bits(key: Sequence[int], length: int, sigma: float = 0.5,
+                           zero_frac: float = 0.05, subnormal_frac: float = 0.05) -> np.ndarray:
+    """fp16 bit patterns of scales with every sign and the edge values a
+    learned real scale can take: |s| = exp(N(0, sigma^2)) with a random sign,
+    except that about zero_frac of the entries are +0 or -0 and about
+    subnormal_frac are fp16 subnormals (random sign, magnitude 2^-24 .. 2^-15)."""
+    g = rng_for(*key)
+    v = np.exp(g.normal(0.0, sigma, size=length)) * np.where(g.integers(0, 2, size=length) == 1, -1.0, 1.0)
+    bits = v.astype(np.float16).view(np.uint16).copy()
+    kind = g.random(size=length)
+    zero = kind < zero_frac
+    sub = (kind >= zero_frac) & (kind < zero_frac + subnormal_frac)
+    sign = (g.integers(0, 2, size=length).astype(np.uint16) << np.uint16(15))
+    bits[zero] = sign[zero]                                                   # +0 / -0
+    mant = g.integers(1, 1 << 10, size=length).astype(np.uint16)             # exponent field 0: subnormal
+    bits[sub] = sign[sub] | mant[sub]
+    return bits
+
+
+def wide_range_activations(key: Sequence[int], tokens: int, n: int, octaves: int = 12) -> np.ndarray:
+    """bf16 bits of N(0, 1) values each multiplied by 2^-u, u uniform in
+    [0, octaves]: every block of 32 consecutive elements then spans about
+    2^octaves in magnitude."""
+    g = rng_for(*key)
+    x = g.normal(0.0, 1.0, size=(tokens, n)) * np.exp2(-g.uniform(0.0, octaves, size=(tokens, n)))
+    return bf16_bits_from_f32(x.astype(np.float32))
+
+
 def bf16_bits_from_f32(v: np.ndarray) -> np.ndarray:
     """Round float32 values to bf16 (nearest, ties to even); returns uint16 bits."""
     b = np.ascontiguousarray(v, dtype=np.float32).view(np.uint32).astype(np.uint64)

@@ -17,8 +17,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "littlebit.h")
 
 
-def header_functions():
-    text = open(HEADER).read()
+def header_functions(path=HEADER):
+    text = open(path).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(lb_[a-z_]+)\s*\(", text)))
 
@@ -27,9 +27,14 @@ def test_library_exports_every_declared_symbol():
     declared = header_functions()
     assert len(declared) >= 16
     assert sorted(lb.EXPORTS) == declared
+    import binary_rank_gemm_amd.probe as probe
+    assert header_functions(os.path.join(ROOT, "include", "littlebit_probe.h")) == sorted(probe.EXPORTS)
     L = lb.lib()
-    for name in declared:
-        assert hasattr(L, name), name
+    headers = sorted(f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h"))
+    assert "littlebit.h" in headers
+    for h in headers:
+        for name in header_functions(os.path.join(ROOT, "include", h)):
+            assert hasattr(L, name), f"{h}: {name}"
 
 
 def test_status_strings():
@@ -110,9 +115,10 @@ def test_argument_validation_before_any_device_work():
     assert L.lb_pack_signs(None, 1, 1, dummy, None) == lb._binding.INVALID_ARGUMENT
     assert L.lb_unpack_signs(dummy, 0, 1, dummy, None) == lb._binding.INVALID_ARGUMENT
     assert L.lb_packed_words_per_row(0) == 0 and L.lb_packed_words_per_row(32) == 1
-    assert L.lb_probe_stream_read(None, 16, None) == lb._binding.INVALID_ARGUMENT
-    assert L.lb_probe_stream_read(dummy, 0, None) == lb._binding.INVALID_ARGUMENT
-    assert L.lb_probe_stream_read(dummy, 24, None) == lb._binding.INVALID_ARGUMENT
+    import binary_rank_gemm_amd.probe as probe
+    assert probe._fn()(None, 16, None) == lb._binding.INVALID_ARGUMENT
+    assert probe._fn()(dummy, 0, None) == lb._binding.INVALID_ARGUMENT
+    assert probe._fn()(dummy, 24, None) == lb._binding.INVALID_ARGUMENT
     outs = (lb._binding.LbPathInit * 1)(lb._binding.LbPathInit(4, dummy, dummy, dummy, dummy, dummy))
     assert L.lb_init_dual_svid(None, 8, 8, outs, 1, None) == lb._binding.INVALID_ARGUMENT
     assert L.lb_init_dual_svid(dummy, 8, 8, None, 1, None) == lb._binding.INVALID_ARGUMENT
@@ -147,3 +153,28 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(b, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         b.lib()
+
+
+def test_bound_stack_checks_every_entry():
+    """BoundStack refuses entries whose shapes do not match their linear, or
+    that are not contiguous device tensors, before any pointer reaches the
+    library (which cannot see shapes)."""
+    torch = pytest.importorskip("torch")
+    from types import SimpleNamespace
+    fake = SimpleNamespace(linears=[SimpleNamespace(d_in=8, d_out=4), SimpleNamespace(d_in=4, d_out=6)])
+    bf = torch.bfloat16
+    good_x = [torch.zeros(3, 8, dtype=bf), torch.zeros(3, 4, dtype=bf)]
+    good_y = [torch.zeros(3, 4, dtype=bf), torch.zeros(3, 6, dtype=bf)]
+    B = lb._binding.BoundStack
+    with pytest.raises(ValueError, match="entry 1: x"):
+        B(fake, [good_x[0], torch.zeros(3, 5, dtype=bf)], good_y, 0, None, 0)
+    with pytest.raises(ValueError, match="entry 0: y"):
+        B(fake, good_x, [torch.zeros(3, 5, dtype=bf), good_y[1]], 0, None, 0)
+    with pytest.raises(ValueError, match="entry 1: x"):
+        B(fake, [good_x[0], torch.zeros(2, 4, dtype=bf)], good_y, 0, None, 0)   # token counts differ
+    with pytest.raises(ValueError, match="contiguous"):
+        B(fake, [good_x[0], torch.zeros(4, 3, dtype=bf).t()], good_y, 0, None, 0)
+    with pytest.raises(ValueError, match="device"):
+        B(fake, good_x, good_y, 0, None, 0)   # host tensors
+    with pytest.raises(ValueError, match="one x and one y"):
+        B(fake, good_x[:1], good_y, 0, None, 0)

@@ -114,3 +114,29 @@ def test_full_70b_stack_decode_as_benchmarked():
         log(f"  layer {l} {s.name:5s}: E_rms {st['erms']:.2e} E_max/rms {st['emax_rel_rms']:.2e}")
     del step
     S.close()
+
+
+def test_full_70b_layer_t64_auto_all_rows():
+    """One whole layer of the Llama-2-70B-shaped stack (q, k, v, o, gate, up,
+    down at 0.1 BPW) at 64 tokens, run through lb_stack_forward with the
+    regime and launch form the library picks by itself (AUTO), and checked
+    against the oracle on every output of every linear (the oracle rebuilds
+    each W in full)."""
+    wl = synth.WORKLOADS["llama2-70b-0.1bpw"]
+    T, layer = 64, 11
+    entries = []
+    for j, s in enumerate(wl.mats):
+        entries.append((s, synth.layer_tensors(wl.wid, layer, j, s.m, s.n, ranks(wl, s)),
+                        synth.layer_activations(wl, layer, j, s.n, T, io="bf16")))
+    lins = [lb.Linear.from_numpy(s.m, s.n, p) for s, p, _ in entries]
+    S = lb.Stack(lins)
+    xd = [x_tensor(x) for *_, x in entries]
+    ys = [torch.empty((T, s.m), dtype=torch.bfloat16, device="cuda") for s, _, _ in entries]
+    log(f"70B layer {layer}, T={T}, AUTO")
+    S.forward(xd, ys)
+    torch.cuda.synchronize()
+    for (s, p, x), y in zip(entries, ys):
+        ref = oracle.forward(x_f64(x), p, s.m, s.n)
+        st = assert_bf16_close(to_f64(y), ref, f"70B layer {layer} {s.name} T={T} AUTO")
+        log(f"  {s.name:5s} {s.m}x{s.n}: E_rms {st['erms']:.2e} E_max/rms {st['emax_rel_rms']:.2e}")
+    S.close()

@@ -409,13 +409,31 @@ def test_stack_chained_in_model_order(regime, T, io):
             assert torch.equal(runs[0][i].view(bits), ys[i].view(bits)), f"stack != singles, entry {i}"
 
 
-def test_stack_refuses_output_over_own_input():
+@pytest.mark.parametrize("regime", [lb.REGIME_DECODE, lb.REGIME_PREFILL])
+def test_stack_refuses_output_over_own_input(regime):
+    """An entry whose y overlaps its own x is refused, also when the same bad
+    call is repeated (a failed call must not leave the stack looking prepared
+    for those pointers); a valid call at the same token count afterwards runs
+    and matches the oracle, and a retry of the bad call is refused again."""
     m = n = 256
+    T = 4 if regime == lb.REGIME_DECODE else 200
     p = seeded_paths((32, 0, 0), m, n, [16])
     S = lb.Stack([build(m, n, p)])
-    x = x_tensor(synth.activations((32, 1, 4), 4, n, io="bf16"))
+    xn = synth.activations((32, 1, T), T, n, io="bf16")
+    x = x_tensor(xn)
+    y = torch.empty((T, m), dtype=torch.bfloat16, device="cuda")
+    S.forward([x], [y], regime=regime)        # a valid call first: the stack holds a plan
+    torch.cuda.synchronize()
+    for _ in range(2):
+        with pytest.raises(lb.LittleBitError, match="overlaps its own x"):
+            S.forward([x], [x], regime=regime)
+    y.zero_()
+    S.forward([x], [y], regime=regime)
+    torch.cuda.synchronize()
+    assert_bf16_close(to_f64(y), oracle.forward(x_f64(xn), p, m, n), "after refused calls")
     with pytest.raises(lb.LittleBitError, match="overlaps its own x"):
-        S.forward([x], [x], regime=lb.REGIME_DECODE)
+        S.forward([x], [x], regime=regime)
+    S.close()
 
 
 def test_stack_exact_fp32_matches_single():
