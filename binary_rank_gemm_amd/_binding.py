@@ -29,7 +29,8 @@ STATUS_NAMES = {OK: "LB_OK", INVALID_ARGUMENT: "LB_ERR_INVALID_ARGUMENT", INVALI
 # include/littlebit_probe.h is bound in probe.py)
 EXPORTS = [
     "lb_packed_words_per_row", "lb_rank_for_bpw", "lb_pack_signs_host", "lb_pack_signs", "lb_unpack_signs",
-    "lb_linear_create", "lb_linear_forward", "lb_linear_forward_ex", "lb_linear_info", "lb_linear_destroy",
+    "lb_linear_create", "lb_linear_forward", "lb_linear_forward_ex", "lb_linear_forward_noalloc", "lb_linear_info",
+    "lb_linear_destroy",
     "lb_stack_create", "lb_stack_forward", "lb_stack_forward_ex", "lb_stack_destroy", "lb_status_string",
     "lb_last_error", "lb_init_dual_svid",
 ]
@@ -72,6 +73,7 @@ def lib():
         "lb_linear_create": (C.c_int, [i64, i64, C.POINTER(LbPath), i32, vp, C.POINTER(vp)]),
         "lb_linear_forward": (C.c_int, [vp, vp, vp, i64, C.c_int, vp]),
         "lb_linear_forward_ex": (C.c_int, [vp, vp, vp, i64, C.c_int, C.c_int, vp]),
+        "lb_linear_forward_noalloc": (C.c_int, [vp, vp, vp, i64, C.c_int, vp]),
         "lb_linear_info": (C.c_int, [vp, C.POINTER(i64), C.POINTER(i64), C.POINTER(i32), C.POINTER(i64),
                                      C.POINTER(i64)]),
         "lb_linear_destroy": (C.c_int, [vp]),
@@ -244,6 +246,18 @@ class Linear:
         return y
 
     __call__ = forward
+
+    def forward_noalloc(self, x, y, stream=None):
+        """lb_linear_forward_noalloc: y = x W^T into the caller's y, with the
+        library allocating nothing (decode kernels for bf16 x, exact kernels
+        for fp32 I/O; its work buffers are the library's fixed scratch)."""
+        if x.dim() != 2 or x.shape[1] != self.d_in or not x.is_contiguous() or not x.is_cuda:
+            raise ValueError(f"x must be a contiguous device tensor [tokens, {self.d_in}]")
+        if y.dim() != 2 or tuple(y.shape) != (x.shape[0], self.d_out) or not y.is_contiguous() or y.device != x.device:
+            raise ValueError(f"y must be a contiguous [{x.shape[0]}, {self.d_out}] tensor on x's device")
+        _check(lib().lb_linear_forward_noalloc(self.handle, x.data_ptr(), y.data_ptr(), x.shape[0], _io_of(x, y),
+                                               _stream(stream)))
+        return y
 
     def close(self):
         if getattr(self, "handle", None) is not None and self.handle.value:

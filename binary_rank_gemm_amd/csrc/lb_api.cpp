@@ -132,6 +132,17 @@ struct lb_linear_s {
   DecodePlan plan;
   PrefillPlan pplan;
   hipStream_t last_stream = nullptr;
+  // no-allocation forward: the decode tables of this linear for every token
+  // bucket, built at create against the fixed per-device scratch
+  struct NoAllocDecode {
+    bool ok = false;                 // the bucket's scratch fits kNoAllocScratchBytes
+    int nv = 0, nm = 0, nu = 0;
+    size_t entries_off = 0, v_off = 0, m_off = 0, u_off = 0;   // bytes into na_tables
+  };
+  NoAllocDecode na[5];               // token buckets 1, 2, 4, 8, 16
+  void* na_scratch = nullptr;        // this device's scratch array
+  uint8_t* na_tables = nullptr;      // device copy of na_host
+  std::vector<uint8_t> na_host;      // host image of the tables (source of the create-time copy)
 };
 
 // The decode layouts (V and U sign words) of every linear of a stack copied
@@ -189,6 +200,7 @@ namespace {
 void linear_free(lb_linear L) {
   if (!L) return;
   if (L->arena.base) (void)hipFree(L->arena.base);
+  if (L->na_tables) (void)hipFree(L->na_tables);
   L->zexact.release();
   L->plan.release();
   prefill_plan_release(L->pplan);
@@ -222,25 +234,34 @@ hipError_t upload(Item** dst, const std::vector<Item>& v) {
   return e;
 }
 
-// Builds (or reuses) the decode plan for `count` linears at `T` tokens per launch.
+// Host side of a decode plan for `count` linears at `T` tokens per launch:
+// the kernels' tables and the scratch they need.
 //   V items: each path's column tiles in groups of at most decode_v_tiles, each
 //     group's 128-row chunks cut into ranges of about kDecodeVItemBytes of sign
 //     words (at least 4 chunks, one per wave, where the path has them).
 //   mid items: one per (entry, path).
 //   U items: runs of 4 qw quads, qw quads per wave, about kDecodeUItemBytes.
-lb_status build_decode_plan(DecodePlan& P, const lb_linear* L, int count, int T, const DecodeImage* img = nullptr) {
-  if (P.T == T && P.count == count) return LB_OK;
-  // the buffers and tables below are freed and reallocated: until every step
-  // has succeeded the plan must not look valid for any token count
-  P.T = -1;
-  P.count = 0;
+// The entries' aimg / cval pointers are left null: they point into the work
+// buffer, wherever the caller places it (img_off / cv_off bytes into it).
+struct DecodeHostPlan {
+  std::vector<DecEntry> entries;
+  std::vector<VItem> vitems;        // largest first
+  std::vector<MItem> mitems;
+  std::vector<UItem> uitems;        // largest first
+  std::vector<size_t> img_off, cv_off;
+  size_t part_bytes = 0;            // V-stage partial slots
+  size_t work_bytes = 0;            // U-stage operands and correction sums
+};
+
+void plan_decode_host(DecodeHostPlan& H, const lb_linear* L, int count, int T, const DecodeImage* img) {
   const int bucket = decode_bucket(T), tb = (bucket + 7) / 8, ct_max = decode_v_tiles(bucket);
-  P.entries_h.assign(count, DecEntry{});
+  H.entries.assign(count, DecEntry{});
+  H.img_off.assign(count, 0);
+  H.cv_off.assign(count, 0);
   std::vector<std::pair<double, VItem>> vl;
   std::vector<std::pair<double, UItem>> ul;
-  std::vector<MItem> ml;
+  H.mitems.clear();
   size_t work_bytes = 0;
-  std::vector<size_t> img_off(count), cv_off(count);
   int slots = 0;
   // Item sizes: about 192 KB of sign words per item when the launch has
   // plenty of work; a launch with less is cut into about one item per
@@ -261,7 +282,7 @@ lb_status build_decode_plan(DecodePlan& P, const lb_linear* L, int count, int T,
   const double utarget = std::min<double>(kDecodeUItemBytes, std::max(kMinItemBytes, utotal / slots_per_launch));
   for (int e = 0; e < count; ++e) {
     const lb_linear l = L[e];
-    DecEntry& E = P.entries_h[e];
+    DecEntry& E = H.entries[e];
     E.m = (int)l->m;
     E.n = (int)l->n;
     E.np = l->np;
@@ -280,7 +301,7 @@ lb_status build_decode_plan(DecodePlan& P, const lb_linear* L, int count, int T,
       const double chunk_bytes = gt * 256.0;
       const int max_split = std::max(1, E.nkc / kWavesPerGroup);
       const int nsplit = std::max(1, std::min(max_split, (int)std::lround(E.nkc * chunk_bytes / vtarget)));
-      ml.push_back(MItem{e, p, slots, groups, nsplit, gt, 0, 0});
+      H.mitems.push_back(MItem{e, p, slots, groups, nsplit, gt, 0, 0});
       for (int g = 0; g < groups; ++g) {
         const int tile0 = g * gt, nt = std::min(gt, nct - tile0);
         for (int sp = 0; sp < nsplit; ++sp) {
@@ -291,9 +312,9 @@ lb_status build_decode_plan(DecodePlan& P, const lb_linear* L, int count, int T,
       }
       slots += groups * nsplit;
     }
-    img_off[e] = work_bytes;
+    H.img_off[e] = work_bytes;
     work_bytes += align256((size_t)E.ug.nu * tb * kABytes);
-    cv_off[e] = work_bytes;
+    H.cv_off[e] = work_bytes;
     work_bytes += align256(2 * 16 * sizeof(float));
     const double qbytes = E.ug.qbytes + 256.0;
     const int qw = std::max(1, std::min(decode_u_qw_max(bucket),
@@ -304,25 +325,78 @@ lb_status build_decode_plan(DecodePlan& P, const lb_linear* L, int count, int T,
       ul.push_back({nq * qbytes, UItem{e, q0, nq, (nq + kWavesPerGroup - 1) / kWavesPerGroup}});
     }
   }
-  work_bytes += kDmaPad;
-  HIP_TRY(P.work.ensure(work_bytes));
-  HIP_TRY(P.part.ensure(std::max<size_t>((size_t)slots * decode_slot_floats(bucket) * sizeof(float), 256)));
+  H.work_bytes = work_bytes + kDmaPad;
+  H.part_bytes = std::max<size_t>((size_t)slots * decode_slot_floats(bucket) * sizeof(float), 256);
+  H.vitems = largest_first(vl);
+  H.uitems = largest_first(ul);
+}
+
+// Builds (or reuses) the decode plan for `count` linears at `T` tokens per
+// launch: the host plan, its scratch buffers and its tables on the device.
+lb_status build_decode_plan(DecodePlan& P, const lb_linear* L, int count, int T, const DecodeImage* img = nullptr) {
+  if (P.T == T && P.count == count) return LB_OK;
+  // the buffers and tables below are freed and reallocated: until every step
+  // has succeeded the plan must not look valid for any token count
+  P.T = -1;
+  P.count = 0;
+  DecodeHostPlan H;
+  plan_decode_host(H, L, count, T, img);
+  HIP_TRY(P.work.ensure(H.work_bytes));
+  HIP_TRY(P.part.ensure(H.part_bytes));
   for (int e = 0; e < count; ++e) {
-    P.entries_h[e].aimg = reinterpret_cast<uint8_t*>(P.work.ptr) + img_off[e];
-    P.entries_h[e].cval = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(P.work.ptr) + cv_off[e]);
+    H.entries[e].aimg = reinterpret_cast<uint8_t*>(P.work.ptr) + H.img_off[e];
+    H.entries[e].cval = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(P.work.ptr) + H.cv_off[e]);
   }
-  const std::vector<VItem> vlist = largest_first(vl);
-  const std::vector<UItem> ulist = largest_first(ul);
+  P.entries_h = H.entries;
   HIP_TRY(upload(&P.entries_d, P.entries_h));
-  HIP_TRY(upload(&P.vitems_d, vlist));
-  HIP_TRY(upload(&P.mitems_d, ml));
-  HIP_TRY(upload(&P.uitems_d, ulist));
-  P.nv = (int)vlist.size();
-  P.nm = (int)ml.size();
-  P.nu = (int)ulist.size();
+  HIP_TRY(upload(&P.vitems_d, H.vitems));
+  HIP_TRY(upload(&P.mitems_d, H.mitems));
+  HIP_TRY(upload(&P.uitems_d, H.uitems));
+  P.nv = (int)H.vitems.size();
+  P.nm = (int)H.mitems.size();
+  P.nu = (int)H.uitems.size();
   P.T = T;
   P.count = count;
   return LB_OK;
+}
+
+// Device tables of one decode plan and its partial-slot buffer.
+struct DecodeTables {
+  const DecEntry* entries;
+  const VItem* vitems;
+  const MItem* mitems;
+  const UItem* uitems;
+  int nv, nm, nu;
+  float* part;
+};
+
+// Launches the three decode kernels over token slices of at most
+// kDecodeMaxTokens, on tables built for Tplan = min(kDecodeMaxTokens, tokens)
+// tokens (a shorter last slice runs the same kernels on fewer tokens).
+hipError_t launch_decode_slices(const DecodeTables& D, const void* const* xs_d, void* const* ys_d, const void* x0,
+                                void* y0, int64_t tokens, int yf32, hipStream_t st) {
+  const int Tplan = (int)std::min<int64_t>(kDecodeMaxTokens, tokens);
+  for (int64_t t0 = 0; t0 < tokens; t0 += kDecodeMaxTokens) {
+    DecArgs a{};
+    a.entries = D.entries;
+    a.xs = xs_d;
+    a.ys = ys_d;
+    a.x0 = x0;
+    a.y0 = y0;
+    a.T = (int)std::min<int64_t>(kDecodeMaxTokens, tokens - t0);
+    a.t0 = (int)t0;
+    a.bucket = decode_bucket(Tplan);
+    a.yf32 = yf32;
+    a.vitems = D.vitems;
+    a.mitems = D.mitems;
+    a.uitems = D.uitems;
+    a.part = D.part;
+    hipError_t e = launch_decode_v(a, D.nv, st);
+    if (e == hipSuccess) e = launch_decode_mid(a, D.nm, st);
+    if (e == hipSuccess) e = launch_decode_u(a, D.nu, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 // Launches the three decode kernels over token slices of at most
@@ -336,27 +410,57 @@ lb_status run_decode(DecodePlan& P, const lb_linear* L, int count, const void* c
   if (P.T != Tplan && P.T != -1) HIP_TRY(hipStreamSynchronize(st));  // the plan is rewritten below
   lb_status s = build_decode_plan(P, L, count, Tplan, img);
   if (s != LB_OK) return s;
-  for (int64_t t0 = 0; t0 < tokens; t0 += kDecodeMaxTokens) {
-    const int T = (int)std::min<int64_t>(kDecodeMaxTokens, tokens - t0);
-    DecArgs a{};
-    a.entries = P.entries_d;
-    a.xs = xs_d;
-    a.ys = ys_d;
-    a.x0 = x0;
-    a.y0 = y0;
-    a.T = T;
-    a.t0 = (int)t0;
-    a.bucket = decode_bucket(Tplan);
-    a.yf32 = yf32;
-    a.vitems = P.vitems_d;
-    a.mitems = P.mitems_d;
-    a.uitems = P.uitems_d;
-    a.part = reinterpret_cast<float*>(P.part.ptr);
-    HIP_TRY(launch_decode_v(a, P.nv, st));
-    HIP_TRY(launch_decode_mid(a, P.nm, st));
-    HIP_TRY(launch_decode_u(a, P.nu, st));
-  }
+  const DecodeTables D{P.entries_d, P.vitems_d, P.mitems_d, P.uitems_d, P.nv, P.nm, P.nu,
+                       reinterpret_cast<float*>(P.part.ptr)};
+  HIP_TRY(launch_decode_slices(D, xs_d, ys_d, x0, y0, tokens, yf32, st));
   return LB_OK;
+}
+
+// index of a token bucket (1, 2, 4, 8, 16) in lb_linear_s::na
+inline int bucket_index(int bucket) { return bucket <= 1 ? 0 : bucket <= 2 ? 1 : bucket <= 4 ? 2 : bucket <= 8 ? 3 : 4; }
+
+// The no-allocation forward's tables of a linear (see lb_linear_s::na): for
+// every token bucket, the single-linear decode plan that lb_linear_forward_ex
+// builds (so both run the same work items), its work buffer placed after the
+// partial slots in this device's scratch array; a bucket whose scratch would
+// not fit is marked unavailable.  One device allocation and one copy, on
+// `st`, from a host image the linear keeps.
+hipError_t build_noalloc_tables(lb_linear L, hipStream_t st) {
+  hipError_t e = noalloc_scratch(L->device, &L->na_scratch);
+  if (e != hipSuccess) return e;
+  std::vector<uint8_t>& img = L->na_host;
+  img.clear();
+  auto put = [&](const void* src, size_t bytes) {
+    const size_t off = align256(img.size());
+    img.resize(off + std::max<size_t>(bytes, 1));
+    if (bytes) std::memcpy(img.data() + off, src, bytes);
+    return off;
+  };
+  static constexpr int kBuckets[5] = {1, 2, 4, 8, 16};
+  for (int b = 0; b < 5; ++b) {
+    DecodeHostPlan H;
+    lb_linear one[1] = {L};
+    plan_decode_host(H, one, 1, kBuckets[b], nullptr);
+    const size_t work_off = align256(H.part_bytes);
+    lb_linear_s::NoAllocDecode& N = L->na[b];
+    N.ok = work_off + H.work_bytes <= kNoAllocScratchBytes;
+    if (!N.ok) continue;
+    uint8_t* work = reinterpret_cast<uint8_t*>(L->na_scratch) + work_off;
+    H.entries[0].aimg = work + H.img_off[0];
+    H.entries[0].cval = reinterpret_cast<float*>(work + H.cv_off[0]);
+    N.entries_off = put(H.entries.data(), sizeof(DecEntry));
+    N.v_off = put(H.vitems.data(), H.vitems.size() * sizeof(VItem));
+    N.m_off = put(H.mitems.data(), H.mitems.size() * sizeof(MItem));
+    N.u_off = put(H.uitems.data(), H.uitems.size() * sizeof(UItem));
+    N.nv = (int)H.vitems.size();
+    N.nm = (int)H.mitems.size();
+    N.nu = (int)H.uitems.size();
+  }
+  if (img.empty()) return hipSuccess;
+  img.resize(align256(img.size()));
+  e = hipMalloc(&L->na_tables, img.size());
+  if (e == hipSuccess) e = hipMemcpyAsync(L->na_tables, img.data(), img.size(), hipMemcpyHostToDevice, st);
+  return e;
 }
 
 lb_status check_io(int64_t tokens, lb_dtype io, lb_regime regime) {
@@ -589,6 +693,7 @@ lb_status lb_linear_create(int64_t d_out, int64_t d_in, const lb_path* paths, in
   if ((e = prefill_layer_build(L->pre, L->arena.take(pre_bytes), pre_bytes, d_out, d_in, L->paths, n_paths, st)) !=
       hipSuccess)
     return bail(e, "prefill layout");
+  if ((e = build_noalloc_tables(L, st)) != hipSuccess) return bail(e, "no-allocation forward tables");
   *out = L;
   return LB_OK;
 }
@@ -646,6 +751,44 @@ lb_status lb_linear_forward_ex(lb_linear L, const void* x, void* y, int64_t toke
 
 lb_status lb_linear_forward(lb_linear L, const void* x, void* y, int64_t tokens, lb_dtype io, void* stream) {
   return lb_linear_forward_ex(L, x, y, tokens, io, LB_REGIME_AUTO, stream);
+}
+
+lb_status lb_linear_forward_noalloc(lb_linear L, const void* x, void* y, int64_t tokens, lb_dtype io, void* stream) {
+  if (!L) return fail(LB_ERR_INVALID_ARGUMENT, "null linear");
+  if (!x || !y) return fail(LB_ERR_INVALID_ARGUMENT, "null x or y");
+  lb_status s = check_io(tokens, io, LB_REGIME_AUTO);
+  if (s != LB_OK) return s;
+  if (!aligned16(x) || !aligned16(y)) return fail(LB_ERR_ALIGNMENT, "x and y must be 16-byte aligned");
+  int dev = -1;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev != L->device)
+    return fail(LB_ERR_INVALID_ARGUMENT, "the linear lives on device %d but device %d is current", L->device, dev);
+  if (!L->na_scratch || !L->na_tables) return fail(LB_ERR_UNSUPPORTED, "no scratch was set up for this linear");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (io == LB_FP32) {
+    int rmax = 0;
+    for (int p = 0; p < L->np; ++p) rmax = std::max(rmax, L->paths[p].r);
+    const int rpad = (rmax + 15) / 16 * 16;
+    const size_t need = exact_scratch_floats(rmax, L->np, tokens, (int)L->n, rpad) * sizeof(float);
+    if (need > kNoAllocScratchBytes)
+      return fail(LB_ERR_UNSUPPORTED, "%lld fp32 tokens need %zu bytes of scratch; the no-allocation forward has %zu",
+                  (long long)tokens, need, kNoAllocScratchBytes);
+    HIP_TRY(launch_exact(L->paths, L->np, (int)L->m, (int)L->n, x, y, (int)tokens, 1, 1,
+                         reinterpret_cast<float*>(L->na_scratch), rpad, st));
+    return LB_OK;
+  }
+  const int Tplan = (int)std::min<int64_t>(kDecodeMaxTokens, tokens);
+  const lb_linear_s::NoAllocDecode& N = L->na[bucket_index(decode_bucket(Tplan))];
+  if (!N.ok)
+    return fail(LB_ERR_UNSUPPORTED, "the decode scratch of this %lld x %lld linear exceeds the %zu bytes of the "
+                "no-allocation forward", (long long)L->m, (long long)L->n, kNoAllocScratchBytes);
+  const DecodeTables D{reinterpret_cast<const DecEntry*>(L->na_tables + N.entries_off),
+                       reinterpret_cast<const VItem*>(L->na_tables + N.v_off),
+                       reinterpret_cast<const MItem*>(L->na_tables + N.m_off),
+                       reinterpret_cast<const UItem*>(L->na_tables + N.u_off), N.nv, N.nm, N.nu,
+                       reinterpret_cast<float*>(L->na_scratch)};
+  HIP_TRY(launch_decode_slices(D, nullptr, nullptr, x, y, tokens, y_is_fp32(io), st));
+  return LB_OK;
 }
 
 lb_status lb_linear_destroy(lb_linear L) {

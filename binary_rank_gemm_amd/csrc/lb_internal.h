@@ -188,6 +188,11 @@ struct InitPathOut {
 // rocBLAS / rocSOLVER status when one of their calls failed, else 0.
 hipError_t dual_svid_init(const float* W, int64_t m, int64_t n, const int64_t* ranks, int np, const InitPathOut* out,
                           hipStream_t st, int* rocstatus);
+// Bytes of the fixed per-device scratch of the no-allocation forward, and its
+// device address on `device` (looked up on the first call for that device,
+// which must then be current; later calls return the kept address).
+constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;
+hipError_t noalloc_scratch(int device, void** ptr);
 // calibration: one read-only streaming pass over a device buffer
 hipError_t launch_probe_stream_read(const void* buf, int64_t bytes, hipStream_t st);
 hipError_t launch_decode_h_layout(const uint16_t* h0, const uint16_t* h1, int m, int nq, uint16_t* hq,

@@ -142,6 +142,28 @@ lb_status lb_linear_forward(lb_linear L, const void* x, void* y, int64_t tokens,
 lb_status lb_linear_forward_ex(lb_linear L, const void* x, void* y, int64_t tokens, lb_dtype io,
                                lb_regime regime, void* stream);
 
+/* Forward for callers that cannot allocate device memory during the call
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  It runs the kernels lb_linear_forward_ex runs with an explicit
+ * regime and gives the same results bit for bit: bf16 x (io LB_BF16 or
+ * LB_BF16_FP32) -> LB_REGIME_DECODE, any token count, in launches of up to 16
+ * tokens; fp32 I/O (LB_FP32) -> LB_REGIME_EXACT.  It calls no allocator:
+ * its work buffers live in one fixed scratch array of 8 MiB per GPU (a device
+ * global of this library, which each GPU it runs on holds until the process
+ * ends), and the kernels' work-item tables were built by lb_linear_create.
+ * Errors: as lb_linear_forward, plus LB_ERR_UNSUPPORTED when the call would
+ * need more than the 8 MiB (the decode partial sums of very long rows or
+ * large ranks; the exact path's latent sums of many fp32 tokens: splits x
+ * n_paths x tokens x rank rounded to 16, 4 bytes each), and
+ * LB_ERR_INVALID_ARGUMENT when the current device is not the linear's.
+ * Every such call on one GPU shares that GPU's scratch: calls that overlap
+ * in time on one GPU (on different streams, or from different threads
+ * without ordering) race and give undefined results; calls ordered on one
+ * stream are safe.  Nothing in the scratch must start at zero: each call
+ * writes every value it reads back. */
+lb_status lb_linear_forward_noalloc(lb_linear L, const void* x, void* y, int64_t tokens, lb_dtype io,
+                                    void* stream);
+
 /* Shape of a linear; any output pointer may be NULL.  ranks receives n_paths
  * values; device_bytes is the library-owned device memory of the linear. */
 lb_status lb_linear_info(lb_linear L, int64_t* d_out, int64_t* d_in, int32_t* n_paths,
