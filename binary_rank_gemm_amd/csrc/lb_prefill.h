@@ -40,6 +40,7 @@ struct PreItem {
   int entry;                 // < 0: idle slot
   int mt, nt;
   int str;                   // GEMM1: a wave's columns reach into both paths
+  int tn;                    // tile width: 256, or 128 / 64 for a narrow last column tile
 };
 
 // Launch plan of the prefill kernels for a list of linears at T tokens.

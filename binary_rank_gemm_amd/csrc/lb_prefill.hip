@@ -205,24 +205,38 @@ __device__ inline void vm_wait_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// A tile in LDS: 256 rows x 64 bf16, 16-byte chunk c of row r at slot
-// 8 r + (c ^ (r & 7)) (rows unpadded, the XOR spreads the 8 rows read together
-// over all banks).  Slots are filled in order by the direct-to-LDS loads: wave
-// w, instruction i, lane l writes slot 64 (W i + w) + l, W = waves.
+// A tile in LDS: 256 rows x 64 bf16 (128 bytes a row, unpadded), 16-byte
+// chunk c of row r at slot 8 r + (c ^ f(r)), f(r) = (r & 7) ^ ((r >> 3) & 1).
+// A fragment read has lane l32 on row base + l32 (base a multiple of 32), all
+// lanes at the same logical chunk.  f puts any 8 consecutive rows of an
+// aligned group on 8 distinct 16-byte positions of a 128-byte line, and the
+// even rows (likewise the odd rows) of any aligned 16 on 8 distinct
+// positions, so the rows a read serves together fall on distinct banks
+// whether the LDS serves 8 lanes over 128 bytes or 16 lanes over 256 bytes
+// per clock.  Slots are filled in order by the direct-to-LDS loads: wave w,
+// instruction i, lane l writes slot 64 (W i + w) + l, W = waves.
+__device__ inline int a_row_xor(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 __device__ inline int a_slot_row(int s) { return s >> 3; }
-__device__ inline int a_slot_chunk(int s) { return (s & 7) ^ ((s >> 3) & 7); }
+__device__ inline int a_slot_chunk(int s) { return (s & 7) ^ a_row_xor(s >> 3); }
 
-// Wave layout of the 256 x 256 workgroup tile: WM x WN waves, each owning
-// (256 / WM) x (256 / WN) outputs as MB x NB blocks of 32 x 32.  STR (GEMM1
-// only): some wave's columns cross from the primary path into the residual
-// one, so |g| is chosen per column block.  PART: the tile's rows run past the
-// last token (the last row stripe when T is not a multiple of 256); each wave
-// then reads and multiplies only its 32-row blocks that hold tokens.
-template <int MODE, int WM, int WN, bool STR, bool PART>
+// Wave layout of a 256 x TN workgroup tile: WM x WN waves, each owning
+// (256 / WM) x (TN / WN) outputs as MB x NB blocks of 32 x 32.  TN = 256 for
+// whole tiles; the last column tile of a GEMM whose N leaves only 128 or 64
+// columns in it takes TN = 128 (4 x 2 waves of 64 x 64) or TN = 64 (8 x 1
+// waves of 32 x 64): waves w and w + 4 share a SIMD, so in every layout the
+// four SIMDs get equal shares and a narrow tile takes a fraction of a whole
+// one's time.  STR (GEMM1 only): some wave's columns cross from the primary
+// path into the residual one, so |g| is chosen per column block.  PART: the
+// tile's rows run past the last token (the last row stripe when T is not a
+// multiple of 256); each wave then reads and multiplies only its 32-row
+// blocks that hold tokens.
+template <int MODE, int WM, int WN, int TN, bool STR, bool PART>
 __device__ __forceinline__ void prefill_tile(const PreArgs& a, const PreItem& it) {
   constexpr int kWaves = WM * WN, kNT = 64 * kWaves;
-  constexpr int MB = kPreBM / WM / 32, NB = kPreBN / WN / 32;
+  constexpr int MB = kPreBM / WM / 32, NB = TN / WN / 32;
   constexpr int kAI = kPreBM * 8 / kNT;                 // A loads (16 B per lane) per wave per block
+  static_assert(kWaves == 8, "eight waves, two per SIMD");
+  static_assert(TN / WN == 64, "a wave covers 64 columns (half a 128-column B tile)");
   static_assert(NB == 2 || NB == 4, "a wave covers half or all of a 128-column B tile");
   static_assert(kWaves >= 3, "waves 0, 1, 2 carry the B words and |g|");
   static_assert(MODE == 1 || !STR, "only GEMM1 columns span paths");
@@ -311,10 +325,10 @@ __device__ __forceinline__ void prefill_tile(const PreArgs& a, const PreItem& it
     }
   };
   // A fragment of row block mb, K step ks: row R = wm 128 + 32 mb + l32,
-  // chunk 2 ks + kg; R & 7 == l32 & 7
+  // chunk 2 ks + kg; R & 15 == l32 & 15
   int aoff[4];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) aoff[ks] = (wm * MB * 32 + l32) * 128 + (((2 * ks + kg) ^ (l32 & 7)) * 16);
+  for (int ks = 0; ks < 4; ++ks) aoff[ks] = (wm * MB * 32 + l32) * 128 + (((2 * ks + kg) ^ a_row_xor(l32)) * 16);
   auto read_a = [&](int buf, int ks, u32x4* af) {
     const uint8_t* Ab = lds + buf * kBuf + aoff[ks];
 #pragma unroll
@@ -512,11 +526,11 @@ __device__ __forceinline__ void prefill_tile(const PreArgs& a, const PreItem& it
   }
   if (c_stage) {
     __syncthreads();
-    constexpr int kChunks = kPreBM * kPreBN / 8;   // 16-byte chunks of the tile
+    constexpr int kChunks = kPreBM * TN / 8;       // 16-byte chunks of the tile
     const int tid_all = threadIdx.x;
 #pragma unroll 4
     for (int c = tid_all; c < kChunks; c += kNT) {
-      const int rt = c / (kPreBN / 8), ch = c % (kPreBN / 8);
+      const int rt = c / (TN / 8), ch = c % (TN / 8);
       const int row = m0 + rt, col = n0 + ch * 8;
       if (row >= T || col >= N) continue;
       // logical slots 2 ch, 2 ch + 1 sit in the 16-byte chunk ch ^ (r / 2),
@@ -540,32 +554,46 @@ __device__ __forceinline__ void prefill_tile(const PreArgs& a, const PreItem& it
 // paths take the body that picks |g| per column block.
 // PART: a launch over the tiles of row stripes that run past the last token
 // (a separate launch, so the full tiles' kernel carries none of it).
-template <int MODE, int WM, int WN, bool PART>
-__global__ void __launch_bounds__(64 * WM * WN, 1) k_prefill(PreArgs a) {
+// The tile width (it.tn: 256, 128 or 64) picks the wave layout, uniformly
+// over the workgroup.
+template <int MODE, bool STR, bool PART>
+__device__ __forceinline__ void prefill_tile_any(const PreArgs& a, const PreItem& it) {
+  if (it.tn == 256) prefill_tile<MODE, 2, 4, 256, STR, PART>(a, it);
+  else if (it.tn == 128) prefill_tile<MODE, 4, 2, 128, STR, PART>(a, it);
+  else prefill_tile<MODE, 8, 1, 64, STR, PART>(a, it);
+}
+
+template <int MODE, bool PART>
+__global__ void __launch_bounds__(512, 1) k_prefill(PreArgs a) {
   const PreItem it = a.items[blockIdx.x];
   if (it.entry < 0) return;
   if constexpr (MODE == 1) {
-    if (it.str) prefill_tile<1, WM, WN, true, PART>(a, it);
-    else prefill_tile<1, WM, WN, false, PART>(a, it);
+    if (it.str) prefill_tile_any<1, true, PART>(a, it);
+    else prefill_tile_any<1, false, PART>(a, it);
   } else {
-    prefill_tile<2, WM, WN, false, PART>(a, it);
+    prefill_tile_any<2, false, PART>(a, it);
   }
 }
 
-// wave layout of the prefill GEMMs
-constexpr int kPreWM = 2, kPreWNv = 4;
-constexpr int kWaveCols = kPreBN / kPreWNv;
+constexpr int kWaveCols = 64;   // columns of one wave in every layout
+
+// width of column tile nt of a GEMM with N columns: 256, or 128 / 64 for a
+// last tile that leaves at most that many columns
+int tile_width(int N, int nt) {
+  const int left = N - nt * kPreBN;
+  return left >= kPreBN ? kPreBN : (left > 128 ? 256 : (left > 64 ? 128 : 64));
+}
 
 // true when a wave of GEMM1 tile nt has columns of both paths
-bool tile_straddles(const PrefillLayer& L, int nt) {
+bool tile_straddles(const PrefillLayer& L, int nt, int tn) {
   if (L.np < 2) return false;
-  for (int w = 0; w < kPreWNv; ++w) {
+  for (int w = 0; w < tn / kWaveCols; ++w) {
     const int c0 = nt * kPreBN + w * kWaveCols;
     if (c0 < L.roff[1] && c0 + kWaveCols - 32 >= L.roff[1]) return true;
   }
   return false;
 }
-constexpr int kThreads = 64 * kPreWM * kPreWNv;
+constexpr int kThreads = 512;
 constexpr size_t kPreLds = kPreBufs * (size_t)(kPreBM * kPreBK * 2 + 2 * 64 * 16 + 2 * kPreBK * 2);
 static_assert(kPreLds >= (size_t)kPreBM * kPreBN * 2, "the epilogue stages the bf16 tile in the LDS buffers");
 
@@ -673,7 +701,7 @@ std::vector<PreItem> xcd_order(const std::vector<std::vector<PreItem>>& stripes,
   }
   size_t len = 0;
   for (auto& v : per) len = std::max(len, v.size());
-  std::vector<PreItem> out(len * kXcd, PreItem{-1, 0, 0, 0});
+  std::vector<PreItem> out(len * kXcd, PreItem{-1, 0, 0, 0, 0});
   for (int x = 0; x < kXcd; ++x)
     for (size_t i = 0; i < per[x].size(); ++i) out[i * kXcd + x] = per[x][i];
   return out;
@@ -699,15 +727,22 @@ hipError_t prefill_prepare(PrefillPlan& P, const PrefillLayer* const* layers, in
     zoffs[e] = zoff;
     zoff += align256((size_t)T * L.Rp * 2);
     const int nt1 = (L.Rp + kPreBN - 1) / kPreBN, nt2 = (L.m + kPreBN - 1) / kPreBN;
+    // work of one row stripe in whole-tile K blocks (a narrow tile counts its share)
+    double w1 = 0, w2 = 0;
+    for (int nt = 0; nt < nt1; ++nt) w1 += tile_width(L.Rp, nt) / (double)kPreBN;
+    for (int nt = 0; nt < nt2; ++nt) w2 += tile_width(L.m, nt) / (double)kPreBN;
     for (int mt = 0; mt < mts; ++mt) {
       std::vector<PreItem> a, b;
-      for (int nt = 0; nt < nt1; ++nt) a.push_back(PreItem{e, mt, nt, tile_straddles(L, nt) ? 1 : 0});
-      for (int nt = 0; nt < nt2; ++nt) b.push_back(PreItem{e, mt, nt, 0});
+      for (int nt = 0; nt < nt1; ++nt) {
+        const int tn = tile_width(L.Rp, nt);
+        a.push_back(PreItem{e, mt, nt, tile_straddles(L, nt, tn) ? 1 : 0, tn});
+      }
+      for (int nt = 0; nt < nt2; ++nt) b.push_back(PreItem{e, mt, nt, 0, tile_width(L.m, nt)});
       const bool part = (mt + 1) * kPreBM > T;
       (part ? s1p : s1).push_back(a);
       (part ? s2p : s2).push_back(b);
-      (part ? k1p : k1).push_back(L.kb1);
-      (part ? k2p : k2).push_back(L.kb2);
+      (part ? k1p : k1).push_back(L.kb1 * w1 / nt1);
+      (part ? k2p : k2).push_back(L.kb2 * w2 / nt2);
     }
   }
   std::vector<PreItem> i1 = xcd_order(s1, k1), i2 = xcd_order(s2, k2);
@@ -777,17 +812,17 @@ hipError_t prefill_run(PrefillPlan& P, const PrefillLayer* const* layers, int co
   // GEMM1 over the full row stripes, then over the stripe past the last token;
   // the same for GEMM2
   a.items = P.items_d;
-  if (P.n1 > 0) hipLaunchKernelGGL((k_prefill<1, kPreWM, kPreWNv, false>), dim3(P.n1), dim3(kThreads), kPreLds, st, a);
+  if (P.n1 > 0) hipLaunchKernelGGL((k_prefill<1, false>), dim3(P.n1), dim3(kThreads), kPreLds, st, a);
   a.items = P.items_d + P.n1;
-  if (P.n1p > 0) hipLaunchKernelGGL((k_prefill<1, kPreWM, kPreWNv, true>), dim3(P.n1p), dim3(kThreads), kPreLds, st, a);
+  if (P.n1p > 0) hipLaunchKernelGGL((k_prefill<1, true>), dim3(P.n1p), dim3(kThreads), kPreLds, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   a.items = P.items_d + P.n1 + P.n1p;
-  if (P.n2 > 0) hipLaunchKernelGGL((k_prefill<2, kPreWM, kPreWNv, false>), dim3(P.n2), dim3(kThreads), kPreLds, st, a);
+  if (P.n2 > 0) hipLaunchKernelGGL((k_prefill<2, false>), dim3(P.n2), dim3(kThreads), kPreLds, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   a.items = P.items_d + P.n1 + P.n1p + P.n2;
-  if (P.n2p > 0) hipLaunchKernelGGL((k_prefill<2, kPreWM, kPreWNv, true>), dim3(P.n2p), dim3(kThreads), kPreLds, st, a);
+  if (P.n2p > 0) hipLaunchKernelGGL((k_prefill<2, true>), dim3(P.n2p), dim3(kThreads), kPreLds, st, a);
   return hipGetLastError();
 }
 

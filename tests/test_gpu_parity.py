@@ -172,6 +172,21 @@ def test_prefill_identity_probe_many_tokens_bit_exact():
     assert np.array_equal(to_f64(y), oracle.forward(x_f64(x), paths, m, n))
 
 
+@pytest.mark.parametrize("m,n,ranks", [(300, 320, [20, 40]), (640, 384, [270, 20]), (1000, 320, [149, 102])])
+def test_prefill_identity_probe_narrow_tiles_bit_exact(m, n, ranks):
+    """x = I_n with unit scales through the prefill GEMMs at shapes whose last
+    column tiles are 128 or 64 wide (GEMM1 N = the concatenated padded rank,
+    GEMM2 N = m), some with a wave's columns in both paths: y = sum_p U_p V_p^T
+    exactly."""
+    ones = lambda k: f16bits(np.ones(k))
+    paths = [dict(rank=r, u_words=synth.sign_words((35, p, 0), m, r), v_words=synth.sign_words((35, p, 1), n, r),
+                  h=ones(m), g=ones(n), l=ones(r)) for p, r in enumerate(ranks)]
+    x = synth.bf16_bits_from_f32(np.eye(n, dtype=np.float32))
+    y = build(m, n, paths).forward(x_tensor(x), regime=lb.REGIME_PREFILL)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_f64(y), oracle.forward(x_f64(x), paths, m, n))
+
+
 DECODE_SHAPES = [
     # m, n, ranks, T, outliers
     (512, 512, [16, 16], 4, 0.0),        # the single-512 shape in bf16
@@ -464,6 +479,8 @@ PREFILL_SHAPES = [
     (2000, 300, [600], 129),             # single path
     (1024, 2048, [704, 704], 512),       # Llama-2-13B-like rank at 0.55 BPW
     (4096, 14336, [478, 478], 256),      # long K: many blocks through the LDS pipeline
+    (700, 520, [20, 40], 300),           # GEMM1: one 128-wide tile whose first wave spans both paths
+    (640, 384, [270, 20], 260),          # GEMM1: a 64-wide last tile spanning both paths; GEMM2: 128-wide last tile
 ]
 
 
