@@ -422,7 +422,8 @@ def run_decode(args, lb, torch):
     # The stack is bound to its buffers once, so each step is one C-ABI call
     # with no per-call marshalling of the 560 pointers; the library's own
     # choice of launch form (lb_stack_forward).
-    fn = S.bind(xs, ys).forward
+    regime = {"auto": lb.REGIME_AUTO, "decode": lb.REGIME_DECODE, "prefill": lb.REGIME_PREFILL}[args.regime]
+    fn = S.bind(xs, ys, regime=regime, use_graph=None if regime == lb.REGIME_AUTO else False).forward
     n_settle = settle(fn, args.settle_s, torch)
     wall, kern_ms = time_steps(fn, args.steps, args.warmup, torch)
     byts, flops = algorithmic(wl, ranks_of, T)
@@ -442,7 +443,7 @@ def launch_forms(r, lb, torch, steps):
     return {f"{k}_us_per_step": round(v * 1e3, 2) for k, v in med.items()} | {"rounds": 3, "order": "alternating"}
 
 
-def token_sweep(r, lb, torch, tokens=(8, 64), steps=20):
+def token_sweep(r, lb, torch, tokens=(8, 16, 32, 64), steps=20):
     """The same linears at other token counts: the regime AUTO picks, and each
     regime forced, µs per step and per token, with algorithmic GB/s and the
     fraction of the larger of the HBM and MFMA roofline times."""
@@ -460,8 +461,7 @@ def token_sweep(r, lb, torch, tokens=(8, 64), steps=20):
             settle(fn, 0.2, torch)
             _, ms = time_steps(fn, steps, 3, torch)
             rec[f"{name}_us_per_step"] = round(ms * 1e3, 1)
-        rec["auto_picks"] = "decode" if abs(rec["auto_us_per_step"] - rec["decode_us_per_step"]) < \
-            abs(rec["auto_us_per_step"] - rec["prefill_us_per_step"]) else "prefill"
+        rec["auto_picks"] = REGIME_NAMES[lb.auto_regime(lins, T)]
         rec["us_per_token"] = round(rec["auto_us_per_step"] / T, 2)
         rec["hbm_gbps"] = round(byts / (rec["auto_us_per_step"] * 1e-6) / 1e9, 1)
         rec["frac_of_roofline"] = round(t_roof * 1e6 / rec["auto_us_per_step"], 4)
@@ -560,6 +560,38 @@ def run_prefill(args, lb, torch, workload):
     return rec
 
 
+FP32_PEAK_TFLOPS = 157.3       # MI355X dense fp32 (matrix cores and vector units alike)
+
+
+def run_fp32_tiled(lb, torch, layers=2, T=2048):
+    """fp32 I/O at many tokens (the exact regime's tiled fp32 matrix-core
+    form): the first `layers` layers of the Llama-2-13B-shaped stack at 2048
+    fp32 tokens, effective TFLOP/s against the fp32 peak."""
+    import synth
+    wl = synth.WORKLOADS["llama2-13b-0.55bpw"]
+    ranks_of = [ranks_for(wl, s, lb) for s in wl.mats]
+    lins, xs, ys = [], [], []
+    for l in range(layers):
+        for j, s in enumerate(wl.mats):
+            lins.append(lb.Linear.from_numpy(s.m, s.n, synth.layer_tensors(wl.wid, l, j, s.m, s.n, ranks_of[j])))
+            x = synth.activations((wl.wid, l, j, 88, T), T, s.n, io="fp32")
+            xs.append(torch.from_numpy(x).cuda())
+            ys.append(torch.empty((T, s.m), dtype=torch.float32, device="cuda"))
+    S = lb.Stack(lins)
+    fn = S.bind(xs, ys).forward
+    settle(fn, 0.3, torch)
+    _, ms = time_steps(fn, 3, 1, torch)
+    flops = sum(2 * T * (s.m + s.n) * sum(ranks_of[j]) for j, s in enumerate(wl.mats)) * layers
+    rec = {"workload": f"{wl.name}: first {layers} layers ({len(lins)} linears), {T} fp32 tokens, fp32 I/O",
+           "ms_per_step": round(ms, 3), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+           "frac_of_fp32_peak": round(flops / (ms * 1e-3) / 1e12 / FP32_PEAK_TFLOPS, 4),
+           "regime": REGIME_NAMES[lb.auto_regime(lins, T, lb.FP32)]}
+    S.close()
+    del S, lins, xs, ys, fn
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -569,6 +601,8 @@ def main():
                     help="seconds of untimed steps before the warm-up, so the clocks have settled whatever --warmup is")
     ap.add_argument("--workload", default="llama2-70b-decode-t1", choices=sorted(WORKLOADS))
     ap.add_argument("--layers", type=int, default=None, help="limit the stack to this many layers (not for reports)")
+    ap.add_argument("--regime", default="auto", choices=["auto", "decode", "prefill"],
+                    help="regime of the headline stack's timed steps (auto: the library's choice)")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-only", action="store_true", help="time only the prefill stack (for profiling)")
     ap.add_argument("--no-cpu", action="store_true")
@@ -666,6 +700,8 @@ def main():
         except lb.LittleBitError as e:
             out["prefill"] = {"error": str(e)}
     if not args.no_context and full:
+        out["fp32_tiled"] = run_fp32_tiled(lb, torch)
+        log(f"fp32 tiled: {out['fp32_tiled']}")
         import synth
         ctx = achievable_peaks(torch)
         ctx["decode_frac_of_probe_read"] = round(r["gbps"] / ctx["probe_read_gbps"], 4)

@@ -8,7 +8,6 @@ from ._binding import (  # noqa: F401
     BF16_FP32,
     EXPORTS,
     FP32,
-    PREFILL_MIN_TOKENS,
     REGIME_AUTO,
     REGIME_DECODE,
     REGIME_EXACT,
@@ -18,6 +17,7 @@ from ._binding import (  # noqa: F401
     LittleBitError,
     BoundStack,
     Stack,
+    auto_regime,
     lib,
     init_dual_svid,
     pack_signs,

@@ -19,7 +19,6 @@ LIB_PATH = os.path.join(HERE, "liblittlebit.so")
 OK, INVALID_ARGUMENT, INVALID_SIGN, ALIGNMENT, UNSUPPORTED, OUT_OF_MEMORY, HIP_ERROR = range(7)
 BF16, FP32, BF16_FP32 = 0, 1, 2   # lb_dtype: element types of (x, y)
 REGIME_AUTO, REGIME_EXACT, REGIME_DECODE, REGIME_PREFILL = 0, 1, 2, 3
-PREFILL_MIN_TOKENS = 64   # LB_PREFILL_MIN_TOKENS
 
 STATUS_NAMES = {OK: "LB_OK", INVALID_ARGUMENT: "LB_ERR_INVALID_ARGUMENT", INVALID_SIGN: "LB_ERR_INVALID_SIGN",
                 ALIGNMENT: "LB_ERR_ALIGNMENT", UNSUPPORTED: "LB_ERR_UNSUPPORTED",
@@ -29,7 +28,8 @@ STATUS_NAMES = {OK: "LB_OK", INVALID_ARGUMENT: "LB_ERR_INVALID_ARGUMENT", INVALI
 # include/littlebit_probe.h is bound in probe.py)
 EXPORTS = [
     "lb_packed_words_per_row", "lb_rank_for_bpw", "lb_pack_signs_host", "lb_pack_signs", "lb_unpack_signs",
-    "lb_linear_create", "lb_linear_forward", "lb_linear_forward_ex", "lb_linear_forward_noalloc", "lb_linear_info",
+    "lb_linear_create", "lb_linear_forward", "lb_linear_forward_ex", "lb_linear_forward_noalloc", "lb_auto_regime",
+    "lb_linear_info",
     "lb_linear_destroy",
     "lb_stack_create", "lb_stack_forward", "lb_stack_forward_ex", "lb_stack_destroy", "lb_status_string",
     "lb_last_error", "lb_init_dual_svid",
@@ -74,6 +74,7 @@ def lib():
         "lb_linear_forward": (C.c_int, [vp, vp, vp, i64, C.c_int, vp]),
         "lb_linear_forward_ex": (C.c_int, [vp, vp, vp, i64, C.c_int, C.c_int, vp]),
         "lb_linear_forward_noalloc": (C.c_int, [vp, vp, vp, i64, C.c_int, vp]),
+        "lb_auto_regime": (C.c_int, [C.POINTER(vp), i32, i64, C.c_int, C.POINTER(C.c_int)]),
         "lb_linear_info": (C.c_int, [vp, C.POINTER(i64), C.POINTER(i64), C.POINTER(i32), C.POINTER(i64),
                                      C.POINTER(i64)]),
         "lb_linear_destroy": (C.c_int, [vp]),
@@ -162,6 +163,15 @@ def init_dual_svid(W, ranks: Sequence[int], stream=None) -> List[Dict]:
     arr = (LbPathInit * len(outs))(*outs)
     _check(lib().lb_init_dual_svid(C.c_void_p(W.data_ptr()), m, n, arr, len(outs), _stream(stream)))
     return paths
+
+
+def auto_regime(linears: Sequence["Linear"], tokens: int, io: int = BF16) -> int:
+    """The regime LB_REGIME_AUTO runs for these linears at `tokens` tokens
+    (lb_auto_regime)."""
+    arr = (C.c_void_p * len(linears))(*[l.handle.value for l in linears])
+    out = C.c_int()
+    _check(lib().lb_auto_regime(arr, len(linears), int(tokens), int(io), C.byref(out)))
+    return out.value
 
 
 def _io_of(x, y) -> int:

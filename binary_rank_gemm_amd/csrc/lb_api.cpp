@@ -193,6 +193,10 @@ struct lb_stack_s {
   int64_t g_tokens = -1;
   int g_io = -1, g_regime = -1;
   hipStream_t last_stream = nullptr;
+  // AUTO's regime for the last (tokens, io) it was asked about
+  int64_t auto_tokens = -1;
+  int auto_io = -1;
+  lb_regime auto_rg = LB_REGIME_DECODE;
 };
 
 namespace {
@@ -478,10 +482,62 @@ lb_status check_io(int64_t tokens, lb_dtype io, lb_regime regime) {
 inline int x_is_fp32(lb_dtype io) { return io == LB_FP32 ? 1 : 0; }
 inline int y_is_fp32(lb_dtype io) { return io == LB_BF16 ? 0 : 1; }
 
-lb_regime pick_regime(int64_t tokens, lb_dtype io, lb_regime regime) {
+// Estimated time (µs) of the decode kernels on `count` linears at T tokens.
+// Per launch sequence of up to 16 tokens: the V stage's and the U stage's
+// sign bytes at rates measured on whole Llama-shaped stacks at 16 tokens on
+// MI355X (V 0.72 µs/MB; U 0.34 µs/MB where a quad's 128-latent units fit the
+// U kernel's registers, 0.76 µs/MB where they do not; sequences of 8 tokens
+// or fewer 0.6 of that), at least 6 µs (one work item's latency), plus 12 µs
+// for the three launches.
+double decode_cost_us(const lb_linear* L, int count, int64_t T) {
+  const int bucket = decode_bucket((int)std::min<int64_t>(T, kDecodeMaxTokens));
+  const int nmax = bucket > 8 ? 6 : 8;   // units a U wave keeps in registers (UShape::NMAX)
+  double us = 0;
+  for (int e = 0; e < count; ++e) {
+    double vb = 0, ub = 0;
+    for (int p = 0; p < L[e]->np; ++p) {
+      vb += (double)L[e]->n * L[e]->r[p] / 8;
+      ub += (double)L[e]->m * L[e]->r[p] / 8;
+    }
+    us += vb * 0.72e-6 + ub * (L[e]->ug.nu <= nmax ? 0.34e-6 : 0.76e-6);
+  }
+  const int64_t launches = (T + kDecodeMaxTokens - 1) / kDecodeMaxTokens;
+  return (double)launches * (std::max(us * (bucket <= 8 ? 0.6 : 1.0), 6.0) + 12.0);
+}
+
+// Estimated time (µs) of the prefill GEMMs on `count` linears at T tokens:
+// the larger of the throughput estimate -- 2.13 ns per (256-column tile,
+// 64-deep K block) of a 64-row stripe and 8.9 ns per tile (measured on the
+// same stacks at 64 tokens); a partial 64-row stripe of at most 32 rows costs
+// 0.9 of a whole one; 256-row stripes (more than kPreSmallMaxTokens tokens)
+// cost 3.2 whole 64-row ones -- and the longest single tile (0.5 µs per K block
+// of both GEMMs), plus 8 µs for the launches.
+double prefill_cost_us(const lb_linear* L, int count, int64_t T) {
+  double stripe = 0, longest = 0;
+  for (int e = 0; e < count; ++e) {
+    const PrefillLayer& P = L[e]->pre;
+    const double t1 = (P.Rp + kPreBN - 1) / kPreBN, t2 = (P.m + kPreBN - 1) / kPreBN;
+    stripe += (t1 * P.kb1 + t2 * P.kb2) * 2.13e-3 + (t1 + t2) * 8.9e-3;
+    longest = std::max(longest, 0.5 * (P.kb1 + P.kb2));
+  }
+  const int bm = prefill_rows_per_tile((int)T);
+  double through;
+  if (bm == kPreBM) {
+    through = stripe * 3.2 * (double)((T + kPreBM - 1) / kPreBM);
+  } else {
+    const int64_t full = T / 64, rest = T % 64;
+    through = stripe * ((double)full + (rest == 0 ? 0.0 : rest <= 32 ? 0.9 : 1.0));
+  }
+  return std::max(through, longest) + 8.0;
+}
+
+// AUTO: fp32 x runs the exact path; bf16 x runs whichever of the decode and
+// prefill kernels the two estimates above make faster for these linears.
+lb_regime pick_regime(const lb_linear* L, int count, int64_t tokens, lb_dtype io, lb_regime regime) {
   if (regime != LB_REGIME_AUTO) return regime;
   if (io == LB_FP32) return LB_REGIME_EXACT;
-  return tokens < LB_PREFILL_MIN_TOKENS ? LB_REGIME_DECODE : LB_REGIME_PREFILL;
+  if (tokens > 4 * kPreSmallMaxTokens) return LB_REGIME_PREFILL;
+  return decode_cost_us(L, count, tokens) <= prefill_cost_us(L, count, tokens) ? LB_REGIME_DECODE : LB_REGIME_PREFILL;
 }
 
 int current_device() {
@@ -698,6 +754,17 @@ lb_status lb_linear_create(int64_t d_out, int64_t d_in, const lb_path* paths, in
   return LB_OK;
 }
 
+lb_status lb_auto_regime(const lb_linear* linears, int32_t count, int64_t tokens, lb_dtype io, lb_regime* out) {
+  if (!linears || !out) return fail(LB_ERR_INVALID_ARGUMENT, "null pointer");
+  if (count < 1) return fail(LB_ERR_INVALID_ARGUMENT, "count must be positive");
+  for (int i = 0; i < count; ++i)
+    if (!linears[i]) return fail(LB_ERR_INVALID_ARGUMENT, "linear %d is null", i);
+  lb_status s = check_io(tokens, io, LB_REGIME_AUTO);
+  if (s != LB_OK) return s;
+  *out = pick_regime(linears, count, tokens, io, LB_REGIME_AUTO);
+  return LB_OK;
+}
+
 lb_status lb_linear_info(lb_linear L, int64_t* d_out, int64_t* d_in, int32_t* n_paths, int64_t* ranks,
                          int64_t* device_bytes) {
   if (!L) return fail(LB_ERR_INVALID_ARGUMENT, "null linear");
@@ -718,21 +785,20 @@ lb_status lb_linear_forward_ex(lb_linear L, const void* x, void* y, int64_t toke
   if (s != LB_OK) return s;
   if (!aligned16(x) || !aligned16(y)) return fail(LB_ERR_ALIGNMENT, "x and y must be 16-byte aligned");
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const lb_regime rg = pick_regime(tokens, io, regime);
+  const lb_regime rg = pick_regime(&L, 1, tokens, io, regime);
   // scratch and plans are rebuilt on the host: order them after the previous call's work
   if (L->last_stream != st && L->last_stream) HIP_TRY(hipStreamSynchronize(L->last_stream));
   L->last_stream = st;
   if (rg == LB_REGIME_EXACT) {
-    int rmax = 0;
-    for (int p = 0; p < L->np; ++p) rmax = std::max(rmax, L->paths[p].r);
-    const int rpad = (rmax + 15) / 16 * 16;
-    const size_t want = exact_scratch_floats(rmax, L->np, tokens, (int)L->n, rpad) * sizeof(float);
+    const size_t want =
+        std::max<size_t>(exact_scratch_floats(L->paths, L->np, tokens, (int)L->n, x_is_fp32(io), y_is_fp32(io)), 64) *
+        sizeof(float);
     if (want > L->zexact.bytes) {
       HIP_TRY(hipStreamSynchronize(st));
       HIP_TRY(L->zexact.ensure(want));
     }
     HIP_TRY(launch_exact(L->paths, L->np, (int)L->m, (int)L->n, x, y, (int)tokens, x_is_fp32(io), y_is_fp32(io),
-                         reinterpret_cast<float*>(L->zexact.ptr), rpad, st));
+                         reinterpret_cast<float*>(L->zexact.ptr), st));
     return LB_OK;
   }
   if (rg == LB_REGIME_DECODE) {
@@ -766,15 +832,12 @@ lb_status lb_linear_forward_noalloc(lb_linear L, const void* x, void* y, int64_t
   if (!L->na_scratch || !L->na_tables) return fail(LB_ERR_UNSUPPORTED, "no scratch was set up for this linear");
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (io == LB_FP32) {
-    int rmax = 0;
-    for (int p = 0; p < L->np; ++p) rmax = std::max(rmax, L->paths[p].r);
-    const int rpad = (rmax + 15) / 16 * 16;
-    const size_t need = exact_scratch_floats(rmax, L->np, tokens, (int)L->n, rpad) * sizeof(float);
+    const size_t need = exact_scratch_floats(L->paths, L->np, tokens, (int)L->n, 1, 1) * sizeof(float);
     if (need > kNoAllocScratchBytes)
       return fail(LB_ERR_UNSUPPORTED, "%lld fp32 tokens need %zu bytes of scratch; the no-allocation forward has %zu",
                   (long long)tokens, need, kNoAllocScratchBytes);
     HIP_TRY(launch_exact(L->paths, L->np, (int)L->m, (int)L->n, x, y, (int)tokens, 1, 1,
-                         reinterpret_cast<float*>(L->na_scratch), rpad, st));
+                         reinterpret_cast<float*>(L->na_scratch), st));
     return LB_OK;
   }
   const int Tplan = (int)std::min<int64_t>(kDecodeMaxTokens, tokens);
@@ -890,12 +953,9 @@ lb_status stack_launch(lb_stack S, lb_regime rg, int64_t tokens, lb_dtype io, hi
   size_t off = 0;
   for (int i = 0; i < count; ++i) {
     lb_linear L = S->linears[i];
-    int rmax = 0;
-    for (int p = 0; p < L->np; ++p) rmax = std::max(rmax, L->paths[p].r);
-    const int rpad = (rmax + 15) / 16 * 16;
     HIP_TRY(launch_exact(L->paths, L->np, (int)L->m, (int)L->n, S->xs_h[i], S->ys_h[i], (int)tokens, x_is_fp32(io),
-                         y_is_fp32(io), reinterpret_cast<float*>(S->zexact.ptr) + off, rpad, st));
-    off += exact_scratch_floats(rmax, L->np, tokens, (int)L->n, rpad);
+                         y_is_fp32(io), reinterpret_cast<float*>(S->zexact.ptr) + off, st));
+    off += exact_scratch_floats(L->paths, L->np, tokens, (int)L->n, x_is_fp32(io), y_is_fp32(io));
   }
   return LB_OK;
 }
@@ -980,11 +1040,8 @@ lb_status stack_prepare(lb_stack S, lb_regime rg, int64_t tokens, lb_dtype io) {
       HIP_TRY(prefill_prepare(G.pplan, G.pre.data(), (int)G.lins.size(), (int)tokens, G.xs_h.data(), G.ys_h.data()));
   } else {
     size_t want = 0;
-    for (lb_linear L : S->linears) {
-      int rmax = 0;
-      for (int p = 0; p < L->np; ++p) rmax = std::max(rmax, L->paths[p].r);
-      want += exact_scratch_floats(rmax, L->np, tokens, (int)L->n, (rmax + 15) / 16 * 16);
-    }
+    for (lb_linear L : S->linears)
+      want += exact_scratch_floats(L->paths, L->np, tokens, (int)L->n, x_is_fp32(io), y_is_fp32(io));
     HIP_TRY(S->zexact.ensure(std::max<size_t>(want, 1) * sizeof(float)));
   }
   return LB_OK;
@@ -1006,7 +1063,13 @@ lb_status lb_stack_forward_ex(lb_stack S, const void* const* xs, void* const* ys
     if (!aligned16(xs[i]) || !aligned16(ys[i])) return fail(LB_ERR_ALIGNMENT, "entry %d: pointer not 16-byte aligned", i);
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const lb_regime rg = pick_regime(tokens, io, regime);
+  // AUTO's choice for these linears, kept per (tokens, io)
+  if (regime == LB_REGIME_AUTO && (S->auto_tokens != tokens || S->auto_io != (int)io)) {
+    S->auto_rg = pick_regime(S->linears.data(), count, tokens, io, LB_REGIME_AUTO);
+    S->auto_tokens = tokens;
+    S->auto_io = (int)io;
+  }
+  const lb_regime rg = regime == LB_REGIME_AUTO ? S->auto_rg : regime;
   const bool same_ptrs = S->xs_h.size() == (size_t)count && std::equal(xs, xs + count, S->xs_h.begin()) &&
                          std::equal(ys, ys + count, S->ys_h.begin());
   const bool same = same_ptrs && S->g_tokens == tokens && S->g_io == (int)io && S->g_regime == (int)rg;
@@ -1066,8 +1129,7 @@ lb_status lb_stack_forward(lb_stack S, const void* const* xs, void* const* ys, i
                            void* stream) {
   // a graph only where launches are many (exact: two per linear); for the
   // decode and prefill kernels a graph replay costs more than it saves
-  const lb_regime rg = pick_regime(tokens, io, LB_REGIME_AUTO);
-  return lb_stack_forward_ex(S, xs, ys, tokens, io, LB_REGIME_AUTO, rg == LB_REGIME_EXACT ? 1 : 0, stream);
+  return lb_stack_forward_ex(S, xs, ys, tokens, io, LB_REGIME_AUTO, io == LB_FP32 ? 1 : 0, stream);
 }
 
 lb_status lb_stack_destroy(lb_stack S) {

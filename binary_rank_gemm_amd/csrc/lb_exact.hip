@@ -1,5 +1,6 @@
-// fp32 forward of one linear with plain vector arithmetic (the fp32-I/O path;
-// it also serves bf16 x with bf16 or fp32 y).
+// fp32 forward of one linear with plain vector arithmetic (the fp32-I/O path
+// for few tokens; it also serves bf16 x with bf16 or fp32 y).  fp32 I/O with
+// many tokens goes to the tiled form in lb_f32gemm.hip.
 //
 // It follows the factorised order of the paper notes ("LittleBit", section
 // "Key design"): per path t = x o g, z = t V, z' = z o l, then
@@ -108,7 +109,12 @@ __global__ void __launch_bounds__(256) k_exact_y(ExactArgs a) {
 }  // namespace
 
 hipError_t launch_exact(const PathDev* p, int np, int m, int n, const void* x, void* y, int T,
-                        int x_fp32, int y_fp32, float* zbuf, int rpad, hipStream_t st) {
+                        int x_fp32, int y_fp32, float* zbuf, hipStream_t st) {
+  if (exact_uses_gemm(T, x_fp32, y_fp32))
+    return launch_f32_gemm(p, np, m, n, reinterpret_cast<const float*>(x), reinterpret_cast<float*>(y), T, zbuf, st);
+  int rpad = 0;
+  for (int i = 0; i < np; ++i) rpad = rpad > p[i].r ? rpad : p[i].r;
+  rpad = (rpad + 15) / 16 * 16;
   ExactArgs a{};
   for (int i = 0; i < np; ++i) a.p[i] = p[i];
   a.x = x; a.y = y; a.zbuf = zbuf; a.np = np; a.m = m; a.n = n; a.T = T; a.rpad = rpad; a.x_fp32 = x_fp32;

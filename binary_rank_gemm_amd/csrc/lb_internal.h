@@ -161,12 +161,29 @@ inline int exact_splits(int rmax, int np, int64_t T, int n) {
   const int64_t most = n / 256 < 1 ? 1 : (n / 256 > 64 ? 64 : n / 256);
   return (int)(want < most ? want : most);
 }
-// Floats of z scratch the exact path needs for one linear: splits x np x T x rpad.
-inline size_t exact_scratch_floats(int rmax, int np, int64_t T, int n, int rpad) {
-  return (size_t)exact_splits(rmax, np, T, n) * np * T * rpad;
+// fp32 I/O with at least this many tokens runs the exact path's tiled form:
+// two fp32 matrix-core contractions (lb_f32gemm.hip) instead of the per-token
+// vector kernels.
+constexpr int kF32GemmMinTokens = 16;
+inline bool exact_uses_gemm(int64_t T, int x_fp32, int y_fp32) {
+  return x_fp32 && y_fp32 && T >= kF32GemmMinTokens;
 }
+// Floats of Z' scratch of the tiled form: T x (r_p rounded up to 32), per path.
+size_t f32_gemm_scratch_floats(const PathDev* p, int np, int64_t T);
+hipError_t launch_f32_gemm(const PathDev* p, int np, int m, int n, const float* x, float* y, int T, float* zbuf,
+                           hipStream_t st);
+// Floats of scratch the exact path needs for one linear: the tiled form's Z',
+// or splits x np x T x rpad latent sums of the vector kernels (rpad = the
+// largest rank rounded up to 16).
+inline size_t exact_scratch_floats(const PathDev* p, int np, int64_t T, int n, int x_fp32, int y_fp32) {
+  if (exact_uses_gemm(T, x_fp32, y_fp32)) return f32_gemm_scratch_floats(p, np, T);
+  int rmax = 0;
+  for (int i = 0; i < np; ++i) rmax = rmax > p[i].r ? rmax : p[i].r;
+  return (size_t)exact_splits(rmax, np, T, n) * np * T * ((rmax + 15) / 16 * 16);
+}
+// the exact path (either form, chosen by exact_uses_gemm)
 hipError_t launch_exact(const PathDev* p, int np, int m, int n, const void* x, void* y, int T,
-                        int x_fp32, int y_fp32, float* zbuf, int rpad, hipStream_t st);
+                        int x_fp32, int y_fp32, float* zbuf, hipStream_t st);
 
 // decode path: V stage, mid stage, U stage, one workgroup per work item
 hipError_t launch_decode_v(const DecArgs& a, int nitems, hipStream_t st);

@@ -10,7 +10,12 @@
 
 namespace lb {
 
-constexpr int kPreBM = 256, kPreBN = 256, kPreBK = 64;   // workgroup tile
+constexpr int kPreBM = 256, kPreBN = 256, kPreBK = 64;   // workgroup tile (rows: kPreBM or 64)
+// Rows per tile of a forward at T tokens: 64-row tiles (two workgroups per
+// CU) up to kPreSmallMaxTokens tokens, so few tokens leave few empty rows;
+// 256-row tiles above.
+constexpr int kPreSmallMaxTokens = 128;
+inline int prefill_rows_per_tile(int T) { return T <= kPreSmallMaxTokens ? 64 : kPreBM; }
 constexpr int kPreWN = 128;                              // wave tile (N) = B tile width in the layouts
 
 // Per-linear device data of the prefill GEMMs (carved from the linear's arena).
@@ -50,6 +55,7 @@ struct PrefillPlan {
   PreEntry* entries_d = nullptr;
   PreItem* items_d = nullptr;       // GEMM1 items (full row stripes, then the partial one), then GEMM2's
   int n1 = 0, n1p = 0, n2 = 0, n2p = 0;
+  int bm = kPreBM;                  // rows per tile (prefill_rows_per_tile(T))
   void* zbuf = nullptr;
   size_t zbytes = 0;
   std::vector<PreEntry> entries_h;

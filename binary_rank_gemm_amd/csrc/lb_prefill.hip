@@ -205,7 +205,7 @@ __device__ inline void vm_wait_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// A tile in LDS: 256 rows x 64 bf16 (128 bytes a row, unpadded), 16-byte
+// A tile in LDS: BM rows x 64 bf16 (128 bytes a row, unpadded), 16-byte
 // chunk c of row r at slot 8 r + (c ^ f(r)), f(r) = (r & 7) ^ ((r >> 3) & 1).
 // A fragment read has lane l32 on row base + l32 (base a multiple of 32), all
 // lanes at the same logical chunk.  f puts any 8 consecutive rows of an
@@ -219,22 +219,25 @@ __device__ inline int a_row_xor(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 __device__ inline int a_slot_row(int s) { return s >> 3; }
 __device__ inline int a_slot_chunk(int s) { return (s & 7) ^ a_row_xor(s >> 3); }
 
-// Wave layout of a 256 x TN workgroup tile: WM x WN waves, each owning
-// (256 / WM) x (TN / WN) outputs as MB x NB blocks of 32 x 32.  TN = 256 for
-// whole tiles; the last column tile of a GEMM whose N leaves only 128 or 64
-// columns in it takes TN = 128 (4 x 2 waves of 64 x 64) or TN = 64 (8 x 1
-// waves of 32 x 64): waves w and w + 4 share a SIMD, so in every layout the
-// four SIMDs get equal shares and a narrow tile takes a fraction of a whole
-// one's time.  STR (GEMM1 only): some wave's columns cross from the primary
+// Wave layout of a BM x TN workgroup tile: WM x WN waves, each owning
+// (BM / WM) x (TN / WN) outputs as MB x NB blocks of 32 x 32.  BM = 256 rows
+// (tokens) when tokens are many; BM = 64 (2 x 4 waves of 32 x 64, two or three
+// workgroups per CU) when they are few, so a row stripe holds no more empty
+// rows than needed.  TN = 256 for whole tiles; with BM = 256, the last column
+// tile of a GEMM whose N leaves only 128 or 64 columns in it takes TN = 128
+// (4 x 2 waves of 64 x 64) or TN = 64 (8 x 1 waves of 32 x 64): waves w and
+// w + 4 share a SIMD, so in every layout the four SIMDs get equal shares and
+// a narrow tile takes a fraction of a whole one's time.  STR (GEMM1 only): some wave's columns cross from the primary
 // path into the residual one, so |g| is chosen per column block.  PART: the
 // tile's rows run past the last token (the last row stripe when T is not a
 // multiple of 256); each wave then reads and multiplies only its 32-row
 // blocks that hold tokens.
-template <int MODE, int WM, int WN, int TN, bool STR, bool PART>
+template <int MODE, int BM, int WM, int WN, int TN, bool STR, bool PART>
 __device__ __forceinline__ void prefill_tile(const PreArgs& a, const PreItem& it) {
   constexpr int kWaves = WM * WN, kNT = 64 * kWaves;
-  constexpr int MB = kPreBM / WM / 32, NB = TN / WN / 32;
-  constexpr int kAI = kPreBM * 8 / kNT;                 // A loads (16 B per lane) per wave per block
+  constexpr int MB = BM / WM / 32, NB = TN / WN / 32;
+  constexpr int kAI = BM * 8 / kNT;                     // A loads (16 B per lane) per wave per block
+  static_assert(MB >= 1 && kAI >= 1, "a wave owns whole 32-row blocks; every wave loads A rows");
   static_assert(kWaves == 8, "eight waves, two per SIMD");
   static_assert(TN / WN == 64, "a wave covers 64 columns (half a 128-column B tile)");
   static_assert(NB == 2 || NB == 4, "a wave covers half or all of a 128-column B tile");
@@ -262,7 +265,7 @@ __device__ __forceinline__ void prefill_tile(const PreArgs& a, const PreItem& it
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
   const int wm = wave / WN, wn = wave % WN;
-  const int m0 = it.mt * kPreBM, n0 = it.nt * kPreBN;
+  const int m0 = it.mt * BM, n0 = it.nt * kPreBN;
   const int l32 = lane & 31, kg = lane >> 5;
   const int wcol = wn * (NB * 32);                       // first column of this wave in the tile
   // row blocks of this wave that hold tokens (all of them unless PART)
@@ -275,8 +278,8 @@ __device__ __forceinline__ void prefill_tile(const PreArgs& a, const PreItem& it
   const bool vec_ok = (lda & 7) == 0;
   const int nkb = (K + kPreBK - 1) / kPreBK;
 
-  // LDS, kPreBufs buffers of: A [256 x 64] bf16 (swizzled) | B words [2 tiles][64 lanes] u32x4 | |g| [2][64] bf16
-  constexpr int kBufA = kPreBM * kPreBK * 2, kBufB = 2 * 64 * 16, kBufG = 2 * kPreBK * 2;
+  // LDS, kPreBufs buffers of: A [BM x 64] bf16 (swizzled) | B words [2 tiles][64 lanes] u32x4 | |g| [2][64] bf16
+  constexpr int kBufA = BM * kPreBK * 2, kBufB = 2 * 64 * 16, kBufG = 2 * kPreBK * 2;
   constexpr int kBuf = kBufA + kBufB + kBufG;
 
   // ---- block loads: rows past T are clamped onto row T - 1 (a row of A only
@@ -526,7 +529,7 @@ __device__ __forceinline__ void prefill_tile(const PreArgs& a, const PreItem& it
   }
   if (c_stage) {
     __syncthreads();
-    constexpr int kChunks = kPreBM * TN / 8;       // 16-byte chunks of the tile
+    constexpr int kChunks = BM * TN / 8;           // 16-byte chunks of the tile
     const int tid_all = threadIdx.x;
 #pragma unroll 4
     for (int c = tid_all; c < kChunks; c += kNT) {
@@ -555,23 +558,27 @@ __device__ __forceinline__ void prefill_tile(const PreArgs& a, const PreItem& it
 // PART: a launch over the tiles of row stripes that run past the last token
 // (a separate launch, so the full tiles' kernel carries none of it).
 // The tile width (it.tn: 256, 128 or 64) picks the wave layout, uniformly
-// over the workgroup.
-template <int MODE, bool STR, bool PART>
+// over the workgroup (64-row tiles take the 256-wide layout only).
+template <int MODE, int BM, bool STR, bool PART>
 __device__ __forceinline__ void prefill_tile_any(const PreArgs& a, const PreItem& it) {
-  if (it.tn == 256) prefill_tile<MODE, 2, 4, 256, STR, PART>(a, it);
-  else if (it.tn == 128) prefill_tile<MODE, 4, 2, 128, STR, PART>(a, it);
-  else prefill_tile<MODE, 8, 1, 64, STR, PART>(a, it);
+  if constexpr (BM == 64) {
+    prefill_tile<MODE, 64, 2, 4, 256, STR, PART>(a, it);
+  } else {
+    if (it.tn == 256) prefill_tile<MODE, BM, 2, 4, 256, STR, PART>(a, it);
+    else if (it.tn == 128) prefill_tile<MODE, BM, 4, 2, 128, STR, PART>(a, it);
+    else prefill_tile<MODE, BM, 8, 1, 64, STR, PART>(a, it);
+  }
 }
 
-template <int MODE, bool PART>
-__global__ void __launch_bounds__(512, 1) k_prefill(PreArgs a) {
+template <int MODE, int BM, bool PART>
+__global__ void __launch_bounds__(512, BM == 64 ? 2 : 1) k_prefill(PreArgs a) {
   const PreItem it = a.items[blockIdx.x];
   if (it.entry < 0) return;
   if constexpr (MODE == 1) {
-    if (it.str) prefill_tile_any<1, true, PART>(a, it);
-    else prefill_tile_any<1, false, PART>(a, it);
+    if (it.str) prefill_tile_any<1, BM, true, PART>(a, it);
+    else prefill_tile_any<1, BM, false, PART>(a, it);
   } else {
-    prefill_tile_any<2, false, PART>(a, it);
+    prefill_tile_any<2, BM, false, PART>(a, it);
   }
 }
 
@@ -594,8 +601,9 @@ bool tile_straddles(const PrefillLayer& L, int nt, int tn) {
   return false;
 }
 constexpr int kThreads = 512;
-constexpr size_t kPreLds = kPreBufs * (size_t)(kPreBM * kPreBK * 2 + 2 * 64 * 16 + 2 * kPreBK * 2);
-static_assert(kPreLds >= (size_t)kPreBM * kPreBN * 2, "the epilogue stages the bf16 tile in the LDS buffers");
+constexpr size_t pre_lds(int bm) { return kPreBufs * (size_t)(bm * kPreBK * 2 + 2 * 64 * 16 + 2 * kPreBK * 2); }
+static_assert(pre_lds(256) >= (size_t)256 * kPreBN * 2, "the epilogue stages the bf16 tile in the LDS buffers");
+static_assert(pre_lds(64) >= (size_t)64 * kPreBN * 2, "the epilogue stages the bf16 tile in the LDS buffers");
 
 }  // namespace
 
@@ -715,7 +723,8 @@ hipError_t prefill_prepare(PrefillPlan& P, const PrefillLayer* const* layers, in
   // all of it has succeeded
   P.T = -1;
   P.count = 0;
-  const int mts = (T + kPreBM - 1) / kPreBM;
+  const int bm = prefill_rows_per_tile(T);
+  const int mts = (T + bm - 1) / bm;
   std::vector<std::vector<PreItem>> s1, s2, s1p, s2p;   // full row stripes, stripes past the last token
   std::vector<double> k1, k2, k1p, k2p;                  // K blocks per tile of each stripe
   size_t zoff = 0;
@@ -728,17 +737,22 @@ hipError_t prefill_prepare(PrefillPlan& P, const PrefillLayer* const* layers, in
     zoff += align256((size_t)T * L.Rp * 2);
     const int nt1 = (L.Rp + kPreBN - 1) / kPreBN, nt2 = (L.m + kPreBN - 1) / kPreBN;
     // work of one row stripe in whole-tile K blocks (a narrow tile counts its share)
+    // (64-row tiles always take the 256-wide layout)
+    auto width = [&](int N, int nt) { return bm == 64 ? kPreBN : tile_width(N, nt); };
     double w1 = 0, w2 = 0;
-    for (int nt = 0; nt < nt1; ++nt) w1 += tile_width(L.Rp, nt) / (double)kPreBN;
-    for (int nt = 0; nt < nt2; ++nt) w2 += tile_width(L.m, nt) / (double)kPreBN;
+    for (int nt = 0; nt < nt1; ++nt) w1 += width(L.Rp, nt) / (double)kPreBN;
+    for (int nt = 0; nt < nt2; ++nt) w2 += width(L.m, nt) / (double)kPreBN;
     for (int mt = 0; mt < mts; ++mt) {
       std::vector<PreItem> a, b;
       for (int nt = 0; nt < nt1; ++nt) {
-        const int tn = tile_width(L.Rp, nt);
+        const int tn = width(L.Rp, nt);
         a.push_back(PreItem{e, mt, nt, tile_straddles(L, nt, tn) ? 1 : 0, tn});
       }
-      for (int nt = 0; nt < nt2; ++nt) b.push_back(PreItem{e, mt, nt, 0, tile_width(L.m, nt)});
-      const bool part = (mt + 1) * kPreBM > T;
+      for (int nt = 0; nt < nt2; ++nt) b.push_back(PreItem{e, mt, nt, 0, width(L.m, nt)});
+      // a stripe past the last token runs the kernel that skips empty 32-row
+      // blocks; with 64-row tiles only when a whole wave's block is empty (the
+      // skipping costs more than it saves otherwise)
+      const bool part = (mt + 1) * bm > T && (bm == kPreBM || T - mt * bm <= 32);
       (part ? s1p : s1).push_back(a);
       (part ? s2p : s2).push_back(b);
       (part ? k1p : k1).push_back(L.kb1 * w1 / nt1);
@@ -783,10 +797,33 @@ hipError_t prefill_prepare(PrefillPlan& P, const PrefillLayer* const* layers, in
   P.n1p = (int)i1p.size();
   P.n2 = (int)i2.size();
   P.n2p = (int)i2p.size();
+  P.bm = bm;
   P.T = T;
   P.count = count;
   return hipSuccess;
 }
+
+namespace {
+
+template <int BM>
+hipError_t launch_gemms(const PrefillPlan& P, PreArgs a, hipStream_t st) {
+  const size_t lds = pre_lds(BM);
+  a.items = P.items_d;
+  if (P.n1 > 0) hipLaunchKernelGGL((k_prefill<1, BM, false>), dim3(P.n1), dim3(kThreads), lds, st, a);
+  a.items = P.items_d + P.n1;
+  if (P.n1p > 0) hipLaunchKernelGGL((k_prefill<1, BM, true>), dim3(P.n1p), dim3(kThreads), lds, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  a.items = P.items_d + P.n1 + P.n1p;
+  if (P.n2 > 0) hipLaunchKernelGGL((k_prefill<2, BM, false>), dim3(P.n2), dim3(kThreads), lds, st, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  a.items = P.items_d + P.n1 + P.n1p + P.n2;
+  if (P.n2p > 0) hipLaunchKernelGGL((k_prefill<2, BM, true>), dim3(P.n2p), dim3(kThreads), lds, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
 
 hipError_t prefill_run(PrefillPlan& P, const PrefillLayer* const* layers, int count, const void* const* xs,
                        void* const* ys, int T, int yf32, hipStream_t st, bool single) {
@@ -811,19 +848,7 @@ hipError_t prefill_run(PrefillPlan& P, const PrefillLayer* const* layers, int co
   a.T = T;
   // GEMM1 over the full row stripes, then over the stripe past the last token;
   // the same for GEMM2
-  a.items = P.items_d;
-  if (P.n1 > 0) hipLaunchKernelGGL((k_prefill<1, false>), dim3(P.n1), dim3(kThreads), kPreLds, st, a);
-  a.items = P.items_d + P.n1;
-  if (P.n1p > 0) hipLaunchKernelGGL((k_prefill<1, true>), dim3(P.n1p), dim3(kThreads), kPreLds, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  a.items = P.items_d + P.n1 + P.n1p;
-  if (P.n2 > 0) hipLaunchKernelGGL((k_prefill<2, false>), dim3(P.n2), dim3(kThreads), kPreLds, st, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  a.items = P.items_d + P.n1 + P.n1p + P.n2;
-  if (P.n2p > 0) hipLaunchKernelGGL((k_prefill<2, true>), dim3(P.n2p), dim3(kThreads), kPreLds, st, a);
-  return hipGetLastError();
+  return P.bm == 64 ? launch_gemms<64>(P, a, st) : launch_gemms<256>(P, a, st);
 }
 
 void prefill_plan_release(PrefillPlan& P) {

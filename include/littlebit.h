@@ -60,21 +60,21 @@ typedef enum {
 typedef enum { LB_BF16 = 0, LB_FP32 = 1, LB_BF16_FP32 = 2 } lb_dtype;
 
 /* Which kernels run a forward.  AUTO picks by tokens and dtype:
- *   fp32 I/O            -> EXACT  (fp32 vector arithmetic end to end);
- *   bf16 x (y bf16 or fp32), tokens <  LB_PREFILL_MIN_TOKENS -> DECODE
- *                          (fused fp8 x fp4 MFMA pass);
- *   bf16 x (y bf16 or fp32), tokens >= LB_PREFILL_MIN_TOKENS -> PREFILL
- *                          (bf16 MFMA GEMMs).
+ *   fp32 I/O -> EXACT (fp32 arithmetic end to end: vector kernels for fewer
+ *               than 16 tokens, fp32 matrix-core contractions from 16 on);
+ *   bf16 x (y bf16 or fp32) -> DECODE (fused fp8 x fp4 MFMA passes of up to
+ *               16 tokens) or PREFILL (bf16 MFMA GEMMs in 64-row tiles up to
+ *               128 tokens, 256-row tiles above), whichever the library's
+ *               cost estimate for these linears at this token count makes
+ *               faster (sign bytes streamed per 16-token pass against GEMM
+ *               tiles and K blocks per row stripe, at rates measured on
+ *               MI355X).  On the Llama-shaped stacks DECODE wins up to 16
+ *               tokens (0.1-0.55 bits per weight) and up to 32 on a
+ *               0.1-bit-per-weight Llama-2-70B stack.
  * Forcing a regime is for tests and measurements; every regime accepts every
  * token count.  DECODE and PREFILL require bf16 x (LB_BF16 or LB_BF16_FP32). */
 typedef enum { LB_REGIME_AUTO = 0, LB_REGIME_EXACT = 1, LB_REGIME_DECODE = 2,
                LB_REGIME_PREFILL = 3 } lb_regime;
-
-/* From this many tokens AUTO runs the prefill GEMMs (256-row tiles, so their
- * time is flat below 256 tokens) instead of 16-token decode slices: the two
- * cross near 50 tokens on a 0.55-bit-per-weight Llama-2-13B stack and near 90
- * on a 0.1-bit-per-weight Llama-2-70B stack. */
-#define LB_PREFILL_MIN_TOKENS 64
 
 /* Limits (LB_ERR_UNSUPPORTED beyond them). */
 #define LB_MAX_DIM    (1 << 20)   /* d_in, d_out                */
@@ -163,6 +163,13 @@ lb_status lb_linear_forward_ex(lb_linear L, const void* x, void* y, int64_t toke
  * writes every value it reads back. */
 lb_status lb_linear_forward_noalloc(lb_linear L, const void* x, void* y, int64_t tokens, lb_dtype io,
                                     void* stream);
+
+/* The regime LB_REGIME_AUTO runs for these `count` linears (one linear, or
+ * the linears of a stack, in which case every entry runs that regime) at
+ * `tokens` tokens and element types `io`, into *out.  Host only: no device
+ * work.  LB_ERR_INVALID_ARGUMENT for null pointers, count < 1, tokens < 1 or
+ * an unknown io. */
+lb_status lb_auto_regime(const lb_linear* linears, int32_t count, int64_t tokens, lb_dtype io, lb_regime* out);
 
 /* Shape of a linear; any output pointer may be NULL.  ranks receives n_paths
  * values; device_bytes is the library-owned device memory of the linear. */

@@ -131,7 +131,18 @@ def test_argument_validation_before_any_device_work():
 
 def test_binding_constants_match_header():
     hdr = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "littlebit.h")).read()
-    assert int(re.search(r"#define LB_PREFILL_MIN_TOKENS (\d+)", hdr).group(1)) == lb.PREFILL_MIN_TOKENS
+    regimes = dict(re.findall(r"LB_REGIME_(\w+) = (\d+)", hdr))
+    assert {k: int(v) for k, v in regimes.items()} == {"AUTO": lb.REGIME_AUTO, "EXACT": lb.REGIME_EXACT,
+                                                      "DECODE": lb.REGIME_DECODE, "PREFILL": lb.REGIME_PREFILL}
+    dtypes = dict(re.findall(r"LB_(BF16|FP32|BF16_FP32) = (\d+)", hdr))
+    assert {k: int(v) for k, v in dtypes.items()} == {"BF16": lb.BF16, "FP32": lb.FP32, "BF16_FP32": lb.BF16_FP32}
+    L = lb.lib()
+    out = C.c_int(-1)
+    assert L.lb_auto_regime(None, 1, 4, 0, C.byref(out)) == lb._binding.INVALID_ARGUMENT
+    one = (C.c_void_p * 1)(None)
+    assert L.lb_auto_regime(one, 1, 4, 0, C.byref(out)) == lb._binding.INVALID_ARGUMENT
+    assert L.lb_auto_regime(one, 0, 4, 0, C.byref(out)) == lb._binding.INVALID_ARGUMENT
+    assert out.value == -1
 
 
 def test_binding_io_types():

@@ -16,7 +16,7 @@ import pytest
 import binary_rank_gemm_amd as lb
 import oracle
 import synth
-from lbtest import assert_bf16_close, log, to_f64, x_f64, x_tensor
+from lbtest import assert_bf16_close, assert_fp32_close, log, to_f64, x_f64, x_tensor
 
 pytestmark = pytest.mark.gpu
 
@@ -140,3 +140,19 @@ def test_full_70b_layer_t64_auto_all_rows():
         st = assert_bf16_close(to_f64(y), ref, f"70B layer {layer} {s.name} T={T} AUTO")
         log(f"  {s.name:5s} {s.m}x{s.n}: E_rms {st['erms']:.2e} E_max/rms {st['emax_rel_rms']:.2e}")
     S.close()
+
+
+def test_full_13b_gate_fp32_tiled_t2048():
+    """A Llama-2-13B-shaped gate projection (13824 x 5120, rank 1027 per path)
+    with fp32 I/O at 2048 tokens: the tiled fp32 form against the oracle on
+    every output, at the fp32 bound max|y - y_ref| <= 1e-5 rms(y_ref)."""
+    wl = synth.WORKLOADS["llama2-13b-0.55bpw"]
+    s = wl.mats[4]
+    T = 2048
+    p = synth.layer_tensors(wl.wid, 5, 4, s.m, s.n, ranks(wl, s))
+    x = synth.activations((wl.wid, 5, 4, 77, T), T, s.n, io="fp32")
+    lin = lb.Linear.from_numpy(s.m, s.n, p)
+    y = lin.forward(x_tensor(x))
+    torch.cuda.synchronize()
+    st = assert_fp32_close(to_f64(y), oracle.forward(x_f64(x), p, s.m, s.n), "13B gate fp32 T=2048")
+    log(f"13B gate fp32 T=2048: E_max/rms {st['emax_rel_rms']:.2e}")

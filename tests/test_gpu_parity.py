@@ -113,6 +113,39 @@ def test_exact_fp32_ragged(m, n, ranks, T):
     assert_fp32_close(to_f64(y), oracle.forward(x_f64(x), paths, m, n), "ragged fp32")
 
 
+@pytest.mark.parametrize("m,n,ranks,T", [(300, 700, [37, 45], 40), (1000, 1200, [149, 102], 130),
+                                         (513, 257, [33, 31], 200), (96, 4100, [1], 16), (4096, 1024, [246, 246], 300)])
+def test_exact_fp32_tiled_form(m, n, ranks, T):
+    """fp32 I/O with 16 tokens or more runs the tiled fp32 matrix-core form:
+    ragged tokens (128-row tiles), ragged n (n % 4 != 0: element-wise loads),
+    ranks not a multiple of 32, one path."""
+    log(f"exact fp32 tiled m={m} n={n} ranks={ranks} T={T}")
+    paths = seeded_paths((36, m, n), m, n, ranks)
+    x = synth.activations((36, T, n), T, n, io="fp32")
+    y = build(m, n, paths).forward(x_tensor(x))
+    torch.cuda.synchronize()
+    s = assert_fp32_close(to_f64(y), oracle.forward(x_f64(x), paths, m, n), "tiled fp32")
+    log(f"  E_max/rms = {s['emax_rel_rms']:.2e}")
+
+
+def test_exact_fp32_tiled_integer_probe_bit_exact():
+    """The tiled form with integer inputs whose every partial sum stays below
+    2^22: exact in fp32 whatever the order, so equal to the oracle bit for bit."""
+    rng = np.random.default_rng(37)
+    m, n, ranks, T = 300, 2048, [64, 40], 150
+    paths = []
+    for p, r in enumerate(ranks):
+        paths.append(dict(rank=r, u_words=synth.sign_words((37, p, 0), m, r), v_words=synth.sign_words((37, p, 1), n, r),
+                          h=f16bits(rng.choice([1.0, -2.0], m)), g=f16bits(rng.choice([-1.0, 2.0], n)),
+                          l=f16bits(rng.choice([1.0, 2.0], r))))
+    x = rng.integers(-2, 3, size=(T, n)).astype(np.float32)
+    y_ref = oracle.forward(x.astype(np.float64), paths, m, n)
+    assert np.max(np.abs(y_ref)) < 2 ** 22
+    y = build(m, n, paths).forward(torch.from_numpy(x).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(to_f64(y), y_ref)
+
+
 # ----------------------------------------------------------------------------
 # decode path (bf16)
 # ----------------------------------------------------------------------------
@@ -172,7 +205,8 @@ def test_prefill_identity_probe_many_tokens_bit_exact():
     assert np.array_equal(to_f64(y), oracle.forward(x_f64(x), paths, m, n))
 
 
-@pytest.mark.parametrize("m,n,ranks", [(300, 320, [20, 40]), (640, 384, [270, 20]), (1000, 320, [149, 102])])
+@pytest.mark.parametrize("m,n,ranks", [(300, 320, [20, 40]), (640, 384, [270, 20]), (1000, 320, [149, 102]),
+                                       (300, 100, [20, 40]), (640, 128, [149, 102])])
 def test_prefill_identity_probe_narrow_tiles_bit_exact(m, n, ranks):
     """x = I_n with unit scales through the prefill GEMMs at shapes whose last
     column tiles are 128 or 64 wide (GEMM1 N = the concatenated padded rank,
@@ -293,7 +327,7 @@ def test_bf16_in_fp32_out(regime, m, n, ranks, T):
     assert torch.equal(yf.to(torch.bfloat16).view(torch.int16), yb.view(torch.int16))
 
 
-@pytest.mark.parametrize("regime,T", [(lb.REGIME_DECODE, 4), (lb.REGIME_PREFILL, 256)])
+@pytest.mark.parametrize("regime,T", [(lb.REGIME_DECODE, 4), (lb.REGIME_PREFILL, 256), (lb.REGIME_PREFILL, 72)])
 def test_stack_bf16_in_fp32_out(regime, T):
     shapes = [(256, 512, [16, 16]), (1024, 300, [33, 20]), (96, 96, [5])]
     lins, paths, xs = make_stack(32, shapes, T)
@@ -390,7 +424,7 @@ def chained_stack(key, layers, T, io):
 
 @pytest.mark.parametrize("regime,T,io", [(lb.REGIME_DECODE, 1, "bf16"), (lb.REGIME_DECODE, 16, "bf16"),
                                          (lb.REGIME_DECODE, 40, "bf16"), (lb.REGIME_PREFILL, 200, "bf16"),
-                                         (lb.REGIME_EXACT, 3, "fp32")])
+                                         (lb.REGIME_EXACT, 3, "fp32"), (lb.REGIME_EXACT, 24, "fp32")])
 def test_stack_chained_in_model_order(regime, T, io):
     """Each entry sees its producer's finished output: every link matches the
     oracle applied to the input the entry actually read, graph and direct
@@ -424,6 +458,32 @@ def test_stack_chained_in_model_order(regime, T, io):
             assert torch.equal(runs[0][i].view(bits), ys[i].view(bits)), f"stack != singles, entry {i}"
 
 
+@pytest.mark.parametrize("T", [1, 16, 40, 100, 300])
+def test_stack_auto_runs_the_regime_it_reports(T):
+    """lb_auto_regime names the regime a stack forward in AUTO runs: the AUTO
+    outputs equal the forced regime's bit for bit, and match the oracle; few
+    tokens run the decode kernels, many the prefill GEMMs."""
+    lins, paths, xs = make_stack(38, STACK_SHAPES, T)
+    rg = lb.auto_regime(lins, T)
+    log(f"stack AUTO T={T}: regime {rg}")
+    assert rg in (lb.REGIME_DECODE, lb.REGIME_PREFILL)
+    if T == 1:
+        assert rg == lb.REGIME_DECODE
+    if T == 300:
+        assert rg == lb.REGIME_PREFILL
+    xd = [x_tensor(x) for x in xs]
+    ya = [torch.empty((T, m), dtype=torch.bfloat16, device="cuda") for m, _, _ in STACK_SHAPES]
+    yb = [torch.empty_like(y) for y in ya]
+    S = lb.Stack(lins)
+    S.forward(xd, ya)
+    S.forward(xd, yb, regime=rg, use_graph=False)
+    torch.cuda.synchronize()
+    for i, (m, n, _) in enumerate(STACK_SHAPES):
+        assert torch.equal(ya[i].view(torch.int16), yb[i].view(torch.int16)), f"entry {i}"
+        assert_bf16_close(to_f64(ya[i]), oracle.forward(x_f64(xs[i]), paths[i], m, n), f"AUTO entry {i}")
+    S.close()
+
+
 @pytest.mark.parametrize("regime", [lb.REGIME_DECODE, lb.REGIME_PREFILL])
 def test_stack_refuses_output_over_own_input(regime):
     """An entry whose y overlaps its own x is refused, also when the same bad
@@ -451,8 +511,8 @@ def test_stack_refuses_output_over_own_input(regime):
     S.close()
 
 
-def test_stack_exact_fp32_matches_single():
-    T = 3
+@pytest.mark.parametrize("T", [3, 40])
+def test_stack_exact_fp32_matches_single(T):
     lins, paths, xs = make_stack(28, STACK_SHAPES[:4], T, io="fp32")
     S = lb.Stack(lins)
     xd = [x_tensor(x) for x in xs]
@@ -481,6 +541,11 @@ PREFILL_SHAPES = [
     (4096, 14336, [478, 478], 256),      # long K: many blocks through the LDS pipeline
     (700, 520, [20, 40], 300),           # GEMM1: one 128-wide tile whose first wave spans both paths
     (640, 384, [270, 20], 260),          # GEMM1: a 64-wide last tile spanning both paths; GEMM2: 128-wide last tile
+    # at most 128 tokens: 64-row tiles
+    (1000, 1200, [149, 102], 16),        # one partial 64-row stripe
+    (4096, 1024, [46, 46], 64),          # one full stripe
+    (700, 520, [20, 40], 100),           # a full and a partial stripe; a wave's columns in both paths
+    (513, 257, [33, 31], 128),           # two full stripes, element-wise A loads (n % 8 != 0)
 ]
 
 
@@ -498,8 +563,8 @@ def test_prefill_parity(m, n, ranks, T):
         y2 = lin.forward(x_tensor(x), regime=lb.REGIME_PREFILL)
         torch.cuda.synchronize()
         assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
-    # AUTO picks prefill at this token count
-    if T >= lb.PREFILL_MIN_TOKENS:
+    # where AUTO picks prefill at this token count, it runs the same kernels
+    if lb.auto_regime([lin], T) == lb.REGIME_PREFILL:
         y3 = lin.forward(x_tensor(x))
         torch.cuda.synchronize()
         assert torch.equal(y.view(torch.int16), y3.view(torch.int16))
@@ -516,8 +581,8 @@ def test_prefill_token_count_changes():
         assert_bf16_close(to_f64(y), oracle.forward(x_f64(x), paths, m, n), f"prefill T={T}")
 
 
-def test_stack_prefill_graph_eager_single_agree():
-    T = 300
+@pytest.mark.parametrize("T", [300, 90])
+def test_stack_prefill_graph_eager_single_agree(T):
     log(f"stack prefill T={T}")
     lins, paths, xs = make_stack(32, STACK_SHAPES, T)
     S = lb.Stack(lins)

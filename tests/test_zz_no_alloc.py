@@ -37,7 +37,7 @@ def layer(key, m, n, ranks):
 CASES = {
     "bf16": [(1000, 1200, [149, 102], 9), (300, 520, [37, 45], 3), (1000, 1200, [149, 102], 1)],
     "bf16_fp32": [(1024, 4096, [246, 246], 16), (640, 384, [20], 5)],
-    "fp32": [(777, 2100, [319, 5], 6), (300, 700, [37, 45], 2)],
+    "fp32": [(1000, 1200, [149, 102], 40), (777, 2100, [319, 5], 6), (300, 700, [37, 45], 2)],
     "long": [(4096, 1024, [46, 46], 40), (513, 257, [33, 31], 17)],   # several 16-token launches
 }
 
