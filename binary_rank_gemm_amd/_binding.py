@@ -14,7 +14,8 @@ from typing import Dict, List, Optional, Sequence
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "liblittlebit.so")
+# LITTLEBIT_LIB names another build of the library (e.g. the host-sanitized one)
+LIB_PATH = os.environ.get("LITTLEBIT_LIB") or os.path.join(HERE, "liblittlebit.so")
 
 OK, INVALID_ARGUMENT, INVALID_SIGN, ALIGNMENT, UNSUPPORTED, OUT_OF_MEMORY, HIP_ERROR = range(7)
 BF16, FP32, BF16_FP32 = 0, 1, 2   # lb_dtype: element types of (x, y)

@@ -467,12 +467,26 @@ hipError_t build_noalloc_tables(lb_linear L, hipStream_t st) {
   return e;
 }
 
-lb_status check_io(int64_t tokens, lb_dtype io, lb_regime regime) {
+// The integer a caller passed for an enum parameter.  A C caller may pass any
+// int; in C++ reading an enum object that holds a value outside its
+// enumerators' range is undefined, so the ABI reads the bytes and checks them
+// before any value is used as the enum.
+template <class E>
+inline int enum_bits(const E& e) {
+  static_assert(sizeof(E) == sizeof(int), "enums of the ABI are int-sized");
+  int v;
+  std::memcpy(&v, &e, sizeof v);
+  return v;
+}
+
+lb_status check_io(int64_t tokens, const lb_dtype& io_arg, const lb_regime& regime_arg) {
   if (tokens <= 0) return fail(LB_ERR_INVALID_ARGUMENT, "tokens must be positive (got %lld)", (long long)tokens);
   if (tokens > LB_MAX_TOKENS) return fail(LB_ERR_UNSUPPORTED, "tokens %lld exceeds %d", (long long)tokens, LB_MAX_TOKENS);
+  const int io = enum_bits(io_arg), regime = enum_bits(regime_arg);
   if (io != LB_BF16 && io != LB_FP32 && io != LB_BF16_FP32)
-    return fail(LB_ERR_INVALID_ARGUMENT, "io must be LB_BF16, LB_FP32 or LB_BF16_FP32");
-  if (regime < LB_REGIME_AUTO || regime > LB_REGIME_PREFILL) return fail(LB_ERR_INVALID_ARGUMENT, "unknown regime");
+    return fail(LB_ERR_INVALID_ARGUMENT, "io must be LB_BF16, LB_FP32 or LB_BF16_FP32 (got %d)", io);
+  if (regime < LB_REGIME_AUTO || regime > LB_REGIME_PREFILL)
+    return fail(LB_ERR_INVALID_ARGUMENT, "unknown regime %d", regime);
   if (io == LB_FP32 && (regime == LB_REGIME_DECODE || regime == LB_REGIME_PREFILL))
     return fail(LB_ERR_UNSUPPORTED, "the decode and prefill kernels read bf16 x; fp32 x runs the exact kernels");
   return LB_OK;
@@ -553,8 +567,8 @@ int current_device() {
 // ---------------------------------------------------------------------------
 extern "C" {
 
-const char* lb_status_string(lb_status s) {
-  switch (s) {
+const char* lb_status_string(lb_status s_arg) {
+  switch (enum_bits(s_arg)) {
     case LB_OK: return "ok";
     case LB_ERR_INVALID_ARGUMENT: return "invalid argument";
     case LB_ERR_INVALID_SIGN: return "sign value outside {-1, +1}";
@@ -1129,7 +1143,7 @@ lb_status lb_stack_forward(lb_stack S, const void* const* xs, void* const* ys, i
                            void* stream) {
   // a graph only where launches are many (exact: two per linear); for the
   // decode and prefill kernels a graph replay costs more than it saves
-  return lb_stack_forward_ex(S, xs, ys, tokens, io, LB_REGIME_AUTO, io == LB_FP32 ? 1 : 0, stream);
+  return lb_stack_forward_ex(S, xs, ys, tokens, io, LB_REGIME_AUTO, enum_bits(io) == LB_FP32 ? 1 : 0, stream);
 }
 
 lb_status lb_stack_destroy(lb_stack S) {

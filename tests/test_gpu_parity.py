@@ -394,6 +394,45 @@ def test_stack_decode_graph_eager_single_agree(T):
             assert torch.equal(ys_g[i].view(torch.int16), ref[i].view(torch.int16)), f"replay {rep} entry {i}"
 
 
+# Stack shapes in whole 64-row quads of y, rows of x read with 16-byte loads
+FLOW_SHAPES = [(256, 512, [16, 16]), (1024, 320, [33, 20]), (192, 2048, [102, 90]), (4096, 1024, [46, 46]),
+               (64, 64, [5]), (704, 704, [149, 149])]
+
+
+@pytest.mark.parametrize("T", [1, 5, 16])
+def test_stack_decode_repeated_steps_and_token_change(T):
+    """Decode steps of one stack: every entry against the oracle, direct
+    launches and a captured graph equal bit for bit over repeated steps, and a
+    token-count change (the plan is rebuilt) and back gives the same outputs."""
+    log(f"decode stack repeated steps T={T}")
+    lins, paths, xs = make_stack(39, FLOW_SHAPES, T)
+    S = lb.Stack(lins)
+    xd = [x_tensor(x) for x in xs]
+    runs = []
+    for g in (False, True, False):
+        ys = [torch.full((T, m), 9.0, dtype=torch.bfloat16, device="cuda") for m, _, _ in FLOW_SHAPES]
+        for _ in range(3):
+            S.forward(xd, ys, regime=lb.REGIME_DECODE, use_graph=g)
+        torch.cuda.synchronize()
+        runs.append(ys)
+    for i, (m, n, _) in enumerate(FLOW_SHAPES):
+        assert_bf16_close(to_f64(runs[0][i]), oracle.forward(x_f64(xs[i]), paths[i], m, n), f"dataflow entry {i}")
+        for r in runs[1:]:
+            assert torch.equal(runs[0][i].view(torch.int16), r[i].view(torch.int16)), f"entry {i} differs between runs"
+    # another token count on the same stack, then back
+    T2 = 2 if T != 2 else 3
+    x2 = [x_tensor(synth.activations((39, i, T2), T2, n)) for i, (_, n, _) in enumerate(FLOW_SHAPES)]
+    y2 = [torch.empty((T2, m), dtype=torch.bfloat16, device="cuda") for m, _, _ in FLOW_SHAPES]
+    S.forward(x2, y2, regime=lb.REGIME_DECODE)
+    ys = [torch.empty((T, m), dtype=torch.bfloat16, device="cuda") for m, _, _ in FLOW_SHAPES]
+    S.forward(xd, ys, regime=lb.REGIME_DECODE)
+    torch.cuda.synchronize()
+    for i, (m, n, _) in enumerate(FLOW_SHAPES):
+        assert torch.equal(ys[i].view(torch.int16), runs[0][i].view(torch.int16)), f"entry {i} after T change"
+        assert_bf16_close(to_f64(y2[i]), oracle.forward(to_f64(x2[i]), paths[i], m, n), f"T={T2} entry {i}")
+    S.close()
+
+
 # A model's linears in their real order, chained through their buffers: per
 # layer q, k, v read the layer input; o reads q's output; gate and up read o's
 # output; down reads gate's output; the next layer's q, k, v read down's
