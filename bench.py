@@ -214,7 +214,8 @@ def achievable_peaks(torch):
     out["launch_floor_us"] = replay_stats(g.replay, torch, n=50)["p50"]
     big = torch.ones(1 << 30, dtype=torch.float32, device="cuda")
     import binary_rank_gemm_amd.probe as probe
-    t = timed_calls(lambda: probe.stream_read(big), 10, torch)
+    settle(lambda: probe.stream_read(big), 0.5, torch)
+    t = timed_calls(lambda: probe.stream_read(big), 20, torch)
     out["probe_read_gbps"] = round(big.numel() * 4 / t / 1e9, 1)
     t = timed_calls(lambda: big.sum(), 10, torch)
     out["sum_read_gbps"] = round(big.numel() * 4 / t / 1e9, 1)
