@@ -241,7 +241,7 @@ hipError_t upload(Item** dst, const std::vector<Item>& v) {
 // Host side of a decode plan for `count` linears at `T` tokens per launch:
 // the kernels' tables and the scratch they need.
 //   V items: each path's column tiles in groups of at most decode_v_tiles, each
-//     group's 128-row chunks cut into ranges of about kDecodeVItemBytes of sign
+//     group's 128-row chunks cut into ranges of about decode_v_item_bytes of sign
 //     words (at least 4 chunks, one per wave, where the path has them).
 //   mid items: one per (entry, path).
 //   U items: runs of 4 qw quads, qw quads per wave, about kDecodeUItemBytes.
@@ -282,7 +282,8 @@ void plan_decode_host(DecodeHostPlan& H, const lb_linear* L, int count, int T, c
     utotal += (double)L[e]->ug.nq * (L[e]->ug.qbytes + 256.0);
   }
   constexpr double kMinItemBytes = 16 * 1024;
-  const double vtarget = std::min<double>(kDecodeVItemBytes, std::max(kMinItemBytes, vtotal / slots_per_launch));
+  const double vtarget =
+      std::min<double>(decode_v_item_bytes(bucket), std::max(kMinItemBytes, vtotal / slots_per_launch));
   const double utarget = std::min<double>(kDecodeUItemBytes, std::max(kMinItemBytes, utotal / slots_per_launch));
   for (int e = 0; e < count; ++e) {
     const lb_linear l = L[e];
@@ -310,7 +311,10 @@ void plan_decode_host(DecodeHostPlan& H, const lb_linear* L, int count, int T, c
         const int tile0 = g * gt, nt = std::min(gt, nct - tile0);
         for (int sp = 0; sp < nsplit; ++sp) {
           const int c0 = (int)((int64_t)E.nkc * sp / nsplit), c1 = (int)((int64_t)E.nkc * (sp + 1) / nsplit);
-          const double cost = (c1 - c0) * (nt * 256.0 + (bucket + 1) * 256.0);
+          // time of the item: its waves' 1 KB ring steps (x / g steps of each
+          // group of chunks, then each chunk's sign steps), per wave
+          const int ch = c1 - c0, grp = bucket == 1 ? (ch + 1) / 2 : ch;
+          const double cost = ((double)grp * ((bucket + 4) / 4) + (double)ch * ((nt + 3) / 4)) / kWavesPerGroup;
           vl.push_back({cost, VItem{e, p, tile0, nt, c0, c1, slots + g * nsplit + sp, 0}});
         }
       }

@@ -495,9 +495,12 @@ __global__ void __launch_bounds__(kThreads, TM >= 16 ? 2 : 3) k_decode_v(DecArgs
   const LB_GLOBAL uint8_t* xb = reinterpret_cast<const LB_GLOBAL uint8_t*>(gp(xv)) + (int64_t)a.t0 * n * 2;
   uint8_t* ring = lds + wave * kRingBytes;
   uint8_t* abuf = lds + kWaves * kRingBytes + wave * TB * kABytes;
-  // this wave's chunks: a contiguous quarter of the item's
-  const int cw = (it.c1 - it.c0 + kWaves - 1) / kWaves;
-  const int ca = min(it.c0 + wave * cw, it.c1), cb = min(ca + cw, it.c1);
+  // this wave's chunks: a contiguous quarter of the item's, the quarters as
+  // even as whole groups of chunks allow (groups of two at one token)
+  constexpr int GV = TM == 1 ? 2 : 1;
+  const int ngrp = (it.c1 - it.c0 + GV - 1) / GV;
+  const int ca = min(it.c0 + GV * (wave * ngrp / kWaves), it.c1);
+  const int cb = min(it.c0 + GV * ((wave + 1) * ngrp / kWaves), it.c1);
 
   v4f acc[CT][TB];
 #pragma unroll

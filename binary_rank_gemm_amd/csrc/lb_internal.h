@@ -139,7 +139,10 @@ __host__ __device__ inline constexpr int decode_slot_floats(int bucket) {
 // its outputs in LDS: 2 KB, or 8 KB at 16 tokens where fewer items fit a CU).
 __host__ __device__ inline constexpr int decode_u_qw_max(int bucket) { return bucket >= 16 ? 4 : 16 / bucket; }
 // Sizes the planner aims at per V and U work item (bytes of sign words).
-constexpr int kDecodeVItemBytes = 192 * 1024;
+// From 4 tokens on a V item's partial slot is large (20 KB at 16 tokens), so
+// fewer, larger items pay: measured on the Llama-2-70B stack, 384 KB items
+// take 2-4 % off the launches of 4, 8 and 16 tokens and add 2 % at one token.
+__host__ __device__ inline constexpr int decode_v_item_bytes(int bucket) { return bucket >= 4 ? 384 * 1024 : 192 * 1024; }
 constexpr int kDecodeUItemBytes = 192 * 1024;
 
 // ---------------------------------------------------------------------------
