@@ -547,7 +547,7 @@ def run_prefill(args, lb, torch, workload):
         wl = dataclasses.replace(wl, layers=min(args.layers, wl.layers))
     S = lb.Stack(lins)
     fn = S.bind(xs, ys).forward
-    settle(fn, 0.3, torch)
+    settle(fn, min(0.3, args.settle_s), torch)
     steps = max(10, args.steps // 10)
     wall, kern_ms = time_steps(fn, steps, 2, torch)
     byts, flops = algorithmic(wl, ranks_of, T)
@@ -606,6 +606,8 @@ def main():
                     help="regime of the headline stack's timed steps (auto: the library's choice)")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-only", action="store_true", help="time only the prefill stack (for profiling)")
+    ap.add_argument("--fp32-tiled-only", action="store_true",
+                    help="time only the fp32 tiled (exact regime, many tokens) stack (for profiling)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-context", action="store_true",
                     help="skip the launch-form and replay timings, the token sweep, the other stacks, the "
@@ -634,6 +636,11 @@ def main():
         del src, dst
         log(f"copy probe: {nb} bytes read + {nb} bytes written")
 
+    if args.fp32_tiled_only:
+        rec = run_fp32_tiled(lb, torch)
+        log(f"fp32 tiled: {rec}")
+        print(json.dumps({"fp32_tiled": rec}), flush=True)
+        return
     if args.prefill_only:
         # a prefill workload named by --workload, else the 13B stack at 2048 tokens
         wk = args.workload if WORKLOADS[args.workload][2] == "prefill" else "llama2-13b-prefill-t2048"
