@@ -132,7 +132,12 @@ lb_status lb_unpack_signs(const uint32_t* packed, int64_t rows, int64_t rank, in
 lb_status lb_linear_create(int64_t d_out, int64_t d_in, const lb_path* paths, int32_t n_paths,
                            void* stream, lb_linear* out);
 
-/* y = x W^T for `tokens` rows.  x and y are device pointers (element types
+/* y = x W^T for `tokens` rows, W the sum over the paths of
+ * diag(h) U diag(l) V^T diag(g) ("LittleBit: Ultra Low-Bit Quantization via
+ * Latent Factorization" paper notes, section "Key design" for one path and
+ * section "Residual compensation" for the sum), computed in the factored
+ * order the same section gives (element-wise scales around two binary matrix
+ * products; W is never formed).  x and y are device pointers (element types
  * per `io`), borrowed until the stream work completes.  Runs the kernels of
  * LB_REGIME_AUTO.  Concurrent forwards of the same linear must be ordered on
  * one stream (they share the linear's scratch memory). */
@@ -186,7 +191,10 @@ lb_status lb_linear_destroy(lb_linear L);
 lb_status lb_stack_create(const lb_linear* linears, int32_t count, lb_stack* out);
 
 /* Runs every linear i of the stack, in order: ys[i] = xs[i] W_i^T, `tokens`
- * rows each (xs and ys are host arrays of `count` device pointers).  Entries
+ * rows each (xs and ys are host arrays of `count` device pointers), each
+ * W_i the layer of lb_linear_forward -- e.g. the seven linears of every
+ * transformer layer of the models the paper notes evaluate (experiments
+ * section: Llama-2 7B / 13B / 70B, Llama-3 8B).  Entries
  * may be chained through their buffers: when ys[i] overlaps xs[j] or ys[j] of
  * a later entry j, or ys[j] overlaps xs[i], entry j runs after entry i (so a
  * model's linears can be listed in their real order, each reading an earlier
