@@ -444,7 +444,7 @@ def launch_forms(r, lb, torch, steps):
     return {f"{k}_us_per_step": round(v * 1e3, 2) for k, v in med.items()} | {"rounds": 3, "order": "alternating"}
 
 
-def token_sweep(r, lb, torch, tokens=(8, 16, 32, 64), steps=20):
+def token_sweep(r, lb, torch, tokens=(2, 4, 8, 16, 32, 64), steps=20):
     """The same linears at other token counts: the regime AUTO picks, and each
     regime forced, µs per step and per token, with algorithmic GB/s and the
     fraction of the larger of the HBM and MFMA roofline times."""
