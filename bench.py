@@ -10,7 +10,7 @@ HBM before timing starts.
 Prints one JSON line: the decode step's microseconds per token and achieved
 HBM GB/s (algorithmic bytes), the roofline of the dominant kernel, the sign-
 and scale-bit budget of every workload, the token sweep of the same stack
-(8 and 64 tokens), the other stacks (Llama-2-7B at batch 1 warm and cold,
+(2 to 64 tokens, AUTO's choice and both regimes), the other stacks (Llama-2-7B at batch 1 warm and cold,
 Llama-3-8B at 16 tokens), the prefill stack's effective TFLOP/s (Llama-2-13B
 shape, 2048 tokens), the dense and decompress-then-compute comparators, and
 the CPU oracle timed on a bounded sample.
