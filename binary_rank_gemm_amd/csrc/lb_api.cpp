@@ -528,9 +528,10 @@ double decode_cost_us(const lb_linear* L, int count, int64_t T) {
 // the larger of the throughput estimate -- 2.13 ns per (256-column tile,
 // 64-deep K block) of a 64-row stripe and 8.9 ns per tile (measured on the
 // same stacks at 64 tokens); a partial 64-row stripe of at most 32 rows costs
-// 0.9 of a whole one; 256-row stripes (more than kPreSmallMaxTokens tokens)
-// cost 3.2 whole 64-row ones -- and the longest single tile (0.5 µs per K block
-// of both GEMMs), plus 8 µs for the launches.
+// 0.9 of a whole one; a 128-row stripe (65 to 128 tokens) 0.47 of a 64-row
+// one per 32-row block that holds tokens; 256-row stripes (more than
+// kPreSmallMaxTokens tokens) 3.2 whole 64-row ones -- and the longest single
+// tile (0.5 µs per K block of both GEMMs), plus 8 µs for the launches.
 double prefill_cost_us(const lb_linear* L, int count, int64_t T) {
   double stripe = 0, longest = 0;
   for (int e = 0; e < count; ++e) {
@@ -543,6 +544,8 @@ double prefill_cost_us(const lb_linear* L, int count, int64_t T) {
   double through;
   if (bm == kPreBM) {
     through = stripe * 3.2 * (double)((T + kPreBM - 1) / kPreBM);
+  } else if (bm == 128) {
+    through = stripe * 0.47 * (double)((T + 31) / 32);
   } else {
     const int64_t full = T / 64, rest = T % 64;
     through = stripe * ((double)full + (rest == 0 ? 0.0 : rest <= 32 ? 0.9 : 1.0));

@@ -221,9 +221,9 @@ __device__ inline int a_slot_chunk(int s) { return (s & 7) ^ a_row_xor(s >> 3); 
 
 // Wave layout of a BM x TN workgroup tile: WM x WN waves, each owning
 // (BM / WM) x (TN / WN) outputs as MB x NB blocks of 32 x 32.  BM = 256 rows
-// (tokens) when tokens are many; BM = 64 (2 x 4 waves of 32 x 64, two or three
-// workgroups per CU) when they are few, so a row stripe holds no more empty
-// rows than needed.  TN = 256 for whole tiles; with BM = 256, the last column
+// (tokens) when tokens are many; BM = 64 (2 x 4 waves of 32 x 64, two
+// workgroups per CU) or 128 (2 x 4 waves of 64 x 64) when they are few, so a
+// row stripe holds no more empty rows than needed.  TN = 256 for whole tiles; with BM = 256, the last column
 // tile of a GEMM whose N leaves only 128 or 64 columns in it takes TN = 128
 // (4 x 2 waves of 64 x 64) or TN = 64 (8 x 1 waves of 32 x 64): waves w and
 // w + 4 share a SIMD, so in every layout the four SIMDs get equal shares and
@@ -561,8 +561,8 @@ __device__ __forceinline__ void prefill_tile(const PreArgs& a, const PreItem& it
 // over the workgroup (64-row tiles take the 256-wide layout only).
 template <int MODE, int BM, bool STR, bool PART>
 __device__ __forceinline__ void prefill_tile_any(const PreArgs& a, const PreItem& it) {
-  if constexpr (BM == 64) {
-    prefill_tile<MODE, 64, 2, 4, 256, STR, PART>(a, it);
+  if constexpr (BM < kPreBM) {
+    prefill_tile<MODE, BM, 2, 4, 256, STR, PART>(a, it);
   } else {
     if (it.tn == 256) prefill_tile<MODE, BM, 2, 4, 256, STR, PART>(a, it);
     else if (it.tn == 128) prefill_tile<MODE, BM, 4, 2, 128, STR, PART>(a, it);
@@ -571,7 +571,7 @@ __device__ __forceinline__ void prefill_tile_any(const PreArgs& a, const PreItem
 }
 
 template <int MODE, int BM, bool PART>
-__global__ void __launch_bounds__(512, BM == 64 ? 2 : 1) k_prefill(PreArgs a) {
+__global__ void __launch_bounds__(512, BM < kPreBM ? 2 : 1) k_prefill(PreArgs a) {
   const PreItem it = a.items[blockIdx.x];
   if (it.entry < 0) return;
   if constexpr (MODE == 1) {
@@ -604,6 +604,8 @@ constexpr int kThreads = 512;
 constexpr size_t pre_lds(int bm) { return kPreBufs * (size_t)(bm * kPreBK * 2 + 2 * 64 * 16 + 2 * kPreBK * 2); }
 static_assert(pre_lds(256) >= (size_t)256 * kPreBN * 2, "the epilogue stages the bf16 tile in the LDS buffers");
 static_assert(pre_lds(64) >= (size_t)64 * kPreBN * 2, "the epilogue stages the bf16 tile in the LDS buffers");
+static_assert(pre_lds(128) >= (size_t)128 * kPreBN * 2, "the epilogue stages the bf16 tile in the LDS buffers");
+static_assert(2 * pre_lds(128) <= 160 * 1024, "two 128-row workgroups fit a CU's LDS");
 
 }  // namespace
 
@@ -737,8 +739,8 @@ hipError_t prefill_prepare(PrefillPlan& P, const PrefillLayer* const* layers, in
     zoff += align256((size_t)T * L.Rp * 2);
     const int nt1 = (L.Rp + kPreBN - 1) / kPreBN, nt2 = (L.m + kPreBN - 1) / kPreBN;
     // work of one row stripe in whole-tile K blocks (a narrow tile counts its share)
-    // (64-row tiles always take the 256-wide layout)
-    auto width = [&](int N, int nt) { return bm == 64 ? kPreBN : tile_width(N, nt); };
+    // (64- and 128-row tiles always take the 256-wide layout)
+    auto width = [&](int N, int nt) { return bm < kPreBM ? kPreBN : tile_width(N, nt); };
     double w1 = 0, w2 = 0;
     for (int nt = 0; nt < nt1; ++nt) w1 += width(L.Rp, nt) / (double)kPreBN;
     for (int nt = 0; nt < nt2; ++nt) w2 += width(L.m, nt) / (double)kPreBN;
@@ -752,7 +754,7 @@ hipError_t prefill_prepare(PrefillPlan& P, const PrefillLayer* const* layers, in
       // a stripe past the last token runs the kernel that skips empty 32-row
       // blocks; with 64-row tiles only when a whole wave's block is empty (the
       // skipping costs more than it saves otherwise)
-      const bool part = (mt + 1) * bm > T && (bm == kPreBM || T - mt * bm <= 32);
+      const bool part = (mt + 1) * bm > T && (bm != 64 || T - mt * bm <= 32);
       (part ? s1p : s1).push_back(a);
       (part ? s2p : s2).push_back(b);
       (part ? k1p : k1).push_back(L.kb1 * w1 / nt1);
@@ -848,7 +850,7 @@ hipError_t prefill_run(PrefillPlan& P, const PrefillLayer* const* layers, int co
   a.T = T;
   // GEMM1 over the full row stripes, then over the stripe past the last token;
   // the same for GEMM2
-  return P.bm == 64 ? launch_gemms<64>(P, a, st) : launch_gemms<256>(P, a, st);
+  return P.bm == 64 ? launch_gemms<64>(P, a, st) : P.bm == 128 ? launch_gemms<128>(P, a, st) : launch_gemms<256>(P, a, st);
 }
 
 void prefill_plan_release(PrefillPlan& P) {

@@ -580,11 +580,14 @@ PREFILL_SHAPES = [
     (4096, 14336, [478, 478], 256),      # long K: many blocks through the LDS pipeline
     (700, 520, [20, 40], 300),           # GEMM1: one 128-wide tile whose first wave spans both paths
     (640, 384, [270, 20], 260),          # GEMM1: a 64-wide last tile spanning both paths; GEMM2: 128-wide last tile
-    # at most 128 tokens: 64-row tiles
+    # at most 64 tokens: 64-row tiles
     (1000, 1200, [149, 102], 16),        # one partial 64-row stripe
     (4096, 1024, [46, 46], 64),          # one full stripe
-    (700, 520, [20, 40], 100),           # a full and a partial stripe; a wave's columns in both paths
-    (513, 257, [33, 31], 128),           # two full stripes, element-wise A loads (n % 8 != 0)
+    # 65 to 128 tokens: 128-row tiles
+    (700, 520, [20, 40], 100),           # a partial stripe; a wave's columns in both paths
+    (4096, 1024, [46, 46], 128),         # one full 128-row stripe
+    (300, 700, [37, 45], 65),            # one 128-row stripe with a single live row
+    (513, 257, [33, 31], 128),           # a full stripe, element-wise A loads (n % 8 != 0)
 ]
 
 
