@@ -505,7 +505,7 @@ inline int y_is_fp32(lb_dtype io) { return io == LB_BF16 ? 0 : 1; }
 // Per launch sequence of up to 16 tokens: the V stage's and the U stage's
 // sign bytes at rates measured on whole Llama-shaped stacks at 16 tokens on
 // MI355X (V 0.72 µs/MB; U 0.34 µs/MB where a quad's 128-latent units fit the
-// U kernel's registers, 0.76 µs/MB where they do not; sequences of 8 tokens
+// U kernel's registers, 0.95 µs/MB where they do not; sequences of 8 tokens
 // or fewer 0.6 of that), at least 6 µs (one work item's latency), plus 12 µs
 // for the three launches.
 double decode_cost_us(const lb_linear* L, int count, int64_t T) {
@@ -518,39 +518,41 @@ double decode_cost_us(const lb_linear* L, int count, int64_t T) {
       vb += (double)L[e]->n * L[e]->r[p] / 8;
       ub += (double)L[e]->m * L[e]->r[p] / 8;
     }
-    us += vb * 0.72e-6 + ub * (L[e]->ug.nu <= nmax ? 0.34e-6 : 0.76e-6);
+    us += vb * 0.72e-6 + ub * (L[e]->ug.nu <= nmax ? 0.34e-6 : 0.95e-6);
   }
   const int64_t launches = (T + kDecodeMaxTokens - 1) / kDecodeMaxTokens;
   return (double)launches * (std::max(us * (bucket <= 8 ? 0.6 : 1.0), 6.0) + 12.0);
 }
 
 // Estimated time (µs) of the prefill GEMMs on `count` linears at T tokens:
-// the larger of the throughput estimate -- 2.13 ns per (256-column tile,
-// 64-deep K block) of a 64-row stripe and 8.9 ns per tile (measured on the
-// same stacks at 64 tokens); a partial 64-row stripe of at most 32 rows costs
-// 0.9 of a whole one; a 128-row stripe (65 to 128 tokens) 0.47 of a 64-row
-// one per 32-row block that holds tokens; 256-row stripes (more than
-// kPreSmallMaxTokens tokens) 3.2 whole 64-row ones -- and the longest single
-// tile (0.5 µs per K block of both GEMMs), plus 8 µs for the launches.
+// the larger of the throughput estimate and the longest single tile (0.5 µs
+// per K block of both GEMMs), plus 8 µs for the launches.  Throughput, fitted
+// to the benchmark stacks (Llama-2-70B, Llama-2-13B, Llama-3-8B) at 8 to 256
+// tokens: a whole 64-row stripe costs 1.54 ns per (256-column tile, 64-deep K
+// block), 7.4 ns per tile and 57 µs; one with at most 32 tokens 0.72 of the
+// K-block term; a 128-row stripe 1.36 + 0.125 whole 64-row stripes per 32-row
+// block it computes, a 256-row stripe 1.6 + 0.3 per block.
 double prefill_cost_us(const lb_linear* L, int count, int64_t T) {
-  double stripe = 0, longest = 0;
+  double tk = 0, tn = 0, longest = 0;
   for (int e = 0; e < count; ++e) {
     const PrefillLayer& P = L[e]->pre;
     const double t1 = (P.Rp + kPreBN - 1) / kPreBN, t2 = (P.m + kPreBN - 1) / kPreBN;
-    stripe += (t1 * P.kb1 + t2 * P.kb2) * 2.13e-3 + (t1 + t2) * 8.9e-3;
+    tk += t1 * P.kb1 + t2 * P.kb2;
+    tn += t1 + t2;
     longest = std::max(longest, 0.5 * (P.kb1 + P.kb2));
   }
+  const double whole = tk * 1.54e-3 + tn * 7.4e-3 + 57.0, small = tk * 1.54e-3 * 0.72 + tn * 7.4e-3 + 57.0;
   const int bm = prefill_rows_per_tile((int)T);
-  double through;
-  if (bm == kPreBM) {
-    through = stripe * 3.2 * (double)((T + kPreBM - 1) / kPreBM);
-  } else if (bm == 128) {
-    through = stripe * 0.47 * (double)((T + 31) / 32);
-  } else {
-    const int64_t full = T / 64, rest = T % 64;
-    through = stripe * ((double)full + (rest == 0 ? 0.0 : rest <= 32 ? 0.9 : 1.0));
+  double us = 0;
+  for (int64_t m0 = 0; m0 < T; m0 += bm) {
+    const int live = (int)std::min<int64_t>(bm, T - m0);
+    // blocks computed: all of the tile unless the stripe skips empty ones
+    const int blocks = live <= bm - 32 ? (live + 31) / 32 : bm / 32;
+    if (bm == 64) us += live <= 32 ? small : whole;
+    else if (bm == 128) us += whole * (1.36 + 0.125 * blocks);
+    else us += whole * (1.6 + 0.3 * blocks);
   }
-  return std::max(through, longest) + 8.0;
+  return std::max(us, longest) + 8.0;
 }
 
 // AUTO: fp32 x runs the exact path; bf16 x runs whichever of the decode and

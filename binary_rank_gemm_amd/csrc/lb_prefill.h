@@ -11,12 +11,15 @@
 namespace lb {
 
 constexpr int kPreBM = 256, kPreBN = 256, kPreBK = 64;   // workgroup tile (rows: kPreBM, 128 or 64)
-// Rows per tile of a forward at T tokens: 64-row tiles up to 64 tokens and
-// 128-row tiles up to kPreSmallMaxTokens, so few tokens leave few empty rows
-// (measured against 64-row tiles, 128-row ones take 17-24 % off 96 tokens
-// and match them at 128); 256-row tiles above.
+// Rows per tile of a forward at T tokens: 64-row tiles up to 64 tokens,
+// 128-row tiles up to kPreSmallMaxTokens and from 256 tokens on, 256-row tiles
+// in between (a 128-row stripe that runs past the last token costs about as
+// much as a whole one, so 129 to 255 tokens take one 256-row stripe; measured
+// on the Llama-2-13B and Llama-3-8B shapes).
 constexpr int kPreSmallMaxTokens = 128;
-inline int prefill_rows_per_tile(int T) { return T <= 64 ? 64 : T <= kPreSmallMaxTokens ? 128 : kPreBM; }
+inline int prefill_rows_per_tile(int T) {
+  return T <= 64 ? 64 : (T <= kPreSmallMaxTokens || T >= 2 * kPreSmallMaxTokens) ? 128 : kPreBM;
+}
 constexpr int kPreWN = 128;                              // wave tile (N) = B tile width in the layouts
 
 // Per-linear device data of the prefill GEMMs (carved from the linear's arena).

@@ -221,9 +221,9 @@ __device__ inline int a_slot_chunk(int s) { return (s & 7) ^ a_row_xor(s >> 3); 
 
 // Wave layout of a BM x TN workgroup tile: WM x WN waves, each owning
 // (BM / WM) x (TN / WN) outputs as MB x NB blocks of 32 x 32.  BM = 256 rows
-// (tokens) when tokens are many; BM = 64 (2 x 4 waves of 32 x 64, two
-// workgroups per CU) or 128 (2 x 4 waves of 64 x 64) when they are few, so a
-// row stripe holds no more empty rows than needed.  TN = 256 for whole tiles; with BM = 256, the last column
+// (tokens) between 129 and 255 tokens; BM = 64 (1 x 4 waves of 64 x 64) up
+// to 64 tokens and BM = 128 (1 x 4 waves of 128 x 64) otherwise (see
+// prefill_rows_per_tile), so a row stripe holds no more empty rows than needed.  TN = 256 for whole tiles; with BM = 256, the last column
 // tile of a GEMM whose N leaves only 128 or 64 columns in it takes TN = 128
 // (4 x 2 waves of 64 x 64) or TN = 64 (8 x 1 waves of 32 x 64): waves w and
 // w + 4 share a SIMD, so in every layout the four SIMDs get equal shares and
@@ -232,13 +232,21 @@ __device__ inline int a_slot_chunk(int s) { return (s & 7) ^ a_row_xor(s >> 3); 
 // tile's rows run past the last token (the last row stripe when T is not a
 // multiple of 256); each wave then reads and multiplies only its 32-row
 // blocks that hold tokens.
+// Threads of a workgroup: 256-row tiles take eight waves (two per SIMD, one
+// workgroup per CU); 64- and 128-row tiles four waves of 64 x 64 and 128 x 64
+// (one per SIMD, three and two workgroups per CU).  Measured against eight
+// waves of 32 x 64 and 64 x 64, the four-wave forms take 18-29 % off 16 to 64
+// tokens and 19-22 % off 128; 128-row tiles of four waves are also faster
+// than 256-row tiles of eight from 256 tokens on (2048 tokens: 6-11 %).
+constexpr int pre_threads(int bm) { return bm < kPreBM ? 256 : 512; }
+
 template <int MODE, int BM, int WM, int WN, int TN, bool STR, bool PART>
 __device__ __forceinline__ void prefill_tile(const PreArgs& a, const PreItem& it) {
   constexpr int kWaves = WM * WN, kNT = 64 * kWaves;
   constexpr int MB = BM / WM / 32, NB = TN / WN / 32;
   constexpr int kAI = BM * 8 / kNT;                     // A loads (16 B per lane) per wave per block
   static_assert(MB >= 1 && kAI >= 1, "a wave owns whole 32-row blocks; every wave loads A rows");
-  static_assert(kWaves == 8, "eight waves, two per SIMD");
+  static_assert(kWaves == 8 || kWaves == 4, "eight waves (two per SIMD) or four (one per SIMD)");
   static_assert(TN / WN == 64, "a wave covers 64 columns (half a 128-column B tile)");
   static_assert(NB == 2 || NB == 4, "a wave covers half or all of a 128-column B tile");
   static_assert(kWaves >= 3, "waves 0, 1, 2 carry the B words and |g|");
@@ -562,7 +570,7 @@ __device__ __forceinline__ void prefill_tile(const PreArgs& a, const PreItem& it
 template <int MODE, int BM, bool STR, bool PART>
 __device__ __forceinline__ void prefill_tile_any(const PreArgs& a, const PreItem& it) {
   if constexpr (BM < kPreBM) {
-    prefill_tile<MODE, BM, 2, 4, 256, STR, PART>(a, it);
+    prefill_tile<MODE, BM, 1, 4, 256, STR, PART>(a, it);
   } else {
     if (it.tn == 256) prefill_tile<MODE, BM, 2, 4, 256, STR, PART>(a, it);
     else if (it.tn == 128) prefill_tile<MODE, BM, 4, 2, 128, STR, PART>(a, it);
@@ -571,7 +579,7 @@ __device__ __forceinline__ void prefill_tile_any(const PreArgs& a, const PreItem
 }
 
 template <int MODE, int BM, bool PART>
-__global__ void __launch_bounds__(512, BM < kPreBM ? 2 : 1) k_prefill(PreArgs a) {
+__global__ void __launch_bounds__(pre_threads(BM), BM == 64 ? 3 : BM < kPreBM ? 2 : 1) k_prefill(PreArgs a) {
   const PreItem it = a.items[blockIdx.x];
   if (it.entry < 0) return;
   if constexpr (MODE == 1) {
@@ -600,7 +608,6 @@ bool tile_straddles(const PrefillLayer& L, int nt, int tn) {
   }
   return false;
 }
-constexpr int kThreads = 512;
 constexpr size_t pre_lds(int bm) { return kPreBufs * (size_t)(bm * kPreBK * 2 + 2 * 64 * 16 + 2 * kPreBK * 2); }
 static_assert(pre_lds(256) >= (size_t)256 * kPreBN * 2, "the epilogue stages the bf16 tile in the LDS buffers");
 static_assert(pre_lds(64) >= (size_t)64 * kPreBN * 2, "the epilogue stages the bf16 tile in the LDS buffers");
@@ -752,9 +759,9 @@ hipError_t prefill_prepare(PrefillPlan& P, const PrefillLayer* const* layers, in
       }
       for (int nt = 0; nt < nt2; ++nt) b.push_back(PreItem{e, mt, nt, 0, width(L.m, nt)});
       // a stripe past the last token runs the kernel that skips empty 32-row
-      // blocks; with 64-row tiles only when a whole wave's block is empty (the
-      // skipping costs more than it saves otherwise)
-      const bool part = (mt + 1) * bm > T && (bm != 64 || T - mt * bm <= 32);
+      // blocks, when it has one (with none the skipping costs more than it
+      // saves: 112 tokens in one 128-row stripe, 9 % slower)
+      const bool part = (mt + 1) * bm > T && T - mt * bm <= bm - 32;
       (part ? s1p : s1).push_back(a);
       (part ? s2p : s2).push_back(b);
       (part ? k1p : k1).push_back(L.kb1 * w1 / nt1);
@@ -811,17 +818,17 @@ template <int BM>
 hipError_t launch_gemms(const PrefillPlan& P, PreArgs a, hipStream_t st) {
   const size_t lds = pre_lds(BM);
   a.items = P.items_d;
-  if (P.n1 > 0) hipLaunchKernelGGL((k_prefill<1, BM, false>), dim3(P.n1), dim3(kThreads), lds, st, a);
+  if (P.n1 > 0) hipLaunchKernelGGL((k_prefill<1, BM, false>), dim3(P.n1), dim3(pre_threads(BM)), lds, st, a);
   a.items = P.items_d + P.n1;
-  if (P.n1p > 0) hipLaunchKernelGGL((k_prefill<1, BM, true>), dim3(P.n1p), dim3(kThreads), lds, st, a);
+  if (P.n1p > 0) hipLaunchKernelGGL((k_prefill<1, BM, true>), dim3(P.n1p), dim3(pre_threads(BM)), lds, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   a.items = P.items_d + P.n1 + P.n1p;
-  if (P.n2 > 0) hipLaunchKernelGGL((k_prefill<2, BM, false>), dim3(P.n2), dim3(kThreads), lds, st, a);
+  if (P.n2 > 0) hipLaunchKernelGGL((k_prefill<2, BM, false>), dim3(P.n2), dim3(pre_threads(BM)), lds, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   a.items = P.items_d + P.n1 + P.n1p + P.n2;
-  if (P.n2p > 0) hipLaunchKernelGGL((k_prefill<2, BM, true>), dim3(P.n2p), dim3(kThreads), lds, st, a);
+  if (P.n2p > 0) hipLaunchKernelGGL((k_prefill<2, BM, true>), dim3(P.n2p), dim3(pre_threads(BM)), lds, st, a);
   return hipGetLastError();
 }
 
