@@ -220,18 +220,20 @@ __device__ inline int a_slot_row(int s) { return s >> 3; }
 __device__ inline int a_slot_chunk(int s) { return (s & 7) ^ a_row_xor(s >> 3); }
 
 // Wave layout of a BM x TN workgroup tile: WM x WN waves, each owning
-// (BM / WM) x (TN / WN) outputs as MB x NB blocks of 32 x 32.  BM = 256 rows
-// (tokens) between 129 and 255 tokens; BM = 64 (1 x 4 waves of 64 x 64) up
-// to 64 tokens and BM = 128 (1 x 4 waves of 128 x 64) otherwise (see
-// prefill_rows_per_tile), so a row stripe holds no more empty rows than needed.  TN = 256 for whole tiles; with BM = 256, the last column
-// tile of a GEMM whose N leaves only 128 or 64 columns in it takes TN = 128
-// (4 x 2 waves of 64 x 64) or TN = 64 (8 x 1 waves of 32 x 64): waves w and
-// w + 4 share a SIMD, so in every layout the four SIMDs get equal shares and
-// a narrow tile takes a fraction of a whole one's time.  STR (GEMM1 only): some wave's columns cross from the primary
-// path into the residual one, so |g| is chosen per column block.  PART: the
-// tile's rows run past the last token (the last row stripe when T is not a
-// multiple of 256); each wave then reads and multiplies only its 32-row
-// blocks that hold tokens.
+// (BM / WM) x (TN / WN) outputs as MB x NB blocks of 32 x 32, every wave 64
+// columns wide.  BM = 256 rows (tokens) between 129 and 255 tokens, eight
+// waves; BM = 64 up to 64 tokens and BM = 128 otherwise, four waves (see
+// prefill_rows_per_tile), so a row stripe holds no more empty rows than
+// needed.  TN = 256 for whole tiles; the last column tile of a GEMM whose N
+// leaves only 128 or 64 columns in it takes TN = 128 or 64 with the rows
+// split over more waves (BM = 256: 4 x 2 waves of 64 x 64, 8 x 1 of 32 x 64;
+// BM = 128: 2 x 2 of 64 x 64, 4 x 1 of 32 x 64; BM = 64: 2 x 2 of 32 x 64,
+// and a 64-wide remainder takes the 128-wide tile), so every SIMD gets an
+// equal share and a narrow tile takes a fraction of a whole one's time.
+// STR (GEMM1 only): some wave's columns cross from the primary path into the
+// residual one, so |g| is chosen per column block.  PART: the tile's rows run
+// past the last token and a 32-row block is empty; each wave then reads and
+// multiplies only its 32-row blocks that hold tokens.
 // Threads of a workgroup: 256-row tiles take eight waves (two per SIMD, one
 // workgroup per CU); 64- and 128-row tiles four waves of 64 x 64 and 128 x 64
 // (one per SIMD, three and two workgroups per CU).  Measured against eight
@@ -566,11 +568,16 @@ __device__ __forceinline__ void prefill_tile(const PreArgs& a, const PreItem& it
 // PART: a launch over the tiles of row stripes that run past the last token
 // (a separate launch, so the full tiles' kernel carries none of it).
 // The tile width (it.tn: 256, 128 or 64) picks the wave layout, uniformly
-// over the workgroup (64-row tiles take the 256-wide layout only).
+// over the workgroup (64-row tiles are 256 or 128 wide).
 template <int MODE, int BM, bool STR, bool PART>
 __device__ __forceinline__ void prefill_tile_any(const PreArgs& a, const PreItem& it) {
-  if constexpr (BM < kPreBM) {
-    prefill_tile<MODE, BM, 1, 4, 256, STR, PART>(a, it);
+  if constexpr (BM == 64) {
+    if (it.tn == 256) prefill_tile<MODE, 64, 1, 4, 256, STR, PART>(a, it);
+    else prefill_tile<MODE, 64, 2, 2, 128, STR, PART>(a, it);
+  } else if constexpr (BM == 128) {
+    if (it.tn == 256) prefill_tile<MODE, 128, 1, 4, 256, STR, PART>(a, it);
+    else if (it.tn == 128) prefill_tile<MODE, 128, 2, 2, 128, STR, PART>(a, it);
+    else prefill_tile<MODE, 128, 4, 1, 64, STR, PART>(a, it);
   } else {
     if (it.tn == 256) prefill_tile<MODE, BM, 2, 4, 256, STR, PART>(a, it);
     else if (it.tn == 128) prefill_tile<MODE, BM, 4, 2, 128, STR, PART>(a, it);
@@ -746,8 +753,8 @@ hipError_t prefill_prepare(PrefillPlan& P, const PrefillLayer* const* layers, in
     zoff += align256((size_t)T * L.Rp * 2);
     const int nt1 = (L.Rp + kPreBN - 1) / kPreBN, nt2 = (L.m + kPreBN - 1) / kPreBN;
     // work of one row stripe in whole-tile K blocks (a narrow tile counts its share)
-    // (64- and 128-row tiles always take the 256-wide layout)
-    auto width = [&](int N, int nt) { return bm < kPreBM ? kPreBN : tile_width(N, nt); };
+    // (64-row tiles are at least 128 wide)
+    auto width = [&](int N, int nt) { return bm == 64 ? std::max(tile_width(N, nt), 128) : tile_width(N, nt); };
     double w1 = 0, w2 = 0;
     for (int nt = 0; nt < nt1; ++nt) w1 += width(L.Rp, nt) / (double)kPreBN;
     for (int nt = 0; nt < nt2; ++nt) w2 += width(L.m, nt) / (double)kPreBN;
