@@ -187,8 +187,18 @@ typedef __attribute__((address_space(3))) void lds_void;
 // load into LDS as touching both memory and LDS and then waits for every
 // outstanding LDS read wherever it needs one, which exposes the latency of
 // the reads just issued for the next step.
+// The base address is taken from the first lane: every base here is the same
+// across the workgroup, but where the compiler cannot prove it, it keeps the
+// resource in vector registers and wraps each load in a loop over the distinct
+// values of the lanes (about a dozen instructions per load).
 __device__ inline __amdgpu_buffer_rsrc_t byte_rsrc(const void* base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
+  // (readfirstlane returns a signed int: each half goes back through uint32_t,
+  // or a low word with bit 31 set would fill the high word with ones)
+  const uint64_t v = reinterpret_cast<uint64_t>(base);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint64_t u = ((uint64_t)hi << 32) | lo;
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(u), 0, 0x7fffffff, 0x00020000);
 }
 
 // Waits until at most VM vector-memory operations of this wave are
@@ -250,7 +260,7 @@ __device__ __forceinline__ void prefill_tile(const PreArgs& a, const PreItem& it
   static_assert(MB >= 1 && kAI >= 1, "a wave owns whole 32-row blocks; every wave loads A rows");
   static_assert(kWaves == 8 || kWaves == 4, "eight waves (two per SIMD) or four (one per SIMD)");
   static_assert(TN / WN == 64, "a wave covers 64 columns (half a 128-column B tile)");
-  static_assert(NB == 2 || NB == 4, "a wave covers half or all of a 128-column B tile");
+  static_assert(NB == 2, "a wave covers two 32-column blocks (half a 128-column B tile)");
   static_assert(kWaves >= 3, "waves 0, 1, 2 carry the B words and |g|");
   static_assert(MODE == 1 || !STR, "only GEMM1 columns span paths");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -357,8 +367,13 @@ __device__ __forceinline__ void prefill_tile(const PreArgs& a, const PreItem& it
   bool bpath[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) bpath[b] = MODE == 1 && L.np > 1 && n0 + wcol + (STR ? 32 * b : 0) >= L.roff[1];
-  auto read_g = [&](int buf, int ks, bool path1) {
-    return *reinterpret_cast<const u32x4*>(lds + buf * kBuf + kBufA + kBufB + (path1 ? kPreBK * 2 : 0) + 16 * kg + 32 * ks);
+  // LDS offsets of the |g| runs of the paths of the wave's first (gofs) and
+  // last (gofs_x, STR only) column block, fixed for the tile: with the path
+  // chosen per read, the STR body read both runs at every K step and selected
+  const int gofs = kBufA + kBufB + __builtin_amdgcn_readfirstlane(bpath[0] ? kPreBK * 2 : 0) + 16 * kg;
+  const int gofs_x = kBufA + kBufB + __builtin_amdgcn_readfirstlane(bpath[NB - 1] ? kPreBK * 2 : 0) + 16 * kg;
+  auto read_g = [&](int buf, int ks, int ofs) {
+    return *reinterpret_cast<const u32x4*>(lds + buf * kBuf + ofs + 32 * ks);
   };
   uint32_t h0[NB], h1[NB];
   if (MODE == 2) {
@@ -372,14 +387,14 @@ __device__ __forceinline__ void prefill_tile(const PreArgs& a, const PreItem& it
     }
   }
   // B operands of one K step: sign bits d (one word per step), magnitudes
-  // gc (GEMM1, path of block 0) / gs (GEMM1, the other path; STR only) / the
-  // GEMM2 path of the step
+  // gc (GEMM1, path of block 0) / gs (GEMM1, path of the last block; STR
+  // only: a wave's 64 columns are two blocks) / the GEMM2 path of the step
   auto make_b = [&](uint32_t d, const u32x4& gc, const u32x4& gs, bool kp, u32x4* bf) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       u32x4 sc;
       if (MODE == 1) {
-        sc = (STR && bpath[b] != bpath[0]) ? gs : gc;
+        sc = (STR && b == NB - 1) ? gs : gc;
       } else {
         const uint32_t h = kp ? h1[b] : h0[b];
         sc = u32x4{h, h, h, h};
@@ -421,10 +436,10 @@ __device__ __forceinline__ void prefill_tile(const PreArgs& a, const PreItem& it
   read_a(0, 0, af[0]);
   u32x4 bw = read_b(0);
   {
-    const u32x4 g0 = MODE == 1 ? read_g(0, 0, bpath[0]) : u32x4{};
-    const u32x4 g1 = (MODE == 1 && STR) ? read_g(0, 0, !bpath[0]) : u32x4{};
-    if (MODE == 1) gq[1][0] = read_g(0, 1, bpath[0]);
-    if (MODE == 1 && STR) gq[1][1] = read_g(0, 1, !bpath[0]);
+    const u32x4 g0 = MODE == 1 ? read_g(0, 0, gofs) : u32x4{};
+    const u32x4 g1 = (MODE == 1 && STR) ? read_g(0, 0, gofs_x) : u32x4{};
+    if (MODE == 1) gq[1][0] = read_g(0, 1, gofs);
+    if (MODE == 1 && STR) gq[1][1] = read_g(0, 1, gofs_x);
     make_b(bw[0], g0, g1, kpath(0, 0), bf[0]);
   }
 
@@ -440,8 +455,8 @@ __device__ __forceinline__ void prefill_tile(const PreArgs& a, const PreItem& it
       read_a(rb, rks, af[(ks + 1) & 1]);
       const uint32_t dn = ks < 3 ? bw[ks + 1] : bwn[0];
       const u32x4 g0 = gq[(ks + 1) & 1][0], g1 = gq[(ks + 1) & 1][1];
-      if (MODE == 1) gq[ks & 1][0] = read_g(gb, gks, bpath[0]);
-      if (MODE == 1 && STR) gq[ks & 1][1] = read_g(gb, gks, !bpath[0]);
+      if (MODE == 1) gq[ks & 1][0] = read_g(gb, gks, gofs);
+      if (MODE == 1 && STR) gq[ks & 1][1] = read_g(gb, gks, gofs_x);
       // the LDS reads of step ks + 1 go out before this step's MFMAs (the
       // scheduler would otherwise sink them next to their use and expose
       // their latency at every step)
@@ -529,10 +544,14 @@ __device__ __forceinline__ void prefill_tile(const PreArgs& a, const PreItem& it
           const int slot = ((col - n0) >> 2) ^ (rt & 15);
           *reinterpret_cast<u32x2*>(lds + rt * (kPreBN * 2) + slot * 8) = u32x2{w0, w1};
         } else if (row < T) {
-          const uint32_t w[2] = {w0, w1};
+          if ((ldc & 3) == 0 && col + 3 < N) {
+            *reinterpret_cast<LB_GLOBAL u32x2*>(cp + col) = u32x2{w0, w1};   // 8-byte aligned run
+          } else {
+            const uint32_t w[2] = {w0, w1};
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (col + i < N) cp[col + i] = (uint16_t)(w[i >> 1] >> (16 * (i & 1)));
+            for (int i = 0; i < 4; ++i)
+              if (col + i < N) cp[col + i] = (uint16_t)(w[i >> 1] >> (16 * (i & 1)));
+          }
         }
       }
     }

@@ -80,40 +80,63 @@ def test_full_size_layers_sampled(name, T, regime, layers):
             f"E_max/rms {st['emax_rel_rms']:.2e}")
 
 
-def test_full_70b_stack_decode_as_benchmarked():
-    """The whole Llama-2-70B-shaped stack (80 layers, 560 linears) at batch 1,
-    run exactly as the benchmark times it: one stack, bound to its buffers,
-    three direct launches per step (so the work items are those of the
-    timed configuration, not of a smaller stack).  Sampled output channels of
-    three layers' linears are checked against the oracle."""
+@pytest.fixture(scope="module")
+def stack70():
+    """The whole Llama-2-70B-shaped stack (80 layers, 560 linears), built once
+    for the tests that run it as the benchmark does; the parameters of three
+    layers are kept for the oracle."""
     wl = synth.WORKLOADS["llama2-70b-0.1bpw"]
-    T = 1
     rk = [ranks(wl, s) for s in wl.mats]
-    lins, xs, ys, keep = [], [], [], {}
-    check_layers = (0, 40, 79)
+    lins, keep = [], {}
     for l in range(wl.layers):
         for j, s in enumerate(wl.mats):
             p = synth.layer_tensors(wl.wid, l, j, s.m, s.n, rk[j])
-            x = synth.layer_activations(wl, l, j, s.n, T, io="bf16")
             lins.append(lb.Linear.from_numpy(s.m, s.n, p))
-            xs.append(x_tensor(x))
-            ys.append(torch.empty((T, s.m), dtype=torch.bfloat16, device="cuda"))
-            if l in check_layers:
-                keep[len(lins) - 1] = (l, s, p, x)
+            if l in (0, 40, 79):
+                keep[len(lins) - 1] = (l, j, s, p)
     log(f"70B stack: {len(lins)} linears")
     S = lb.Stack(lins)
-    step = S.bind(xs, ys, regime=lb.REGIME_DECODE, use_graph=False)
+    yield wl, lins, S, keep
+    S.close()
+
+
+def run_stack70(stack70, T, regime, seed):
+    wl, lins, S, keep = stack70
+    xs, ys = [], []
+    for i, lin in enumerate(lins):
+        l, j = divmod(i, len(wl.mats))
+        xs.append(x_tensor(synth.layer_activations(wl, l, j, lin.d_in, T, io="bf16")))
+        ys.append(torch.empty((T, lin.d_out), dtype=torch.bfloat16, device="cuda"))
+    step = S.bind(xs, ys, regime=regime, use_graph=False)
     for _ in range(3):
         step.forward()
     torch.cuda.synchronize()
-    rng = np.random.default_rng(5601)
-    for i, (l, s, p, x) in keep.items():
+    rng = np.random.default_rng(seed)
+    for i, (l, j, s, p) in keep.items():
+        x = synth.layer_activations(wl, l, j, s.n, T, io="bf16")
         rows = np.sort(rng.choice(s.m, size=min(SAMPLE_ROWS, s.m), replace=False))
         ref = oracle.forward_rows(x_f64(x), p, s.m, s.n, rows)
-        st = assert_bf16_close(to_f64(ys[i])[:, rows], ref, f"70B stack layer {l} {s.name}")
+        st = assert_bf16_close(to_f64(ys[i])[:, rows], ref, f"70B stack T={T} layer {l} {s.name}")
         log(f"  layer {l} {s.name:5s}: E_rms {st['erms']:.2e} E_max/rms {st['emax_rel_rms']:.2e}")
     del step
-    S.close()
+
+
+def test_full_70b_stack_decode_as_benchmarked(stack70):
+    """The whole Llama-2-70B-shaped stack at batch 1, run exactly as the
+    benchmark times it: one stack, bound to its buffers, three direct launches
+    per step (so the work items are those of the timed configuration, not of a
+    smaller stack).  Sampled output channels of three layers' linears are
+    checked against the oracle."""
+    run_stack70(stack70, 1, lb.REGIME_DECODE, 5601)
+
+
+def test_full_70b_stack_t64_auto_as_benchmarked(stack70):
+    """The whole stack at 64 tokens in the regime AUTO picks for it, as the
+    benchmark's token sweep runs it (the work items and tile order are those
+    of the timed 560-linear launch, not of one layer).  Sampled output
+    channels of three layers' linears against the oracle."""
+    log(f"70B stack T=64: AUTO picks {lb.auto_regime(stack70[1], 64)}")
+    run_stack70(stack70, 64, lb.REGIME_AUTO, 6401)
 
 
 def test_full_70b_layer_t64_auto_all_rows():
