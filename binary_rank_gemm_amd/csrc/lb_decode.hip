@@ -119,10 +119,21 @@ __device__ inline float wave_sum(float v) {
 // memory fence here would also wait for the prefetched global loads).
 __device__ inline void wave_lds_fence() { __asm__ volatile("" ::: "memory"); }
 
-// fp4 B operand from one packed word (bit layout of fp4_bit_of_elem).
-__device__ inline v8i expand_signs(uint32_t w) {
+// 1.0 in every fp4 nibble, held in a register (made once per stream):
+// three-operand instructions take no literal here, so with the constant as
+// an immediate the sign class of expand_signs costs an and plus an or, with
+// it in a register one v_and_or.
+__device__ inline uint32_t fp4_ones() {
+  uint32_t one = 0x22222222u;
+  __asm__("" : "+v"(one));
+  return one;
+}
+
+// fp4 B operand from one packed word (bit layout of fp4_bit_of_elem); one =
+// fp4_ones().
+__device__ inline v8i expand_signs(uint32_t w, uint32_t one) {
   v8i b;
-  b[0] = (int)((w & 0x88888888u) | 0x22222222u);  // +-1
+  b[0] = (int)((w & 0x88888888u) | one);           // +-1
   b[1] = (int)(w & 0x44444444u);                  // {0, 2}
   b[2] = (int)(w & 0x22222222u);                  // {0, 1}
   b[3] = (int)(w & 0x11111111u);                  // {0, 0.5}
@@ -354,6 +365,7 @@ __device__ __attribute__((always_inline)) inline void v_stream(const DecArgs& a,
     return slot;
   };
   const ConvLane L(lane);
+  const uint32_t one = fp4_ones();
   for (int c0 = ca; c0 < cb; c0 += G) {
     const int ngc = min(G, cb - c0);
     // this lane's elements kloc, kloc + 1 (= 2 lane, 2 lane + 1) of g and of each token row, per chunk
@@ -414,7 +426,7 @@ __device__ __attribute__((always_inline)) inline void v_stream(const DecArgs& a,
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               if (4 * j + i < S::CT && 4 * j + i < ntl) {
-                const v8i B = expand_signs(w[i]);
+                const v8i B = expand_signs(w[i], one);
 #pragma unroll
                 for (int tb = 0; tb < TB; ++tb) acc[4 * j + i][tb] = mfma(A[tb], B, acc[4 * j + i][tb], sc[tb]);
               }
@@ -442,6 +454,7 @@ __device__ __attribute__((always_inline)) inline void v_plain(const DecArgs& a, 
   const ConvLane L(lane);
   const LB_GLOBAL uint16_t* x = reinterpret_cast<const LB_GLOBAL uint16_t*>(xb);
   const LB_GLOBAL uint16_t* g = reinterpret_cast<const LB_GLOBAL uint16_t*>(gdec);
+  const uint32_t one = fp4_ones();
   for (int c = ca; c < cb; ++c) {
     const int k0 = c * kChunk + L.kloc;
     const bool v0 = k0 < n, v1 = k0 + 1 < n;
@@ -469,7 +482,7 @@ __device__ __attribute__((always_inline)) inline void v_plain(const DecArgs& a, 
       if (i < ntl) {
         const uint32_t w = *reinterpret_cast<const LB_GLOBAL uint32_t*>(vdec + ((int64_t)c * nct + it.tile0 + i) * 256 +
                                                                        lane * 4);
-        const v8i B = expand_signs(w);
+        const v8i B = expand_signs(w, one);
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) acc[i][tb] = mfma(A[tb], B, acc[i][tb], sc[tb]);
       }
@@ -818,6 +831,7 @@ __device__ __attribute__((always_inline)) inline void u_stream(const DecArgs& a,
   // quads whose 64 rows are whole (and 16-byte aligned in y) are staged
   // (as many as the staging area holds: half as many when y is fp32)
   const int nst = (C.m & 7) == 0 ? min(max(0, min(qb, C.m / 64) - qa), C.yf32 ? S::QW / 2 : S::QW) : 0;
+  const uint32_t one = fp4_ones();
   int s = 0;
   for (int q = qa; q < qb; ++q) {
     v4f acc[4][TB];
@@ -846,7 +860,7 @@ __device__ __attribute__((always_inline)) inline void u_stream(const DecArgs& a,
         const u32x4 w = *reinterpret_cast<const u32x4*>(slot + lane * 16);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-          const v8i B = expand_signs(w[rt]);
+          const v8i B = expand_signs(w[rt], one);
 #pragma unroll
           for (int tb = 0; tb < TB; ++tb) acc[rt][tb] = mfma(A[u][tb], B, acc[rt][tb], sc[u][tb]);
         }
@@ -894,13 +908,14 @@ __device__ __attribute__((always_inline)) inline void u_plain(const DecArgs& a, 
       const bool half = (u == g.nu0 - 1 && g.half0) || (u == g.nu - 1 && g.half1);
       const int off = (u < g.nu0 ? 1024 * u : g.uoff1 + 1024 * (u - g.nu0)) + (half ? (lane & 31) : lane) * 16;
       const u32x4 w = *reinterpret_cast<const LB_GLOBAL u32x4*>(udec + (int64_t)q * g.qbytes + off);
+      const uint32_t one = fp4_ones();
       v8i A[TB];
       int sc[TB];
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) load_a(aimg + (int64_t)(u * TB + tb) * kABytes, mr, gr, A[tb], sc[tb]);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
-        const v8i B = expand_signs(w[rt]);
+        const v8i B = expand_signs(w[rt], one);
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) acc[rt][tb] = mfma(A[tb], B, acc[rt][tb], sc[tb]);
       }
