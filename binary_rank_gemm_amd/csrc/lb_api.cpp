@@ -533,17 +533,22 @@ double decode_cost_us(const lb_linear* L, int count, int64_t T) {
 // K-block term; a 128-row stripe 1.36 + 0.125 whole 64-row stripes per 32-row
 // block it computes, a 256-row stripe 1.6 + 0.3 per block.
 double prefill_cost_us(const lb_linear* L, int count, int64_t T) {
-  double tk = 0, tn = 0, longest = 0;
+  double tk = 0, tn = 0, longest = 0, blocks1 = 0;
+  const int bm = prefill_rows_per_tile((int)T), mts = (int)((T + bm - 1) / bm);
+  for (int e = 0; e < count; ++e)
+    blocks1 += (double)mts * ((L[e]->pre.Rp + kPreBN - 1) / kPreBN) * L[e]->pre.kb1;
+  bool cut = false;
   for (int e = 0; e < count; ++e) {
     const PrefillLayer& P = L[e]->pre;
     const double t1 = (P.Rp + kPreBN - 1) / kPreBN, t2 = (P.m + kPreBN - 1) / kPreBN;
     tk += t1 * P.kb1 + t2 * P.kb2;
     tn += t1 + t2;
-    longest = std::max(longest, 0.5 * (P.kb1 + P.kb2));
+    const int nks = prefill_k_parts(P.kb1, (int)T, blocks1);   // GEMM1 K parts (the longest tile's blocks)
+    cut = cut || nks > 1;
+    longest = std::max(longest, 0.5 * ((P.kb1 + nks - 1) / nks + P.kb2));
   }
   const double whole = tk * 1.54e-3 + tn * 7.4e-3 + 57.0, small = tk * 1.54e-3 * 0.72 + tn * 7.4e-3 + 57.0;
-  const int bm = prefill_rows_per_tile((int)T);
-  double us = 0;
+  double us = cut ? 6.0 : 0.0;                         // the launch adding the K parts
   for (int64_t m0 = 0; m0 < T; m0 += bm) {
     const int live = (int)std::min<int64_t>(bm, T - m0);
     // blocks computed: all of the tile unless the stripe skips empty ones

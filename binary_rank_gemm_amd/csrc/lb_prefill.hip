@@ -297,6 +297,14 @@ __device__ __forceinline__ void prefill_tile(const PreArgs& a, const PreItem& it
   const int bb0 = (wcol & (kPreWN - 1)) / 32;            // first 32-column block inside its B tile
   const bool vec_ok = (lda & 7) == 0;
   const int nkb = (K + kPreBK - 1) / kPreBK;
+  // K blocks [kb_lo, kb_hi) of this item: all of K, or GEMM1 part it.ks of Eg.nks
+  int kb_lo = 0, kb_hi = nkb;
+  if (MODE == 1 && Eg.nks > 1) {
+    const int kbs = (nkb + Eg.nks - 1) / Eg.nks;
+    kb_lo = min(nkb, it.ks * kbs);
+    kb_hi = min(nkb, kb_lo + kbs);
+  }
+  const int nloc = kb_hi - kb_lo;
 
   // LDS, kPreBufs buffers of: A [BM x 64] bf16 (swizzled) | B words [2 tiles][64 lanes] u32x4 | |g| [2][64] bf16
   constexpr int kBufA = BM * kPreBK * 2, kBufB = 2 * 64 * 16, kBufG = 2 * kPreBK * 2;
@@ -420,10 +428,10 @@ __device__ __forceinline__ void prefill_tile(const PreArgs& a, const PreItem& it
   // ks + 1 are read and expanded (for ks = 3: step 0 of the next block, whose
   // buffer is complete since the previous barrier; past the last block the
   // buffer is stale and the result unused).
-  issue(0, 0);
-  if (nkb > 1) issue(1, 1);
-  if (nkb > 2) {
-    issue(2, 2);
+  issue(kb_lo, 0);
+  if (nloc > 1) issue(kb_lo + 1, 1);
+  if (nloc > 2) {
+    issue(kb_lo + 2, 2);
     vm_wait_barrier<kAI>();
   } else {
     vm_wait_barrier<0>();
@@ -443,10 +451,10 @@ __device__ __forceinline__ void prefill_tile(const PreArgs& a, const PreItem& it
     make_b(bw[0], g0, g1, kpath(0, 0), bf[0]);
   }
 
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int cur = kb & 3, nxt = (kb + 1) & 3;
-    const bool more = kb + 3 < nkb;
-    if (more) issue(kb + 3, (kb + 3) & 3);
+  for (int kb = kb_lo; kb < kb_hi; ++kb) {
+    const int cur = (kb - kb_lo) & 3, nxt = (kb - kb_lo + 1) & 3;
+    const bool more = kb + 3 < kb_hi;
+    if (more) issue(kb + 3, (kb - kb_lo + 3) & 3);
     const u32x4 bwn = read_b(nxt);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -481,6 +489,28 @@ __device__ __forceinline__ void prefill_tile(const PreArgs& a, const PreItem& it
   // every wave is past the loop's last barrier, which waited for all LDS
   // reads) and writes whole 512-byte row segments; otherwise each run goes
   // straight out.
+  if (MODE == 1 && Eg.nks > 1) {
+    // one K part of a cut GEMM1: fp32 partial sums (l is applied where the
+    // parts are added); N = Rp is a multiple of 64, so a run is wholly in or out
+    LB_GLOBAL float* Cp = gp(Eg.zpart) + (int64_t)it.ks * T * ldc;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int cb = n0 + wcol + 32 * b + 4 * kg;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int row = m0 + wm * MB * 32 + mb * 32 + l32;
+        if (row >= T) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int col = cb + 8 * j;
+          if (col < N)
+            *reinterpret_cast<LB_GLOBAL f4*>(Cp + (int64_t)row * ldc + col) =
+                f4{acc[mb][b][4 * j], acc[mb][b][4 * j + 1], acc[mb][b][4 * j + 2], acc[mb][b][4 * j + 3]};
+        }
+      }
+    }
+    return;
+  }
   if (MODE == 2 && a.yf32) {
     // fp32 y: each run of four adjacent columns is one 16-byte store
     float* Cf = reinterpret_cast<float*>(first ? a.y0 : Eg.y);
@@ -580,6 +610,27 @@ __device__ __forceinline__ void prefill_tile(const PreArgs& a, const PreItem& it
       }
     }
   }
+}
+
+// Adds the K parts of cut GEMM1s in part order and applies l:
+// Z' = bf16((P_0 + P_1 + ...) l), four adjacent outputs per thread.
+__global__ void __launch_bounds__(256) k_prefill_combine(const PreEntry* entries, const PreComb* items, int T) {
+  const PreComb c = items[blockIdx.x];
+  const PreEntry& E = entries[c.entry];
+  const int Rp = E.L.Rp;
+  const int64_t plane = (int64_t)T * Rp, e = (int64_t)c.e0 + threadIdx.x * 4;
+  if (e >= plane) return;
+  const LB_GLOBAL float* P = gp(E.zpart);
+  f4 s = *reinterpret_cast<const LB_GLOBAL f4*>(P + e);
+  for (int k = 1; k < E.nks; ++k) {
+    const f4 v = *reinterpret_cast<const LB_GLOBAL f4*>(P + k * plane + e);
+    s = f4{s[0] + v[0], s[1] + v[1], s[2] + v[2], s[3] + v[3]};
+  }
+  const f4 l = *reinterpret_cast<const LB_GLOBAL f4*>(gp(E.L.lpad) + (int)(e % Rp));
+  const f2 lo = {s[0] * l[0], s[1] * l[1]}, hi = {s[2] * l[2], s[3] * l[3]};
+  *reinterpret_cast<LB_GLOBAL u32x2*>(gp(E.z) + e) =
+      u32x2{__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf2)),
+            __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf2))};
 }
 
 // One workgroup per tile; GEMM1 tiles where a wave's columns reach into both
@@ -744,13 +795,21 @@ std::vector<PreItem> xcd_order(const std::vector<std::vector<PreItem>>& stripes,
   }
   size_t len = 0;
   for (auto& v : per) len = std::max(len, v.size());
-  std::vector<PreItem> out(len * kXcd, PreItem{-1, 0, 0, 0, 0});
+  std::vector<PreItem> out(len * kXcd, PreItem{-1, 0, 0, 0, 0, 0});
   for (int x = 0; x < kXcd; ++x)
     for (size_t i = 0; i < per[x].size(); ++i) out[i * kXcd + x] = per[x][i];
   return out;
 }
 
 }  // namespace
+
+double prefill_gemm1_blocks(const PrefillLayer* const* layers, int count, int T) {
+  const int bm = prefill_rows_per_tile(T), mts = (T + bm - 1) / bm;
+  double blocks = 0;
+  for (int e = 0; e < count; ++e)
+    blocks += (double)mts * ((layers[e]->Rp + kPreBN - 1) / kPreBN) * layers[e]->kb1;
+  return blocks;
+}
 
 hipError_t prefill_prepare(PrefillPlan& P, const PrefillLayer* const* layers, int count, int T,
                            const void* const* xs, void* const* ys) {
@@ -762,14 +821,23 @@ hipError_t prefill_prepare(PrefillPlan& P, const PrefillLayer* const* layers, in
   const int mts = (T + bm - 1) / bm;
   std::vector<std::vector<PreItem>> s1, s2, s1p, s2p;   // full row stripes, stripes past the last token
   std::vector<double> k1, k2, k1p, k2p;                  // K blocks per tile of each stripe
-  size_t zoff = 0;
-  std::vector<size_t> zoffs(count);
+  size_t zoff = 0, poff = 0;
+  std::vector<size_t> zoffs(count), poffs(count);
+  std::vector<PreComb> comb;
   P.entries_h.assign(count, PreEntry{});
+  const double blocks1 = prefill_gemm1_blocks(layers, count, T);
   for (int e = 0; e < count; ++e) {
     const PrefillLayer& L = *layers[e];
     P.entries_h[e].L = L;
     zoffs[e] = zoff;
     zoff += align256((size_t)T * L.Rp * 2);
+    const int nks = prefill_k_parts(L.kb1, T, blocks1);
+    P.entries_h[e].nks = nks;
+    poffs[e] = poff;
+    if (nks > 1) {
+      poff += align256((size_t)nks * T * L.Rp * 4);
+      for (int64_t e0 = 0; e0 < (int64_t)T * L.Rp; e0 += 1024) comb.push_back(PreComb{e, (int)e0});
+    }
     const int nt1 = (L.Rp + kPreBN - 1) / kPreBN, nt2 = (L.m + kPreBN - 1) / kPreBN;
     // work of one row stripe in whole-tile K blocks (a narrow tile counts its share)
     // (64-row tiles are at least 128 wide)
@@ -779,18 +847,19 @@ hipError_t prefill_prepare(PrefillPlan& P, const PrefillLayer* const* layers, in
     for (int nt = 0; nt < nt2; ++nt) w2 += width(L.m, nt) / (double)kPreBN;
     for (int mt = 0; mt < mts; ++mt) {
       std::vector<PreItem> a, b;
-      for (int nt = 0; nt < nt1; ++nt) {
-        const int tn = width(L.Rp, nt);
-        a.push_back(PreItem{e, mt, nt, tile_straddles(L, nt, tn) ? 1 : 0, tn});
-      }
-      for (int nt = 0; nt < nt2; ++nt) b.push_back(PreItem{e, mt, nt, 0, width(L.m, nt)});
+      for (int ks = 0; ks < nks; ++ks)
+        for (int nt = 0; nt < nt1; ++nt) {
+          const int tn = width(L.Rp, nt);
+          a.push_back(PreItem{e, mt, nt, tile_straddles(L, nt, tn) ? 1 : 0, tn, ks});
+        }
+      for (int nt = 0; nt < nt2; ++nt) b.push_back(PreItem{e, mt, nt, 0, width(L.m, nt), 0});
       // a stripe past the last token runs the kernel that skips empty 32-row
       // blocks, when it has one (with none the skipping costs more than it
       // saves: 112 tokens in one 128-row stripe, 9 % slower)
       const bool part = (mt + 1) * bm > T && T - mt * bm <= bm - 32;
       (part ? s1p : s1).push_back(a);
       (part ? s2p : s2).push_back(b);
-      (part ? k1p : k1).push_back(L.kb1 * w1 / nt1);
+      (part ? k1p : k1).push_back(L.kb1 * w1 / nt1 / nks);
       (part ? k2p : k2).push_back(L.kb2 * w2 / nt2);
     }
   }
@@ -807,16 +876,34 @@ hipError_t prefill_prepare(PrefillPlan& P, const PrefillLayer* const* layers, in
     if (e != hipSuccess) return e;
     P.zbytes = zoff;
   }
+  if (poff > P.pbytes) {
+    if (P.pbuf) {
+      hipError_t e = hipFree(P.pbuf);
+      if (e != hipSuccess) return e;
+      P.pbuf = nullptr;
+      P.pbytes = 0;
+    }
+    hipError_t e = hipMalloc(&P.pbuf, poff);
+    if (e != hipSuccess) return e;
+    P.pbytes = poff;
+  }
   for (int e = 0; e < count; ++e) {
     P.entries_h[e].z = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(P.zbuf) + zoffs[e]);
+    P.entries_h[e].zpart = P.entries_h[e].nks > 1 ? reinterpret_cast<float*>(reinterpret_cast<char*>(P.pbuf) + poffs[e])
+                                                  : nullptr;
     P.entries_h[e].x = xs ? xs[e] : nullptr;
     P.entries_h[e].y = ys ? ys[e] : nullptr;
   }
   if (P.entries_d) (void)hipFree(P.entries_d);
   if (P.items_d) (void)hipFree(P.items_d);
+  if (P.comb_d) (void)hipFree(P.comb_d);
   P.entries_d = nullptr;
   P.items_d = nullptr;
+  P.comb_d = nullptr;
   hipError_t e = hipMalloc(&P.entries_d, count * sizeof(PreEntry));
+  if (e == hipSuccess && !comb.empty()) e = hipMalloc(&P.comb_d, comb.size() * sizeof(PreComb));
+  if (e == hipSuccess && !comb.empty())
+    e = hipMemcpy(P.comb_d, comb.data(), comb.size() * sizeof(PreComb), hipMemcpyHostToDevice);
   if (e == hipSuccess)
     e = hipMalloc(&P.items_d, std::max<size_t>(1, i1.size() + i1p.size() + i2.size() + i2p.size()) * sizeof(PreItem));
   if (e == hipSuccess) e = hipMemcpy(P.entries_d, P.entries_h.data(), count * sizeof(PreEntry), hipMemcpyHostToDevice);
@@ -832,6 +919,7 @@ hipError_t prefill_prepare(PrefillPlan& P, const PrefillLayer* const* layers, in
   P.n1p = (int)i1p.size();
   P.n2 = (int)i2.size();
   P.n2p = (int)i2p.size();
+  P.ncomb = (int)comb.size();
   P.bm = bm;
   P.T = T;
   P.count = count;
@@ -847,6 +935,7 @@ hipError_t launch_gemms(const PrefillPlan& P, PreArgs a, hipStream_t st) {
   if (P.n1 > 0) hipLaunchKernelGGL((k_prefill<1, BM, false>), dim3(P.n1), dim3(pre_threads(BM)), lds, st, a);
   a.items = P.items_d + P.n1;
   if (P.n1p > 0) hipLaunchKernelGGL((k_prefill<1, BM, true>), dim3(P.n1p), dim3(pre_threads(BM)), lds, st, a);
+  if (P.ncomb > 0) hipLaunchKernelGGL(k_prefill_combine, dim3(P.ncomb), dim3(256), 0, st, a.entries, P.comb_d, a.T);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   a.items = P.items_d + P.n1 + P.n1p;
@@ -890,10 +979,16 @@ void prefill_plan_release(PrefillPlan& P) {
   if (P.entries_d) (void)hipFree(P.entries_d);
   if (P.items_d) (void)hipFree(P.items_d);
   if (P.zbuf) (void)hipFree(P.zbuf);
+  if (P.comb_d) (void)hipFree(P.comb_d);
+  if (P.pbuf) (void)hipFree(P.pbuf);
   P.entries_d = nullptr;
   P.items_d = nullptr;
   P.zbuf = nullptr;
   P.zbytes = 0;
+  P.comb_d = nullptr;
+  P.ncomb = 0;
+  P.pbuf = nullptr;
+  P.pbytes = 0;
   P.T = -1;
   P.count = 0;
   P.entries_h.clear();

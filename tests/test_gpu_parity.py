@@ -205,6 +205,25 @@ def test_prefill_identity_probe_many_tokens_bit_exact():
     assert np.array_equal(to_f64(y), oracle.forward(x_f64(x), paths, m, n))
 
 
+def test_prefill_k_parts_probe_bit_exact():
+    """48 tokens, K = 9000 (141 K blocks: GEMM1 in two K parts).  Each token
+    row holds two ones, one in each part's K range; with unit scales every sum
+    is a small integer, so the parts' fp32 sums and the bf16 results are exact."""
+    m, n, ranks, T = 300, 9000, [40, 30], 48
+    ones = lambda k: f16bits(np.ones(k))
+    paths = [dict(rank=r, u_words=synth.sign_words((35, p, 0), m, r), v_words=synth.sign_words((35, p, 1), n, r),
+                  h=ones(m), g=ones(n), l=ones(r)) for p, r in enumerate(ranks)]
+    xf = np.zeros((T, n), np.float32)
+    split = 71 * 64                                   # first K element of the second part
+    for t in range(T):
+        xf[t, (t * 97) % split] = 1.0
+        xf[t, split + (t * 131) % (n - split)] = 1.0
+    x = synth.bf16_bits_from_f32(xf)
+    y = build(m, n, paths).forward(x_tensor(x), regime=lb.REGIME_PREFILL)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_f64(y), oracle.forward(x_f64(x), paths, m, n))
+
+
 @pytest.mark.parametrize("m,n,ranks", [(300, 320, [20, 40]), (640, 384, [270, 20]), (1000, 320, [149, 102]),
                                        (300, 100, [20, 40]), (640, 128, [149, 102])])
 def test_prefill_identity_probe_narrow_tiles_bit_exact(m, n, ranks):
@@ -588,6 +607,12 @@ PREFILL_SHAPES = [
     (4096, 1024, [46, 46], 128),         # one full 128-row stripe
     (300, 700, [37, 45], 65),            # one 128-row stripe with a single live row
     (513, 257, [33, 31], 128),           # a full stripe, element-wise A loads (n % 8 != 0)
+    # one row stripe and more than 128 K blocks: GEMM1 runs in K parts, added by a second launch
+    (300, 9000, [37, 45], 40),           # 141 blocks: 2 parts, ragged last block
+    (256, 20000, [20, 20], 64),          # 313 blocks: 3 parts, full 64-row stripe
+    (513, 8300, [33, 31], 16),           # 2 parts, partial-stripe kernel, element-wise A loads
+    (700, 17000, [20, 40], 100),         # 128-row tiles, 3 parts, a wave's columns in both paths
+    (300, 16500, [37, 45], 200),         # 256-row tiles, 3 parts
 ]
 
 
@@ -621,6 +646,26 @@ def test_prefill_token_count_changes():
         y = lin.forward(x_tensor(x), regime=lb.REGIME_PREFILL)
         torch.cuda.synchronize()
         assert_bf16_close(to_f64(y), oracle.forward(x_f64(x), paths, m, n), f"prefill T={T}")
+
+
+@pytest.mark.parametrize("T", [40, 7])
+def test_stack_prefill_k_parts(T):
+    """A stack whose long-K entries (141 and 313 K blocks) have their GEMM1 cut
+    into K parts, beside whole ones: every entry against the oracle, and
+    against the same linear run alone (cut the same way), bit for bit."""
+    shapes = [(300, 9000, [37, 45]), (256, 512, [16, 16]), (256, 20000, [20, 20]), (200, 2000, [102, 90])]
+    lins, paths, xs = make_stack(36, shapes, T)
+    S = lb.Stack(lins)
+    xd = [x_tensor(x) for x in xs]
+    ys = [torch.empty((T, m), dtype=torch.bfloat16, device="cuda") for m, _, _ in shapes]
+    S.forward(xd, ys, regime=lb.REGIME_PREFILL, use_graph=False)
+    torch.cuda.synchronize()
+    for i, (m, n, _) in enumerate(shapes):
+        single = lins[i].forward(xd[i], regime=lb.REGIME_PREFILL)
+        torch.cuda.synchronize()
+        assert torch.equal(ys[i].view(torch.int16), single.view(torch.int16)), f"stack != single, entry {i}"
+        assert_bf16_close(to_f64(ys[i]), oracle.forward(x_f64(xs[i]), paths[i], m, n), f"K-part stack {i}")
+    S.close()
 
 
 @pytest.mark.parametrize("T", [300, 90])
