@@ -505,7 +505,7 @@ inline int y_is_fp32(lb_dtype io) { return io == LB_BF16 ? 0 : 1; }
 // Per launch sequence of up to 16 tokens: the V stage's and the U stage's
 // sign bytes at rates measured on whole Llama-shaped stacks at 16 tokens on
 // MI355X (V 0.72 µs/MB; U 0.34 µs/MB where a quad's 128-latent units fit the
-// U kernel's registers, 0.95 µs/MB where they do not; sequences of 8 tokens
+// U kernel's registers, 0.62 µs/MB where they do not; sequences of 8 tokens
 // or fewer 0.6 of that), at least 6 µs (one work item's latency), plus 12 µs
 // for the three launches.
 double decode_cost_us(const lb_linear* L, int count, int64_t T) {
@@ -518,7 +518,7 @@ double decode_cost_us(const lb_linear* L, int count, int64_t T) {
       vb += (double)L[e]->n * L[e]->r[p] / 8;
       ub += (double)L[e]->m * L[e]->r[p] / 8;
     }
-    us += vb * 0.72e-6 + ub * (L[e]->ug.nu <= nmax ? 0.34e-6 : 0.95e-6);
+    us += vb * 0.72e-6 + ub * (L[e]->ug.nu <= nmax ? 0.34e-6 : 0.62e-6);
   }
   const int64_t launches = (T + kDecodeMaxTokens - 1) / kDecodeMaxTokens;
   return (double)launches * (std::max(us * (bucket <= 8 ? 0.6 : 1.0), 6.0) + 12.0);

@@ -228,6 +228,11 @@ __device__ inline void vm_wait_barrier() {
 __device__ inline int a_row_xor(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 __device__ inline int a_slot_row(int s) { return s >> 3; }
 __device__ inline int a_slot_chunk(int s) { return (s & 7) ^ a_row_xor(s >> 3); }
+// C staging: the 8-byte slots of tile row rt are XOR-ed with c_slot_xor(rt),
+// so that the 16 rows a write phase covers hit distinct banks, while the two
+// slots of each 16-byte chunk stay adjacent and in order (chunk ch of row rt
+// sits at chunk ch ^ c_slot_xor(rt) / 2)
+__device__ inline int c_slot_xor(int rt) { return (rt & 14) | ((rt & 1) << 4); }
 
 // Wave layout of a BM x TN workgroup tile: WM x WN waves, each owning
 // (BM / WM) x (TN / WN) outputs as MB x NB blocks of 32 x 32, every wave 64
@@ -412,13 +417,17 @@ __device__ __forceinline__ void prefill_tile(const PreArgs& a, const PreItem& it
   };
   auto kpath = [&](int kb, int ks) { return MODE == 2 && L.np > 1 && kb * kPreBK + ks * 16 >= L.roff[1]; };
 
+  // the first K step's MFMAs start from zero (see kblock); blocks a PART
+  // wave skips keep these zeros
   v16f acc[MB][NB];
+  if constexpr (PART) {
 #pragma unroll
-  for (int i = 0; i < MB; ++i)
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
+      for (int j = 0; j < NB; ++j)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+  }
 
   // Pipeline over four LDS buffers: block kb + 3 is issued at the start of
   // block kb (into the buffer block kb - 1 used), and the barrier that ends
@@ -451,7 +460,9 @@ __device__ __forceinline__ void prefill_tile(const PreArgs& a, const PreItem& it
     make_b(bw[0], g0, g1, kpath(0, 0), bf[0]);
   }
 
-  for (int kb = kb_lo; kb < kb_hi; ++kb) {
+  // one K block; FIRST (the item's first block) starts the sums from zero
+  auto kblock = [&](int kb, auto first) __attribute__((always_inline)) {
+    constexpr bool FIRST = decltype(first)::value;
     const int cur = (kb - kb_lo) & 3, nxt = (kb - kb_lo + 1) & 3;
     const bool more = kb + 3 < kb_hi;
     if (more) issue(kb + 3, (kb - kb_lo + 3) & 3);
@@ -474,12 +485,15 @@ __device__ __forceinline__ void prefill_tile(const PreArgs& a, const PreItem& it
       for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
-          if (!PART || mb < mba) acc[mb][b] = mfma32(bf[ks & 1][b], af[ks & 1][mb], acc[mb][b]);
+          if (!PART || mb < mba)
+            acc[mb][b] = mfma32(bf[ks & 1][b], af[ks & 1][mb], (FIRST && ks == 0) ? v16f{} : acc[mb][b]);
     }
     bw = bwn;
     if (more) vm_wait_barrier<kAI>();
     else vm_wait_barrier<0>();
-  }
+  };
+  kblock(kb_lo, std::true_type{});
+  for (int kb = kb_lo + 1; kb < kb_hi; ++kb) kblock(kb, std::false_type{});
 
   // ---- epilogue.  The MFMAs take the B operand as their first factor, so
   // block (mb, b) holds the transposed product: lane (l32, kg) has output row
@@ -569,9 +583,8 @@ __device__ __forceinline__ void prefill_tile(const PreArgs& a, const PreItem& it
         const uint32_t w0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf2));
         const uint32_t w1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf2));
         if (c_stage) {
-          // 8-byte slot (col - n0) / 4 of tile row rt, XOR-swizzled by rt % 16
-          // so that the 16 rows a write phase covers hit distinct banks
-          const int slot = ((col - n0) >> 2) ^ (rt & 15);
+          // 8-byte slot (col - n0) / 4 of tile row rt, swizzled (c_slot_xor)
+          const int slot = ((col - n0) >> 2) ^ c_slot_xor(rt);
           *reinterpret_cast<u32x2*>(lds + rt * (kPreBN * 2) + slot * 8) = u32x2{w0, w1};
         } else if (row < T) {
           if ((ldc & 3) == 0 && col + 3 < N) {
@@ -588,25 +601,24 @@ __device__ __forceinline__ void prefill_tile(const PreArgs& a, const PreItem& it
   }
   if (c_stage) {
     __syncthreads();
-    constexpr int kChunks = BM * TN / 8;           // 16-byte chunks of the tile
-    const int tid_all = threadIdx.x;
-#pragma unroll 4
-    for (int c = tid_all; c < kChunks; c += kNT) {
-      const int rt = c / (TN / 8), ch = c % (TN / 8);
-      const int row = m0 + rt, col = n0 + ch * 8;
-      if (row >= T || col >= N) continue;
-      // logical slots 2 ch, 2 ch + 1 sit in the 16-byte chunk ch ^ (r / 2),
-      // in swapped order when r is odd (r = rt % 16)
-      const int r = rt & 15;
-      u32x4 v = *reinterpret_cast<const u32x4*>(lds + rt * (kPreBN * 2) + ((ch ^ (r >> 1)) * 16));
-      if (r & 1) v = u32x4{v[2], v[3], v[0], v[1]};
-      LB_GLOBAL uint16_t* cp = gp(C) + (int64_t)row * ldc + col;
-      if (col + 7 < N) {
-        *reinterpret_cast<LB_GLOBAL u32x4*>(cp) = v;
-      } else {
+    // thread t copies 16-byte chunk ch = t % (TN / 8) of tile rows r0 + k RS
+    // (r0 = t / (TN / 8)); C rows are whole multiples of 8 elements here
+    // (ldc = N, a multiple of 8), so a chunk is wholly inside or outside.  Rows
+    // r0 + k RS have the same swizzle when RS is a multiple of 16 and two that
+    // alternate when it is 8.
+    constexpr int kCPR = TN / 8, RS = kNT / kCPR, NIT = BM / RS;
+    static_assert(RS % 8 == 0 && BM % RS == 0, "whole rows per pass, a multiple of 8");
+    const int tid_all = threadIdx.x, ch = tid_all % kCPR, r0 = tid_all / kCPR;
+    const int col = n0 + ch * 8;
+    if (col < N) {
+      const uint8_t* lb0 = lds + r0 * (kPreBN * 2) + ((ch ^ (c_slot_xor(r0) >> 1)) * 16);
+      const uint8_t* lb1 = lds + (r0 + 8) * (kPreBN * 2) + ((ch ^ (c_slot_xor(r0 + 8) >> 1)) * 16);
+      LB_GLOBAL uint16_t* cp = gp(C) + (int64_t)(m0 + r0) * ldc + col;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          if (col + i < N) cp[i] = (uint16_t)(v[i >> 1] >> (16 * (i & 1)));
+      for (int k = 0; k < NIT; ++k) {
+        if (m0 + r0 + k * RS >= T) break;
+        const uint8_t* lp = RS % 16 == 0 ? lb0 + k * RS * (kPreBN * 2) : (k & 1 ? lb1 : lb0) + (k >> 1) * 16 * (kPreBN * 2);
+        *reinterpret_cast<LB_GLOBAL u32x4*>(cp + (int64_t)k * RS * ldc) = *reinterpret_cast<const u32x4*>(lp);
       }
     }
   }
