@@ -524,16 +524,26 @@ def run_chained(r, lb, torch, steps=20, warmup=5):
         src = {"q": inp, "k": inp, "v": inp, "o": ys[b + qi], "gate": ys[b + oi], "up": ys[b + oi],
                "down": ys[b + gi]}
         xs += [src[nm] for nm in names]
+    # one stack runs the levels in one persistent launch, the other (the
+    # default) as three launches per level; a graph replays the level launches
     S = lb.Stack(lins)
-    fns = {"direct": S.bind(xs, ys, regime=lb.REGIME_DECODE, use_graph=False).forward,
-           "graph": S.bind(xs, ys, regime=lb.REGIME_DECODE, use_graph=True).forward,
-           "auto": S.bind(xs, ys).forward}
+    S.set_persistent(1)
+    SL = lb.Stack(lins)
+    fns = {"persistent": S.bind(xs, ys, regime=lb.REGIME_DECODE, use_graph=False).forward,
+           "levels": SL.bind(xs, ys, regime=lb.REGIME_DECODE, use_graph=False).forward,
+           "graph": SL.bind(xs, ys, regime=lb.REGIME_DECODE, use_graph=True).forward,
+           "auto": SL.bind(xs, ys).forward}
     med = alternating(fns, steps, 2, torch)
+    st = S.persistent_status()
     out = {f"us_per_token_{k}": round(v * 1e3 / T, 1) for k, v in med.items()}
     out["levels"] = 4 * wl.layers
-    out["us_per_level_auto"] = round(med["auto"] * 1e3 / (4 * wl.layers), 2)
+    out["us_per_level_persistent"] = round(med["persistent"] * 1e3 / (4 * wl.layers), 2)
+    out["us_per_level_launches"] = round(med["levels"] * 1e3 / (4 * wl.layers), 2)
+    out["persistent_active"] = st["active"]
+    out["persistent_aborted"] = st["aborted"]
     out["workload"] = f"{wl.name}: {wl.count} linears chained in model order, batch {T}"
     S.close()
+    SL.close()
     return out
 
 
@@ -608,6 +618,8 @@ def main():
     ap.add_argument("--prefill-only", action="store_true", help="time only the prefill stack (for profiling)")
     ap.add_argument("--fp32-tiled-only", action="store_true",
                     help="time only the fp32 tiled (exact regime, many tokens) stack (for profiling)")
+    ap.add_argument("--chained-only", action="store_true",
+                    help="time only the headline stack chained in model order (persistent launch, level launches)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-context", action="store_true",
                     help="skip the launch-form and replay timings, the token sweep, the other stacks, the "
@@ -650,6 +662,11 @@ def main():
         return
     r = run_decode(args, lb, torch)
     wl, T = r["wl"], r["T"]
+    if args.chained_only:
+        c = run_chained(r, lb, torch, steps=max(5, args.steps // 10))
+        log(f"chained decode: {c}")
+        print(json.dumps({"chained_decode": c}), flush=True)
+        return
     log(f"decode: {r['kern_ms'] * 1e3:.1f} us/step (events), {r['ms'] * 1e3:.1f} us/step (wall), {r['gbps']:.0f} GB/s")
     us_per_token = r["ms"] * 1e3 / T
     out = {

@@ -32,7 +32,8 @@ EXPORTS = [
     "lb_linear_create", "lb_linear_forward", "lb_linear_forward_ex", "lb_linear_forward_noalloc", "lb_auto_regime",
     "lb_linear_info",
     "lb_linear_destroy",
-    "lb_stack_create", "lb_stack_forward", "lb_stack_forward_ex", "lb_stack_destroy", "lb_status_string",
+    "lb_stack_create", "lb_stack_forward", "lb_stack_forward_ex", "lb_stack_set_persistent",
+    "lb_stack_persistent_status", "lb_stack_destroy", "lb_status_string",
     "lb_last_error", "lb_init_dual_svid",
 ]
 
@@ -82,6 +83,8 @@ def lib():
         "lb_stack_create": (C.c_int, [C.POINTER(vp), i32, C.POINTER(vp)]),
         "lb_stack_forward": (C.c_int, [vp, C.POINTER(vp), C.POINTER(vp), i64, C.c_int, vp]),
         "lb_stack_forward_ex": (C.c_int, [vp, C.POINTER(vp), C.POINTER(vp), i64, C.c_int, C.c_int, i32, vp]),
+        "lb_stack_set_persistent": (C.c_int, [vp, i32]),
+        "lb_stack_persistent_status": (C.c_int, [vp, C.POINTER(i32), C.POINTER(i32)]),
         "lb_stack_destroy": (C.c_int, [vp]),
         "lb_status_string": (C.c_char_p, [C.c_int]),
         "lb_last_error": (C.c_char_p, []),
@@ -311,6 +314,23 @@ class Stack:
         return BoundStack(self, xs, ys, regime, use_graph, stream)
 
     __call__ = forward
+
+    def set_persistent(self, mode) -> None:
+        """lb_stack_set_persistent: run a chained decode's levels in one
+        persistent launch (True or 1), as launches per level (False or 0, the
+        default), or the persistent kernel's plans as launches per level (2,
+        the same bits as 1)."""
+        m = int(mode)
+        if m not in (0, 1, 2):
+            raise ValueError("mode must be 0, 1 or 2")
+        _check(lib().lb_stack_set_persistent(self.handle, m))
+
+    def persistent_status(self) -> Dict:
+        """lb_stack_persistent_status: whether the current plan runs the
+        persistent kernel, and whether a launch of it gave up (synchronises)."""
+        active, aborted = C.c_int32(), C.c_int32()
+        _check(lib().lb_stack_persistent_status(self.handle, C.byref(active), C.byref(aborted)))
+        return dict(active=bool(active.value), aborted=bool(aborted.value))
 
     def close(self):
         if getattr(self, "handle", None) is not None and self.handle.value:

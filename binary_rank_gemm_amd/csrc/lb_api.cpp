@@ -197,6 +197,22 @@ struct lb_stack_s {
   int64_t auto_tokens = -1;
   int auto_io = -1;
   lb_regime auto_rg = LB_REGIME_DECODE;
+  // persistent chained decode (lb_stack_set_persistent): all levels of a
+  // chained decode in one cooperative launch of k_decode_chain
+  int chain_enable = 0;                     // lb_stack_set_persistent's mode (0: level launches)
+  int chain_active = 0;                     // the current plans run it
+  int chain_grid = 0, chain_bucket = 0, chain_nlev = 0;
+  ChainLevel* chain_levels_d = nullptr;     // per level: its decode tables and buffers
+  std::vector<DecodePlan> chain_plans;      // per level, planned for the kernel's participants
+  Scratch chain_sync;                       // epoch, abort flag, barrier and mid counters
+  void chain_release() {
+    if (chain_levels_d) (void)hipFree(chain_levels_d);
+    chain_levels_d = nullptr;
+    for (DecodePlan& P : chain_plans) P.release();
+    chain_plans.clear();
+    chain_active = 0;
+    chain_grid = chain_bucket = chain_nlev = 0;
+  }
 };
 
 namespace {
@@ -257,7 +273,8 @@ struct DecodeHostPlan {
   size_t work_bytes = 0;            // U-stage operands and correction sums
 };
 
-void plan_decode_host(DecodeHostPlan& H, const lb_linear* L, int count, int T, const DecodeImage* img) {
+void plan_decode_host(DecodeHostPlan& H, const lb_linear* L, int count, int T, const DecodeImage* img,
+                      int item_slots = 0) {
   const int bucket = decode_bucket(T), tb = (bucket + 7) / 8, ct_max = decode_v_tiles(bucket);
   H.entries.assign(count, DecEntry{});
   H.img_off.assign(count, 0);
@@ -275,7 +292,7 @@ void plan_decode_host(DecodeHostPlan& H, const lb_linear* L, int count, int T, c
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, L[0]->device) != hipSuccess || cus <= 0)
     cus = 256;
-  const double slots_per_launch = (double)cus * (bucket >= 16 ? 2 : 3);
+  const double slots_per_launch = item_slots > 0 ? (double)item_slots : (double)cus * (bucket >= 16 ? 2 : 3);
   double vtotal = 0, utotal = 0;
   for (int e = 0; e < count; ++e) {
     const int nkc = (int)((L[e]->n + kChunk - 1) / kChunk);
@@ -316,7 +333,7 @@ void plan_decode_host(DecodeHostPlan& H, const lb_linear* L, int count, int T, c
           // group of chunks, then each chunk's sign steps), per wave
           const int ch = c1 - c0, grp = bucket == 1 ? (ch + 1) / 2 : ch;
           const double cost = ((double)grp * ((bucket + 4) / 4) + (double)ch * ((nt + 3) / 4)) / kWavesPerGroup;
-          vl.push_back({cost, VItem{e, p, tile0, nt, c0, c1, slots + g * nsplit + sp, 0}});
+          vl.push_back({cost, VItem{e, p, tile0, nt, c0, c1, slots + g * nsplit + sp, (int)H.mitems.size() - 1}});
         }
       }
       slots += groups * nsplit;
@@ -342,14 +359,16 @@ void plan_decode_host(DecodeHostPlan& H, const lb_linear* L, int count, int T, c
 
 // Builds (or reuses) the decode plan for `count` linears at `T` tokens per
 // launch: the host plan, its scratch buffers and its tables on the device.
-lb_status build_decode_plan(DecodePlan& P, const lb_linear* L, int count, int T, const DecodeImage* img = nullptr) {
+// slots: work-item slots the launch has (0: every workgroup slot of the GPU).
+lb_status build_decode_plan(DecodePlan& P, const lb_linear* L, int count, int T, const DecodeImage* img = nullptr,
+                            int slots = 0) {
   if (P.T == T && P.count == count) return LB_OK;
   // the buffers and tables below are freed and reallocated: until every step
   // has succeeded the plan must not look valid for any token count
   P.T = -1;
   P.count = 0;
   DecodeHostPlan H;
-  plan_decode_host(H, L, count, T, img);
+  plan_decode_host(H, L, count, T, img, slots);
   HIP_TRY(P.work.ensure(H.work_bytes));
   HIP_TRY(P.part.ensure(H.part_bytes));
   for (int e = 0; e < count; ++e) {
@@ -961,9 +980,25 @@ lb_status lb_stack_create(const lb_linear* linears, int32_t count, lb_stack* out
 
 namespace {
 
-// Enqueues the stack's kernels on `st` (no graph).
-lb_status stack_launch(lb_stack S, lb_regime rg, int64_t tokens, lb_dtype io, hipStream_t st) {
+// Enqueues the stack's kernels on `st`; `capture`: into a graph being
+// captured (level launches only).
+lb_status stack_launch(lb_stack S, lb_regime rg, int64_t tokens, lb_dtype io, hipStream_t st, bool capture) {
   const int count = (int)S->linears.size();
+  if (rg == LB_REGIME_DECODE && S->chain_active) {
+    if (S->chain_enable == 1 && !capture) {
+      const ChainArgs c{S->chain_levels_d, reinterpret_cast<uint64_t*>(S->chain_sync.ptr), S->chain_nlev, 0};
+      HIP_TRY(launch_decode_chain(c, S->chain_bucket, S->chain_grid, st));
+      return LB_OK;
+    }
+    // the same plans as launches per level (a graph, or mode 2): the same bits
+    for (size_t g = 0; g < S->groups.size(); ++g) {
+      StackGroup& G = S->groups[g];
+      lb_status s = run_decode(S->chain_plans[g], G.lins.data(), (int)G.lins.size(), G.xs_d, G.ys_d, nullptr, nullptr,
+                               tokens, y_is_fp32(io), st, &G.view);
+      if (s != LB_OK) return s;
+    }
+    return LB_OK;
+  }
   if (rg == LB_REGIME_DECODE) {
     for (StackGroup& G : S->groups) {
       lb_status s = run_decode(G.plan, G.lins.data(), (int)G.lins.size(), G.xs_d, G.ys_d, nullptr, nullptr, tokens,
@@ -1049,8 +1084,63 @@ lb_status stack_groups(lb_stack S, int64_t tokens, lb_dtype io) {
   return LB_OK;
 }
 
+// The persistent chained decode for the stack's levels, when it can run
+// them: more than one level, one launch of at most kDecodeMaxTokens tokens,
+// bf16 y, every entry in the kernel's fast forms, and a device that can
+// launch all of its workgroups at once.  Otherwise the levels run as launches
+// (chain_active stays 0).  Direct launches use it; a captured graph holds
+// the level launches (both give the same bits).
+lb_status chain_prepare(lb_stack S, int64_t tokens, lb_dtype io, hipStream_t st) {
+  S->chain_release();
+  if (!S->chain_enable || S->groups.size() < 2 || tokens > kDecodeMaxTokens || y_is_fp32(io)) return LB_OK;
+  const int bucket = decode_bucket((int)tokens);
+  for (const StackGroup& G : S->groups)
+    for (const DecEntry& e : G.plan.entries_h)
+      if (!decode_chain_takes(e, bucket)) return LB_OK;
+  const int grid = decode_chain_grid(bucket, S->device);
+  if (grid <= 0) return LB_OK;
+  const int slots = decode_chain_participants(grid);
+  S->chain_plans.resize(S->groups.size());
+  std::vector<ChainLevel> lv;
+  int moff = 0;
+  for (size_t g = 0; g < S->groups.size(); ++g) {
+    StackGroup& G = S->groups[g];
+    DecodePlan& P = S->chain_plans[g];
+    lb_status s = build_decode_plan(P, G.lins.data(), (int)G.lins.size(), (int)tokens, &G.view, slots);
+    if (s != LB_OK) return s;
+    ChainLevel c{};
+    c.a.entries = P.entries_d;
+    c.a.xs = G.xs_d;
+    c.a.ys = G.ys_d;
+    c.a.vitems = P.vitems_d;
+    c.a.mitems = P.mitems_d;
+    c.a.uitems = P.uitems_d;
+    c.a.part = reinterpret_cast<float*>(P.part.ptr);
+    c.a.T = (int)tokens;
+    c.a.t0 = 0;
+    c.a.bucket = bucket;
+    c.a.yf32 = 0;
+    c.nv = P.nv;
+    c.nm = P.nm;
+    c.nu = P.nu;
+    c.moff = moff;
+    moff += P.nm;
+    lv.push_back(c);
+  }
+  HIP_TRY(upload(&S->chain_levels_d, lv));
+  // counters start at zero for a new plan (stream-ordered before its first launch)
+  HIP_TRY(S->chain_sync.ensure(chain_sync_bytes(moff)));
+  HIP_TRY(hipMemsetAsync(S->chain_sync.ptr, 0, chain_sync_bytes(moff), st));
+  S->chain_grid = grid;
+  S->chain_bucket = bucket;
+  S->chain_nlev = (int)lv.size();
+  S->chain_active = 1;
+  return LB_OK;
+}
+
 // Prepares everything a launch sequence needs outside of any graph capture.
-lb_status stack_prepare(lb_stack S, lb_regime rg, int64_t tokens, lb_dtype io) {
+lb_status stack_prepare(lb_stack S, lb_regime rg, int64_t tokens, lb_dtype io, hipStream_t st) {
+  S->chain_release();
   if (rg == LB_REGIME_DECODE) {
     lb_status s = stack_groups(S, tokens, io);
     if (s != LB_OK) return s;
@@ -1059,6 +1149,8 @@ lb_status stack_prepare(lb_stack S, lb_regime rg, int64_t tokens, lb_dtype io) {
       s = build_decode_plan(G.plan, G.lins.data(), (int)G.lins.size(), T, &G.view);
       if (s != LB_OK) return s;
     }
+    s = chain_prepare(S, tokens, io, st);
+    if (s != LB_OK) return s;
     // (a ragged last slice of a long decode uses another plan shape: those
     // runs launch directly and rebuild the plan per slice)
   } else if (rg == LB_REGIME_PREFILL) {
@@ -1122,8 +1214,9 @@ lb_status lb_stack_forward_ex(lb_stack S, const void* const* xs, void* const* ys
     S->groups.clear();
     S->xs_h.assign(xs, xs + count);
     S->ys_h.assign(ys, ys + count);
-    s = stack_prepare(S, rg, tokens, io);
+    s = stack_prepare(S, rg, tokens, io, st);
     if (s != LB_OK) {
+      S->chain_release();
       for (StackGroup& G : S->groups) G.release();
       S->groups.clear();
       S->xs_h.clear();
@@ -1136,10 +1229,10 @@ lb_status lb_stack_forward_ex(lb_stack S, const void* const* xs, void* const* ys
   }
   S->last_stream = st;
   const bool ragged_decode = rg == LB_REGIME_DECODE && tokens > kDecodeMaxTokens && tokens % kDecodeMaxTokens;
-  if (!use_graph || ragged_decode) return stack_launch(S, rg, tokens, io, st);
+  if (!use_graph || ragged_decode) return stack_launch(S, rg, tokens, io, st, false);
   if (!S->exec) {
     HIP_TRY(hipStreamBeginCapture(S->cap_stream, hipStreamCaptureModeThreadLocal));
-    lb_status ls = stack_launch(S, rg, tokens, io, S->cap_stream);
+    lb_status ls = stack_launch(S, rg, tokens, io, S->cap_stream, true);
     hipGraph_t g = nullptr;
     hipError_t ce = hipStreamEndCapture(S->cap_stream, &g);
     if (ls != LB_OK) {
@@ -1161,11 +1254,44 @@ lb_status lb_stack_forward(lb_stack S, const void* const* xs, void* const* ys, i
   return lb_stack_forward_ex(S, xs, ys, tokens, io, LB_REGIME_AUTO, enum_bits(io) == LB_FP32 ? 1 : 0, stream);
 }
 
+lb_status lb_stack_set_persistent(lb_stack S, int32_t enable) {
+  if (!S) return fail(LB_ERR_INVALID_ARGUMENT, "null stack");
+  if (enable < 0 || enable > 2) return fail(LB_ERR_INVALID_ARGUMENT, "enable must be 0, 1 or 2");
+  if (S->chain_enable != enable) {
+    S->chain_enable = enable;
+    S->g_tokens = -1;                       // the next forward plans again
+  }
+  return LB_OK;
+}
+
+lb_status lb_stack_persistent_status(lb_stack S, int32_t* active, int32_t* aborted) {
+  if (!S) return fail(LB_ERR_INVALID_ARGUMENT, "null stack");
+  if (active) *active = S->chain_active;
+  if (aborted) {
+    *aborted = 0;
+    if (S->chain_sync.ptr) {
+      int dev = 0;
+      HIP_TRY(hipGetDevice(&dev));
+      if (dev != S->device) HIP_TRY(hipSetDevice(S->device));
+      uint64_t flag = 0;
+      hipError_t e = S->last_stream ? hipStreamSynchronize(S->last_stream) : hipSuccess;
+      if (e == hipSuccess) e = hipMemcpy(&flag, reinterpret_cast<uint64_t*>(S->chain_sync.ptr) + kChainAbort, 8,
+                                         hipMemcpyDeviceToHost);
+      if (dev != S->device) (void)hipSetDevice(dev);
+      if (e != hipSuccess) return hip_fail(e, "reading the persistent kernel's abort flag");
+      *aborted = flag != 0;
+    }
+  }
+  return LB_OK;
+}
+
 lb_status lb_stack_destroy(lb_stack S) {
   if (!S) return LB_OK;
   if (S->exec) (void)hipGraphExecDestroy(S->exec);
   if (S->graph) (void)hipGraphDestroy(S->graph);
   if (S->cap_stream) (void)hipStreamDestroy(S->cap_stream);
+  S->chain_release();
+  S->chain_sync.release();
   for (StackGroup& G : S->groups) G.release();
   S->zexact.release();
   S->dimg.buf.release();

@@ -83,6 +83,20 @@ __device__ inline T cld(const LB_CONST T* p) {
   return v;
 }
 
+// Loads of data another workgroup wrote earlier in the same launch (HL = true,
+// the persistent chained kernel, whose workgroups all run on one XCD): group-
+// scope loads, which miss in the compute unit's vector cache and read the
+// XCD's L2, where the writer's stores have landed.  Other launches (HL =
+// false) read plainly: a kernel boundary makes the data visible.
+template <bool HL, class T>
+__device__ inline T ld_h(const LB_GLOBAL T* p) {
+  if constexpr (HL) return __hip_atomic_load(const_cast<LB_GLOBAL T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  else return *p;
+}
+// cache policy of direct-to-LDS loads of such data (x): group scope when HL
+template <bool HL>
+constexpr int kHandAux = HL ? 1 : 0;
+
 __device__ inline float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 __device__ inline float f16f(uint16_t b) { return __half2float(__ushort_as_half(b)); }
 
@@ -205,14 +219,23 @@ __device__ inline float convert_pair(const ConvLane& L, float t0, float t1, int 
 // Reads lane (mr, gr)'s A operand and scale from an A image (LDS or global).
 // Rows past the real tokens hold stale values: MFMA rows are independent and
 // those rows of the result are never read.
-template <class Ptr>
+template <bool HL = false, class Ptr>
 __device__ inline void load_a(Ptr ab, int mr, int gr, v8i& a, int& sc) {
-  using V4 = typename std::conditional<std::is_same<Ptr, const uint8_t*>::value || std::is_same<Ptr, uint8_t*>::value,
-                                      const v4i, const LB_GLOBAL v4i>::type;
-  const v4i lo = *reinterpret_cast<V4*>(ab + img_off(mr, gr, 0));
-  const v4i hi = *reinterpret_cast<V4*>(ab + img_off(mr, gr, 16));
-  a = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  sc = ab[2048 + mr * 4 + gr];
+  constexpr bool kLds = std::is_same<Ptr, const uint8_t*>::value || std::is_same<Ptr, uint8_t*>::value;
+  if constexpr (HL && !kLds) {
+    // hand-over loads of 8 bytes (the widest such load)
+    const LB_GLOBAL uint64_t* lo = reinterpret_cast<const LB_GLOBAL uint64_t*>(ab + img_off(mr, gr, 0));
+    const LB_GLOBAL uint64_t* hi = reinterpret_cast<const LB_GLOBAL uint64_t*>(ab + img_off(mr, gr, 16));
+    const uint64_t w0 = ld_h<true>(lo), w1 = ld_h<true>(lo + 1), w2 = ld_h<true>(hi), w3 = ld_h<true>(hi + 1);
+    a = v8i{(int)w0, (int)(w0 >> 32), (int)w1, (int)(w1 >> 32), (int)w2, (int)(w2 >> 32), (int)w3, (int)(w3 >> 32)};
+    sc = ld_h<true>(ab + 2048 + mr * 4 + gr);
+  } else {
+    using V4 = typename std::conditional<kLds, const v4i, const LB_GLOBAL v4i>::type;
+    const v4i lo = *reinterpret_cast<V4*>(ab + img_off(mr, gr, 0));
+    const v4i hi = *reinterpret_cast<V4*>(ab + img_off(mr, gr, 16));
+    a = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    sc = ab[2048 + mr * 4 + gr];
+  }
 }
 
 
@@ -229,8 +252,9 @@ typedef const __attribute__((address_space(1))) void gbl_void;
 
 // 16 bytes per lane from global memory straight into LDS: lane l's bytes land
 // at lds_block + 16 l.
+template <int AUX = 0>
 __device__ inline void dma16(const LB_GLOBAL void* src, void* lds_block) {
-  __builtin_amdgcn_global_load_lds((gbl_void*)src, (lds_void*)lds_block, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds((gbl_void*)src, (lds_void*)lds_block, 16, 0, AUX);
 }
 // The same with the non-temporal cache policy (NT), for data a step reads
 // exactly once (the sign words and row scales): measured on MI355X, a ring of
@@ -291,7 +315,7 @@ struct VShape {
 // the wave's ring (x rows of n % 8 == 0 elements).  The chunks go in groups of
 // G (two at one token, so that one 1 KB step carries both chunks' g and x
 // rows), each group being its x/g steps followed by each chunk's sign steps.
-template <int TM>
+template <int TM, bool HL>
 __device__ __attribute__((always_inline)) inline void v_stream(const DecArgs& a, const VItem& it, int n, int nct,
                                                               const LB_GLOBAL uint8_t* xb, const LB_GLOBAL uint8_t* gdec,
                                                               const LB_GLOBAL uint8_t* vdec, int ca, int cb, uint8_t* ring,
@@ -351,7 +375,7 @@ __device__ __attribute__((always_inline)) inline void v_stream(const DecArgs& a,
       last_signs = false;
     }
     if (last_signs) dma16_once<TM>(last, ring + slot * 1024);
-    else dma16(last, ring + slot * 1024);
+    else dma16<kHandAux<HL>>(last, ring + slot * 1024);
   };
 #pragma unroll
   for (int k = 0; k < kRing - 1; ++k) issue(k);
@@ -490,12 +514,12 @@ __device__ __attribute__((always_inline)) inline void v_plain(const DecArgs& a, 
   }
 }
 
-template <int TM>
-__global__ void __launch_bounds__(kThreads, TM >= 16 ? 2 : 3) k_decode_v(DecArgs a) {
+// One V work item on this workgroup (lds: VShape<TM>::lds bytes).  HL: x is
+// read with hand-over loads (only entries with xdirect).
+template <int TM, bool HL>
+__device__ __attribute__((always_inline)) inline void v_item(const DecArgs& a, const VItem& it, uint8_t* lds) {
   using S = VShape<TM>;
   constexpr int TB = S::TB, CT = S::CT;
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  const VItem it = cld(cp(a.vitems) + blockIdx.x);
   const LB_CONST DecEntry& Eg = cp(a.entries)[it.entry];
   const int tid = threadIdx.x, lane = tid & 63, mr = lane & 15, gr = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -524,7 +548,7 @@ __global__ void __launch_bounds__(kThreads, TM >= 16 ? 2 : 3) k_decode_v(DecArgs
 #pragma unroll
   for (int t = 0; t < TM; ++t) cpart[t] = 0.f;
   if (ca < cb) {
-    if (xdirect) v_stream<TM>(a, it, n, nct, xb, gdec, vdec, ca, cb, ring, abuf, acc, cpart);
+    if (HL || xdirect) v_stream<TM, HL>(a, it, n, nct, xb, gdec, vdec, ca, cb, ring, abuf, acc, cpart);
     else v_plain<TM>(a, it, n, nct, xb, gdec, vdec, ca, cb, abuf, acc, cpart);
   }
 
@@ -588,6 +612,12 @@ __global__ void __launch_bounds__(kThreads, TM >= 16 ? 2 : 3) k_decode_v(DecArgs
   }
 }
 
+template <int TM>
+__global__ void __launch_bounds__(kThreads, TM >= 16 ? 2 : 3) k_decode_v(DecArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  v_item<TM, false>(a, cld(cp(a.vitems) + blockIdx.x), lds);
+}
+
 // ---------------------------------------------------------------------------
 // mid stage
 // ---------------------------------------------------------------------------
@@ -595,11 +625,14 @@ __global__ void __launch_bounds__(kThreads, TM >= 16 ? 2 : 3) k_decode_v(DecArgs
 // written as the U stage's A operands: each 16-lane row takes one (token,
 // 32-latent block), lane sub holding latents 2 sub and 2 sub + 1 of it.  Every
 // block of the path's units is written (zeros past the rank).
-template <int TM>
-__global__ void __launch_bounds__(kThreads) k_decode_mid(DecArgs a) {
+// Floats of LDS the mid step uses (per-block correction sums).
+constexpr int kMidLdsFloats = kDecodeMaxTokens * 4 * (LB_MAX_RANK / kChunk);
+
+// One mid work item on this workgroup (cblk: kMidLdsFloats floats of LDS).
+// HL: the partial sums are read with hand-over loads.
+template <int TM, bool HL>
+__device__ __attribute__((always_inline)) inline void mid_item(const DecArgs& a, const MItem& it, float* cblk) {
   constexpr int TB = (TM + 7) / 8, CT = decode_v_tiles(TM), SF = decode_slot_floats(TM);
-  __shared__ float cblk[kDecodeMaxTokens * 4 * (LB_MAX_RANK / kChunk)];
-  const MItem it = cld(cp(a.mitems) + blockIdx.x);
   const LB_CONST DecEntry& E = cp(a.entries)[it.entry];
   const int p = it.path, r = E.p[p].r, T = a.T;
   const LB_GLOBAL uint16_t* lsc = gp(E.p[p].l);
@@ -612,41 +645,35 @@ __global__ void __launch_bounds__(kThreads) k_decode_mid(DecArgs a) {
     const int jj = 32 * blk + 2 * sub;             // latents jj, jj + 1
     const ConvLane LK(((jj % kChunk) / 32) * 16 + sub);
     // the partial sums of both latents over the splits, added in split order;
-    // the loads of up to kB splits go out together
-    constexpr int kB = 8;
-    const LB_GLOBAL float* sp[2];
-    int off[2];
-    bool in[2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int j = jj + q, tile = j / 16, col = j % 16, g = tile / it.gtiles, tl = tile - g * it.gtiles;
-      in[q] = j < r;
-      sp[q] = part + (int64_t)(it.slot0 + g * it.nsplit) * SF;
-      off[q] = (tl * TM + t) * 16 + col;
-    }
-    float d[2] = {0.f, 0.f}, c[2] = {0.f, 0.f};
+    // the loads of up to kB splits go out together (the two latents share a
+    // column tile, hence a partial slot and its correction sum)
+    constexpr int kB = 32;
+    const int tile = jj / 16, col = jj % 16, g = tile / it.gtiles, tl = tile - g * it.gtiles;
+    const bool in[2] = {jj < r, jj + 1 < r};
+    const LB_GLOBAL float* sp = part + (int64_t)(it.slot0 + g * it.nsplit) * SF;
+    const int off = (tl * TM + t) * 16 + col;
+    float d[2] = {0.f, 0.f}, c = 0.f;
     for (int s0 = 0; s0 < it.nsplit; s0 += kB) {
-      float dv[2][kB], cv[2][kB];
+      float dv[2][kB], cv[kB];
 #pragma unroll
-      for (int q = 0; q < 2; ++q)
+      for (int i = 0; i < kB; ++i)
+        if (in[0] && s0 + i < it.nsplit) {
+          const LB_GLOBAL float* q = sp + (int64_t)(s0 + i) * SF;
+          dv[0][i] = ld_h<HL>(q + off);
+          if (in[1]) dv[1][i] = ld_h<HL>(q + off + 1);
+          cv[i] = ld_h<HL>(q + CT * TM * 16 + t);
+        }
 #pragma unroll
-        for (int i = 0; i < kB; ++i)
-          if (in[q] && s0 + i < it.nsplit) {
-            dv[q][i] = sp[q][(int64_t)(s0 + i) * SF + off[q]];
-            cv[q][i] = sp[q][(int64_t)(s0 + i) * SF + CT * TM * 16 + t];
-          }
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
-#pragma unroll
-        for (int i = 0; i < kB; ++i)
-          if (in[q] && s0 + i < it.nsplit) {
-            d[q] += dv[q][i];
-            c[q] += cv[q][i];
-          }
+      for (int i = 0; i < kB; ++i)
+        if (in[0] && s0 + i < it.nsplit) {
+          d[0] += dv[0][i];
+          if (in[1]) d[1] += dv[1][i];
+          c += cv[i];
+        }
     }
     float v[2];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) v[q] = in[q] ? (d[q] + c[q]) * f16f(lsc[jj + q]) * LK.fcls : 0.f;
+    for (int q = 0; q < 2; ++q) v[q] = in[q] ? (d[q] + c) * f16f(lsc[jj + q]) * LK.fcls : 0.f;
     uint8_t* ab = E.aimg + ((int64_t)(ufirst + jj / kChunk) * TB + tb) * kABytes;
     const float cc = row16_sum(convert_pair(LK, v[0], v[1], tt, gp(ab)));
     if (sub == 0) cblk[u] = cc;
@@ -657,6 +684,12 @@ __global__ void __launch_bounds__(kThreads) k_decode_mid(DecArgs a) {
     for (int blk = 0; blk < nblk; ++blk) s += cblk[tid * nblk + blk];
     gp(E.cval)[p * 16 + tid] = s;
   }
+}
+
+template <int TM>
+__global__ void __launch_bounds__(kThreads) k_decode_mid(DecArgs a) {
+  __shared__ float cblk[kMidLdsFloats];
+  mid_item<TM, false>(a, cld(cp(a.mitems) + blockIdx.x), cblk);
 }
 
 // ---------------------------------------------------------------------------
@@ -776,7 +809,7 @@ __device__ __attribute__((always_inline)) inline void u_flush(const UCtx<TM>& C,
 
 // Fast form: NPC units, operands in registers, every read through the ring.
 // Steps per quad: the row scales, then one per unit.
-template <int TM, int NPC>
+template <int TM, int NPC, bool HL>
 __device__ __attribute__((always_inline)) inline void u_stream(const DecArgs& a, const LB_CONST DecEntry& Eg, UCtx<TM>& C,
                                                               int qa, int qb, uint8_t* ring, uint8_t* stg) {
   using S = UShape<TM>;
@@ -818,7 +851,7 @@ __device__ __attribute__((always_inline)) inline void u_stream(const DecArgs& a,
   for (int u = 0; u < NPC; ++u)
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
-      if (mr < 2 * C.T) load_a(aimg + (int64_t)(u * TB + tb) * kABytes, mr, gr, A[u][tb], sc[u][tb]);
+      if (mr < 2 * C.T) load_a<HL>(aimg + (int64_t)(u * TB + tb) * kABytes, mr, gr, A[u][tb], sc[u][tb]);
       else {
         A[u][tb] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
         sc[u][tb] = 127;
@@ -934,12 +967,14 @@ __device__ __attribute__((always_inline)) inline void u_plain(const DecArgs& a, 
 }
 
 // YF: y is fp32 (a separate instantiation, so the bf16 kernel carries none of it)
-template <int TM, bool YF>
-__global__ void __launch_bounds__(kThreads, TM >= 16 ? 2 : 3) k_decode_u(DecArgs a) {
+// One U work item on this workgroup (lds: UShape<TM>::lds bytes).  HL: the
+// persistent chained kernel's form: A operands and correction sums read with
+// hand-over loads, and only entries whose units fit the fast form (the plain
+// form is left out).
+template <int TM, bool YF, bool HL>
+__device__ __attribute__((always_inline)) inline void u_item(const DecArgs& a, const UItem& it, uint8_t* lds) {
   using S = UShape<TM>;
   constexpr int TB = S::TB;
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  const UItem it = cld(cp(a.uitems) + blockIdx.x);
   const LB_CONST DecEntry& Eg = cp(a.entries)[it.entry];
   const int lane = threadIdx.x & 63, gr = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -962,16 +997,183 @@ __global__ void __launch_bounds__(kThreads, TM >= 16 ? 2 : 3) k_decode_u(DecArgs
 #pragma unroll
       for (int qq = 0; qq < 2; ++qq) {
         const int t = tb * 8 + 2 * gr + qq;
-        C.cv[p][tb][qq] = (p < C.np && t < C.T && t < TM) ? cval[p * 16 + t] : 0.f;
+        C.cv[p][tb][qq] = (p < C.np && t < C.T && t < TM) ? ld_h<HL>(cval + p * 16 + t) : 0.f;
       }
   uint8_t* ring = lds + wave * kRingBytes;
   uint8_t* stg = lds + kWaves * kRingBytes + wave * S::STG;
   const int nu = Eg.ug.nu;
   static_for<S::NMAX>([&](auto I) __attribute__((always_inline)) {
     constexpr int k = decltype(I)::value + 1;
-    if (nu == k) u_stream<TM, k>(a, Eg, C, qa, qb, ring, stg);
+    if (nu == k) u_stream<TM, k, HL>(a, Eg, C, qa, qb, ring, stg);
   });
-  if (nu > S::NMAX) u_plain<TM>(a, Eg, C, qa, qb);
+  if constexpr (!HL) {
+    if (nu > S::NMAX) u_plain<TM>(a, Eg, C, qa, qb);
+  }
+}
+
+template <int TM, bool YF>
+__global__ void __launch_bounds__(kThreads, TM >= 16 ? 2 : 3) k_decode_u(DecArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  u_item<TM, YF, false>(a, cld(cp(a.uitems) + blockIdx.x), lds);
+}
+
+// ---------------------------------------------------------------------------
+// Persistent chained decode
+// ---------------------------------------------------------------------------
+// A chained stack (entries reading earlier entries' outputs) runs level after
+// level, and at batch 1 each level is a few hundred KB to a few MB of sign
+// words: its time is the latency of its three dependent stages, not
+// bandwidth.  This kernel runs every level in one launch, on the compute
+// units of ONE XCD, so that the data one workgroup hands to another (partial
+// sums, A operands, correction sums, y as the next level's x) stays in that
+// XCD's L2: plain stores, and hand-over loads that miss in the compute unit's
+// vector cache and hit the L2 (ld_h, kHandAux), at L2 latency instead of a
+// trip to memory and a kernel boundary.  One XCD streams about 1.3 TB/s,
+// enough for levels of this size.  The counters are device-scope atomics
+// (performed where all XCDs see them), polled with device-scope loads.  Per
+// level: a V phase, in which the last V item to finish for an (entry, path)
+// runs that pair's mid step, then a U phase, each followed by a barrier of
+// the participating workgroups.  Work items (planned for the participants),
+// buffers and arithmetic are those of the kernels above, so the results are
+// the same bits as launches per level.
+//
+// The launch is cooperative over the whole GPU (all workgroups resident), a
+// multiple of 8 workgroups; the dispatcher hands workgroups to the 8 XCDs in
+// turn (from wherever the previous dispatch stopped), so each XCD holds an
+// eighth of them.  The participants are the workgroups that find themselves
+// on XCD 0 (hardware register XCC_ID); they take ranks from a ticket counter
+// (which workgroup runs which item does not change any result), and the
+// others leave at once.  A participant whose ticket is past the expected
+// count sets the abort flag.  Counters only grow: a launch reads the epoch
+// (launches of this plan so far) and aims at epoch-scaled targets, and rank 0
+// advances the epoch after the last barrier.
+
+constexpr int kChainXcds = 8;
+
+__device__ inline unsigned xcc_id() {
+  unsigned v;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+  return v & 0xf;
+}
+__device__ inline uint64_t dev_add(uint64_t* p, uint64_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline uint64_t dev_load(uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Longest wait at one barrier: 1 s of the 100 MHz constant clock.
+constexpr uint64_t kChainTimeoutTicks = 100000000ull;
+
+// Waits (thread 0) until *w reaches `target` or the abort flag is set; sets
+// the flag itself after kChainTimeoutTicks.  Returns false on abort.
+__device__ inline bool chain_wait(uint64_t* sync, uint64_t* w, uint64_t target) {
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  for (int i = 1; dev_load(w) < target; ++i) {
+    if ((i & 15) == 0) {
+      if (dev_load(sync + kChainAbort)) return false;
+      if (__builtin_amdgcn_s_memrealtime() - t0 > kChainTimeoutTicks) {
+        dev_add(sync + kChainAbort, 1);
+        return false;
+      }
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  return true;
+}
+
+// Barrier number `target` of the P participants (counted over all launches
+// of the plan): every wave first waits for its own stores (in the L2 once
+// complete), then thread 0 adds to the barrier counter and waits for
+// P x target.  Returns false when the launch was aborted (every participant
+// then leaves).
+__device__ inline bool chain_barrier(uint64_t* sync, uint64_t target, uint64_t P, int* flag) {
+  vm_wait<0>();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    dev_add(sync + kChainBar, 1);
+    *flag = chain_wait(sync, sync + kChainBar, target * P);
+  }
+  __syncthreads();
+  return *flag != 0;
+}
+
+template <int TM>
+__global__ void __launch_bounds__(kThreads, TM >= 16 ? 1 : 2) k_decode_chain(ChainArgs c) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  __shared__ int flag, rank_s;
+  __shared__ uint64_t epoch_s;
+  const int tid = threadIdx.x;
+  if (xcc_id() != 0) return;
+  const uint64_t P = gridDim.x / kChainXcds;
+  uint64_t* sync = c.sync;
+  if (tid == 0) {
+    const uint64_t epoch = dev_load(sync + kChainEpoch);
+    const uint64_t rank = dev_add(sync + kChainTicket, 1) - epoch * P;
+    flag = 1;
+    if (rank >= P) {                               // more workgroups on XCD 0 than an eighth
+      dev_add(sync + kChainAbort, 1);
+      flag = 0;
+    }
+    if (dev_load(sync + kChainAbort)) flag = 0;    // an aborted plan runs no more
+    epoch_s = epoch;
+    rank_s = (int)rank;
+  }
+  __syncthreads();
+  if (!flag) return;
+  const uint64_t epoch = epoch_s;
+  const int rank = rank_s;
+  uint64_t bar = epoch * 2 * (uint64_t)c.nlev;
+  for (int lev = 0; lev < c.nlev; ++lev) {
+    const ChainLevel L = cld(cp(c.levels) + lev);
+    for (int i = rank; i < L.nv; i += (int)P) {
+      const VItem it = cld(cp(L.a.vitems) + i);
+      v_item<TM, true>(L.a, it, lds);
+      vm_wait<0>();                                // this wave's partial sums are in the L2
+      __syncthreads();
+      if (tid == 0) {
+        const MItem mi = cld(cp(L.a.mitems) + it.mid);
+        const uint64_t need = (uint64_t)mi.ngroups * (uint64_t)mi.nsplit;
+        const uint64_t old = dev_add(sync + kChainCnt + kChainCntStride * (L.moff + it.mid), 1);
+        flag = old + 1 == (epoch + 1) * need;      // the last V item of its (entry, path)
+      }
+      __syncthreads();
+      if (flag) mid_item<TM, true>(L.a, cld(cp(L.a.mitems) + it.mid), reinterpret_cast<float*>(lds));
+      __syncthreads();                             // LDS is the next item's
+    }
+    if (!chain_barrier(sync, ++bar, P, &flag)) return;
+    for (int i = rank; i < L.nu; i += (int)P) {
+      u_item<TM, false, true>(L.a, cld(cp(L.a.uitems) + i), lds);
+      __syncthreads();
+    }
+    if (!chain_barrier(sync, ++bar, P, &flag)) return;
+  }
+  if (rank == 0 && tid == 0) __hip_atomic_store(sync + kChainEpoch, epoch + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int TM>
+constexpr size_t chain_lds() {
+  constexpr size_t v = VShape<TM>::lds, u = UShape<TM>::lds, m = (size_t)kMidLdsFloats * 4;
+  return v > u ? (v > m ? v : m) : (u > m ? u : m);
+}
+
+template <int TM>
+int chain_grid_of(int device) {
+  int coop = 0, cus = 0, per = 0;
+  if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, device) != hipSuccess || !coop) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus <= 0) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k_decode_chain<TM>, kThreads, chain_lds<TM>()) != hipSuccess)
+    return 0;
+  const int grid = per * cus;
+  return grid % kChainXcds == 0 ? grid : 0;        // an equal share per XCD
+}
+
+template <int TM>
+hipError_t launch_chain(const ChainArgs& c, int grid, hipStream_t st) {
+  ChainArgs arg = c;
+  void* args[] = {&arg};
+  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k_decode_chain<TM>), dim3(grid), dim3(kThreads),
+                                    args, (unsigned)chain_lds<TM>(), st);
 }
 
 }  // namespace
@@ -1016,6 +1218,37 @@ hipError_t launch_decode_u(const DecArgs& a, int nitems, hipStream_t st) {
   if (a.yf32) launch_u<true>(a, nitems, st);
   else launch_u<false>(a, nitems, st);
   return hipGetLastError();
+}
+
+}  // namespace lb
+
+namespace lb {
+
+bool decode_chain_takes(const DecEntry& e, int bucket) {
+  return e.xdirect != 0 && e.ug.nu <= (bucket > 8 ? UShape<16>::NMAX : UShape<8>::NMAX);
+}
+
+int decode_chain_grid(int bucket, int device) {
+  switch (bucket) {
+    case 1: return chain_grid_of<1>(device);
+    case 2: return chain_grid_of<2>(device);
+    case 4: return chain_grid_of<4>(device);
+    case 8: return chain_grid_of<8>(device);
+    default: return chain_grid_of<16>(device);
+  }
+}
+
+int decode_chain_participants(int grid) { return grid / kChainXcds; }
+
+hipError_t launch_decode_chain(const ChainArgs& c, int bucket, int grid, hipStream_t st) {
+  if (grid <= 0 || c.nlev <= 0) return hipErrorInvalidValue;
+  switch (bucket) {
+    case 1: return launch_chain<1>(c, grid, st);
+    case 2: return launch_chain<2>(c, grid, st);
+    case 4: return launch_chain<4>(c, grid, st);
+    case 8: return launch_chain<8>(c, grid, st);
+    default: return launch_chain<16>(c, grid, st);
+  }
 }
 
 }  // namespace lb

@@ -87,9 +87,9 @@ struct DecEntry {
 
 // V-stage work item (one workgroup): column tiles [tile0, tile0 + ntiles) of
 // one path over chunks [c0, c1) of 128 input rows; its partial sums go to
-// partial slot `slot`.
+// partial slot `slot`; `mid` is the index of its (entry, path)'s mid item.
 struct VItem {
-  int entry, path, tile0, ntiles, c0, c1, slot, pad;
+  int entry, path, tile0, ntiles, c0, c1, slot, mid;
 };
 // Mid-stage work item (one workgroup): one path of one entry; its V items are
 // `ngroups` column groups of `gtiles` tiles, each split into `nsplit` chunk
@@ -192,6 +192,41 @@ hipError_t launch_exact(const PathDev* p, int np, int m, int n, const void* x, v
 hipError_t launch_decode_v(const DecArgs& a, int nitems, hipStream_t st);
 hipError_t launch_decode_mid(const DecArgs& a, int nitems, hipStream_t st);
 hipError_t launch_decode_u(const DecArgs& a, int nitems, hipStream_t st);
+
+// Persistent chained decode: one launch runs the levels of a chained stack in
+// order, on the compute units of one XCD (hand-overs through its L2), each
+// level a V phase (whose last V item of every (entry, path) runs that pair's
+// mid step) and a U phase, with a barrier of the participating workgroups
+// after each phase.  Every level has its own plan (tables and buffers),
+// planned for the participants.
+struct ChainLevel {
+  DecArgs a;
+  int nv, nm, nu, moff;    // items of the three stages; first counter of this level's mid items
+};
+// Synchronisation words (uint64, one per 128 bytes): launch epoch, abort flag,
+// barrier counter, rank tickets; the mid items' arrival counters follow, one
+// per 64 bytes.
+constexpr int kChainEpoch = 0, kChainAbort = 16, kChainBar = 32, kChainTicket = 48;
+constexpr int kChainCnt = 64;                                        // first mid counter (uint64 index)
+constexpr int kChainCntStride = 8;                                   // uint64 per mid counter
+inline size_t chain_sync_bytes(int mid_items) { return ((size_t)kChainCnt + (size_t)kChainCntStride * mid_items) * 8; }
+struct ChainArgs {
+  const ChainLevel* levels;
+  uint64_t* sync;          // chain_sync_bytes, zero before the first launch of a plan
+  int nlev;
+  int pad;
+};
+// Entries the persistent kernel takes (x rows read with 16-byte loads, U units
+// within the fast form) at a token bucket.
+bool decode_chain_takes(const DecEntry& e, int bucket);
+// Workgroups of the persistent kernel's launch at this token bucket (all
+// resident at once: occupancy x compute units), or 0 when the device cannot
+// run it; of these, decode_chain_participants(grid) do the work (those on
+// XCD 0: the grid is a multiple of the 8 XCDs, which take workgroups in
+// turn), and the plans are made for that many work-item slots.
+int decode_chain_grid(int bucket, int device);
+int decode_chain_participants(int grid);
+hipError_t launch_decode_chain(const ChainArgs& c, int bucket, int grid, hipStream_t st);
 // layouts of the decode U stage (built once per linear)
 hipError_t launch_decode_u_layout(const uint32_t* ucan0, const uint32_t* ucan1, int m, const int* W, const UGeom& g,
                                   uint8_t* udec, hipStream_t st);

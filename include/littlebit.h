@@ -215,6 +215,45 @@ lb_status lb_stack_forward(lb_stack S, const void* const* xs, void* const* ys, i
 lb_status lb_stack_forward_ex(lb_stack S, const void* const* xs, void* const* ys, int64_t tokens,
                               lb_dtype io, lb_regime regime, int32_t use_graph, void* stream);
 
+/* Persistent chained decode.  A stack whose entries are chained (levels, see
+ * lb_stack_forward), run in the decode regime with at most 16 tokens and
+ * bf16 y, whose entries all have d_in a multiple of 8 and
+ * ceil(r_1/128) + ceil(r_2/128) <= 8 (<= 6 above 8 tokens; e.g. ranks up to
+ * 512 per path), runs all of its levels in ONE launch when enable = 1 and
+ * the device supports cooperative launches, instead of three launches per
+ * level.  It is meant for a model's linears run in their real order at batch
+ * 1, where each level is a few hundred KB to a few MB of signs and its time
+ * is latency, not bandwidth; measured on MI355X it is slower than the level
+ * launches (about 21 against 17 us per level of a Llama-2-70B-shaped stack),
+ * so the default is enable = 0 (paper notes "LittleBit:
+ * Ultra Low-Bit Quantization via Latent Factorization", section "Key
+ * design": the layer's factorised order, which every form follows).  The
+ * kernel works on the compute units of one XCD, so that the data its stages
+ * hand to each other stays in that XCD's L2 cache; per level a V phase
+ * (partial latent sums; the last V work item of each (entry, path) forms that
+ * pair's z' = z o l) and a U phase, each followed by a barrier of those
+ * workgroups.  Its work items are planned for those workgroups, so its sums
+ * are grouped differently from the level launches of enable = 0 (both within
+ * the same tolerance of the exact result).  enable = 2 runs the persistent
+ * kernel's plans as launches per level, with the same bits as enable = 1 (a
+ * reference for tests); a captured graph (lb_stack_forward_ex with
+ * use_graph = 1) does the same when enable is 1 or 2.  enable = 0 plans and
+ * launches per level as any stack.  Any other value ->
+ * LB_ERR_INVALID_ARGUMENT.  The change applies from the next forward (which
+ * plans again). */
+lb_status lb_stack_set_persistent(lb_stack S, int32_t enable);
+
+/* Whether the stack's current plan runs the persistent chained kernel's plans
+ * (*active, 0 or 1; host only), and whether a launch of that kernel gave up
+ * (*aborted, 0 or 1): a barrier that waits longer than one second (a
+ * workgroup that never arrives), or a participating workgroup that finds
+ * itself on another XCD than the dispatch order puts it on, makes every
+ * participant leave; the outputs of that launch and of every later launch of
+ * the plan are then not written, and the flag stays set until the stack plans
+ * again.  Reading *aborted synchronises the stream of the stack's last
+ * forward.  Either pointer may be NULL. */
+lb_status lb_stack_persistent_status(lb_stack S, int32_t* active, int32_t* aborted);
+
 /* Frees the stack (not its linears).  Does not synchronise.  NULL accepted. */
 lb_status lb_stack_destroy(lb_stack S);
 

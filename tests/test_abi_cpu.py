@@ -112,6 +112,8 @@ def test_argument_validation_before_any_device_work():
     assert L.lb_stack_create(one, 1, C.byref(h)) == lb._binding.INVALID_ARGUMENT
     assert L.lb_linear_destroy(None) == lb._binding.OK
     assert L.lb_stack_destroy(None) == lb._binding.OK
+    assert L.lb_stack_set_persistent(None, 1) == lb._binding.INVALID_ARGUMENT
+    assert L.lb_stack_persistent_status(None, None, None) == lb._binding.INVALID_ARGUMENT
     assert L.lb_pack_signs(None, 1, 1, dummy, None) == lb._binding.INVALID_ARGUMENT
     assert L.lb_unpack_signs(dummy, 0, 1, dummy, None) == lb._binding.INVALID_ARGUMENT
     assert L.lb_packed_words_per_row(0) == 0 and L.lb_packed_words_per_row(32) == 1
