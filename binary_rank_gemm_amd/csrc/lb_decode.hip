@@ -646,8 +646,11 @@ __device__ __attribute__((always_inline)) inline void mid_item(const DecArgs& a,
     const ConvLane LK(((jj % kChunk) / 32) * 16 + sub);
     // the partial sums of both latents over the splits, added in split order;
     // the loads of up to kB splits go out together (the two latents share a
-    // column tile, hence a partial slot and its correction sum)
-    constexpr int kB = 32;
+    // column tile, hence a partial slot and its correction sum).  The mid
+    // launch takes 8 (more registers would lower its occupancy: 32 measured
+    // 7.8 against 4.9 us on the Llama-2-70B stack); the chained kernel, whose
+    // mid steps sit on the critical path one at a time, takes 32
+    constexpr int kB = HL ? 32 : 8;
     const int tile = jj / 16, col = jj % 16, g = tile / it.gtiles, tl = tile - g * it.gtiles;
     const bool in[2] = {jj < r, jj + 1 < r};
     const LB_GLOBAL float* sp = part + (int64_t)(it.slot0 + g * it.nsplit) * SF;
