@@ -217,7 +217,10 @@ __device__ inline float convert_pair(const ConvLane& L, float t0, float t1, int 
   using U16 = typename std::conditional<std::is_same<Ptr, uint8_t*>::value, uint16_t, LB_GLOBAL uint16_t>::type;
   *reinterpret_cast<U16*>(ab + img_off(mhi, L.gdst, L.edst)) = (uint16_t)hi;
   *reinterpret_cast<U16*>(ab + img_off(mlo, L.gdst, L.edst)) = (uint16_t)lo;
-  if (L.sub == 0) {
+  if (std::is_same<Ptr, uint8_t*>::value || L.sub == 0) {
+    // into LDS every lane of the row writes its block's scale bytes (the same
+    // value to the same byte): no branch, so the conversions of successive
+    // tokens stay in one block that the compiler can interleave
     ab[2048 + mhi * 4 + L.kb] = (uint8_t)(E + 127);
     ab[2048 + mlo * 4 + L.kb] = (uint8_t)(E + 127 - 4);
   }
@@ -437,7 +440,12 @@ __device__ __attribute__((always_inline)) inline void v_stream(const DecArgs& a,
 #pragma unroll
           for (int tt = 0; tt < 8; ++tt) {
             const int t = tb * 8 + tt;
-            if (t < TM && t < T) {
+            // up to 8 tokens every token slot of the bucket: the ring holds
+            // the last token's row again for slots past T, whose MFMA rows are
+            // never read, and without a test per token the conversions form
+            // one block the compiler interleaves (at 16 tokens that takes more
+            // registers than two workgroups per CU leave: it keeps the test)
+            if (t < TM && (TM <= 8 || t < T)) {
               const float x0 = bf16f((uint16_t)(xpair[g][t] & 0xffff)), x1 = bf16f((uint16_t)(xpair[g][t] >> 16));
               cpart[t] += convert_pair(L, v0 ? x0 * g0 : 0.f, v1 ? x1 * g1 : 0.f, tt, abuf + tb * kABytes);
             }
