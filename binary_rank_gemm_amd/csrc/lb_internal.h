@@ -135,9 +135,17 @@ __host__ __device__ inline constexpr int decode_v_tiles(int bucket) { return 20;
 __host__ __device__ inline constexpr int decode_slot_floats(int bucket) {
   return decode_v_tiles(bucket) * 16 * bucket + 16;
 }
-// Most quads per wave of a U item at a token bucket (the wave stages all of
-// its outputs in LDS: 2 KB, or 8 KB at 16 tokens where fewer items fit a CU).
-__host__ __device__ inline constexpr int decode_u_qw_max(int bucket) { return bucket >= 16 ? 4 : 16 / bucket; }
+// Most quads per wave of a U item at a token bucket.  The wave stages all of
+// its outputs in LDS: 3 KB from 2 to 8 tokens, so that three workgroups of
+// ring and staging (52 KB each) still fit a CU's 160 KB (fewer quads per item
+// would make the A-operand prologue as large as the stream: at 8 tokens and 2
+// quads a wave of a gate projection loaded 12 KB of operands for 11 KB of
+// signs; 3 quads took the Llama-2-70B stack from 280 to 273 us, 4 tokens 225
+// to 221); 2 KB at one token, where the items are not limited by it and the
+// larger allocation measured 1 % slower; 8 KB at 16 tokens, where two fit a CU.
+__host__ __device__ inline constexpr int decode_u_qw_max(int bucket) {
+  return bucket >= 16 ? 4 : bucket == 1 ? 16 : 24 / bucket;
+}
 // Sizes the planner aims at per V and U work item (bytes of sign words).
 // From 4 tokens on a V item's partial slot is large (20 KB at 16 tokens), so
 // fewer, larger items pay: measured on the Llama-2-70B stack, 384 KB items
