@@ -656,8 +656,11 @@ __device__ __attribute__((always_inline)) inline void mid_item(const DecArgs& a,
   const LB_GLOBAL float* part = gp(a.part);
   const int ufirst = p ? E.ug.nu0 : 0;
   const int nblk = 4 * ((r + kChunk - 1) / kChunk);
-  const int tid = threadIdx.x, row = tid >> 4, sub = tid & 15;
-  for (int u = row; u < T * nblk; u += 16) {
+  // 16-lane rows of the workgroup (16 in the chained kernel's 256 threads;
+  // the mid launch has 64 from 4 tokens: with one memory round trip per
+  // position a row takes, more rows mean fewer round trips in a row)
+  const int tid = threadIdx.x, row = tid >> 4, sub = tid & 15, nrows = (int)(blockDim.x >> 4);
+  for (int u = row; u < T * nblk; u += nrows) {
     const int t = u / nblk, blk = u % nblk, tb = t / 8, tt = t % 8;
     const int jj = 32 * blk + 2 * sub;             // latents jj, jj + 1
     const ConvLane LK(((jj % kChunk) / 32) * 16 + sub);
@@ -706,8 +709,13 @@ __device__ __attribute__((always_inline)) inline void mid_item(const DecArgs& a,
   }
 }
 
+// Threads of a mid workgroup: 256 up to 2 tokens (a path's positions fit
+// 16 rows), 1024 from 4 tokens.
 template <int TM>
-__global__ void __launch_bounds__(kThreads) k_decode_mid(DecArgs a) {
+constexpr int mid_threads() { return TM >= 4 ? 1024 : kThreads; }
+
+template <int TM>
+__global__ void __launch_bounds__(mid_threads<TM>()) k_decode_mid(DecArgs a) {
   __shared__ float cblk[kMidLdsFloats];
   mid_item<TM, false>(a, cld(cp(a.mitems) + blockIdx.x), cblk);
 }
@@ -1213,11 +1221,11 @@ hipError_t launch_decode_v(const DecArgs& a, int nitems, hipStream_t st) {
 hipError_t launch_decode_mid(const DecArgs& a, int nitems, hipStream_t st) {
   if (nitems <= 0) return hipSuccess;
   switch (a.bucket) {
-    case 1: hipLaunchKernelGGL(k_decode_mid<1>, dim3(nitems), dim3(kThreads), 0, st, a); break;
-    case 2: hipLaunchKernelGGL(k_decode_mid<2>, dim3(nitems), dim3(kThreads), 0, st, a); break;
-    case 4: hipLaunchKernelGGL(k_decode_mid<4>, dim3(nitems), dim3(kThreads), 0, st, a); break;
-    case 8: hipLaunchKernelGGL(k_decode_mid<8>, dim3(nitems), dim3(kThreads), 0, st, a); break;
-    default: hipLaunchKernelGGL(k_decode_mid<16>, dim3(nitems), dim3(kThreads), 0, st, a); break;
+    case 1: hipLaunchKernelGGL(k_decode_mid<1>, dim3(nitems), dim3(mid_threads<1>()), 0, st, a); break;
+    case 2: hipLaunchKernelGGL(k_decode_mid<2>, dim3(nitems), dim3(mid_threads<2>()), 0, st, a); break;
+    case 4: hipLaunchKernelGGL(k_decode_mid<4>, dim3(nitems), dim3(mid_threads<4>()), 0, st, a); break;
+    case 8: hipLaunchKernelGGL(k_decode_mid<8>, dim3(nitems), dim3(mid_threads<8>()), 0, st, a); break;
+    default: hipLaunchKernelGGL(k_decode_mid<16>, dim3(nitems), dim3(mid_threads<16>()), 0, st, a); break;
   }
   return hipGetLastError();
 }
