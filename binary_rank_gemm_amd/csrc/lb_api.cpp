@@ -95,8 +95,8 @@ struct DecodePlan {
   DecEntry* entries_d = nullptr;
   VItem* vitems_d = nullptr;      // V items, largest first
   MItem* mitems_d = nullptr;      // mid items, one per (entry, path)
-  UItem* uitems_d = nullptr;      // U items, largest first
-  int nv = 0, nm = 0, nu = 0;
+  UItem* uitems_d = nullptr;      // U items, largest first; the last nuw of them for the wide U launch
+  int nv = 0, nm = 0, nu = 0, nuw = 0;
   Scratch part;                   // V-stage partial slots
   Scratch work;                   // U-stage A operands and correction sums of every entry
   void release() {
@@ -136,7 +136,7 @@ struct lb_linear_s {
   // bucket, built at create against the fixed per-device scratch
   struct NoAllocDecode {
     bool ok = false;                 // the bucket's scratch fits kNoAllocScratchBytes
-    int nv = 0, nm = 0, nu = 0;
+    int nv = 0, nm = 0, nu = 0, nuw = 0;
     size_t entries_off = 0, v_off = 0, m_off = 0, u_off = 0;   // bytes into na_tables
   };
   NoAllocDecode na[5];               // token buckets 1, 2, 4, 8, 16
@@ -267,7 +267,8 @@ struct DecodeHostPlan {
   std::vector<DecEntry> entries;
   std::vector<VItem> vitems;        // largest first
   std::vector<MItem> mitems;
-  std::vector<UItem> uitems;        // largest first
+  std::vector<UItem> uitems;        // largest first, then the wide U launch's items largest first
+  int nuw = 0;                      // items of the wide U launch (decode_u_wide), at the end
   std::vector<size_t> img_off, cv_off;
   size_t part_bytes = 0;            // V-stage partial slots
   size_t work_bytes = 0;            // U-stage operands and correction sums
@@ -280,7 +281,7 @@ void plan_decode_host(DecodeHostPlan& H, const lb_linear* L, int count, int T, c
   H.img_off.assign(count, 0);
   H.cv_off.assign(count, 0);
   std::vector<std::pair<double, VItem>> vl;
-  std::vector<std::pair<double, UItem>> ul;
+  std::vector<std::pair<double, UItem>> ul, ulw;
   H.mitems.clear();
   size_t work_bytes = 0;
   int slots = 0;
@@ -348,13 +349,17 @@ void plan_decode_host(DecodeHostPlan& H, const lb_linear* L, int count, int T, c
     for (int q0 = 0; q0 < E.ug.nq; q0 += kWavesPerGroup * qw) {
       const int nq = std::min(kWavesPerGroup * qw, E.ug.nq - q0);
       // a short run (small entries, the last run) is spread over all four waves
-      ul.push_back({nq * qbytes, UItem{e, q0, nq, (nq + kWavesPerGroup - 1) / kWavesPerGroup}});
+      (decode_u_wide(bucket, E.ug.nu) ? ulw : ul)
+          .push_back({nq * qbytes, UItem{e, q0, nq, (nq + kWavesPerGroup - 1) / kWavesPerGroup}});
     }
   }
   H.work_bytes = work_bytes + kDmaPad;
   H.part_bytes = std::max<size_t>((size_t)slots * decode_slot_floats(bucket) * sizeof(float), 256);
   H.vitems = largest_first(vl);
   H.uitems = largest_first(ul);
+  const std::vector<UItem> wide = largest_first(ulw);
+  H.uitems.insert(H.uitems.end(), wide.begin(), wide.end());
+  H.nuw = (int)wide.size();
 }
 
 // Builds (or reuses) the decode plan for `count` linears at `T` tokens per
@@ -383,6 +388,7 @@ lb_status build_decode_plan(DecodePlan& P, const lb_linear* L, int count, int T,
   P.nv = (int)H.vitems.size();
   P.nm = (int)H.mitems.size();
   P.nu = (int)H.uitems.size();
+  P.nuw = H.nuw;
   P.T = T;
   P.count = count;
   return LB_OK;
@@ -394,7 +400,7 @@ struct DecodeTables {
   const VItem* vitems;
   const MItem* mitems;
   const UItem* uitems;
-  int nv, nm, nu;
+  int nv, nm, nu, nuw;     // nuw: the last U items, for the wide U launch
   float* part;
 };
 
@@ -421,7 +427,11 @@ hipError_t launch_decode_slices(const DecodeTables& D, const void* const* xs_d, 
     a.part = D.part;
     hipError_t e = launch_decode_v(a, D.nv, st);
     if (e == hipSuccess) e = launch_decode_mid(a, D.nm, st);
-    if (e == hipSuccess) e = launch_decode_u(a, D.nu, st);
+    if (e == hipSuccess) e = launch_decode_u(a, D.nu - D.nuw, st);
+    if (e == hipSuccess && D.nuw > 0) {
+      a.uitems = D.uitems + (D.nu - D.nuw);
+      e = launch_decode_u_wide(a, D.nuw, st);
+    }
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -438,7 +448,7 @@ lb_status run_decode(DecodePlan& P, const lb_linear* L, int count, const void* c
   if (P.T != Tplan && P.T != -1) HIP_TRY(hipStreamSynchronize(st));  // the plan is rewritten below
   lb_status s = build_decode_plan(P, L, count, Tplan, img);
   if (s != LB_OK) return s;
-  const DecodeTables D{P.entries_d, P.vitems_d, P.mitems_d, P.uitems_d, P.nv, P.nm, P.nu,
+  const DecodeTables D{P.entries_d, P.vitems_d, P.mitems_d, P.uitems_d, P.nv, P.nm, P.nu, P.nuw,
                        reinterpret_cast<float*>(P.part.ptr)};
   HIP_TRY(launch_decode_slices(D, xs_d, ys_d, x0, y0, tokens, yf32, st));
   return LB_OK;
@@ -483,6 +493,7 @@ hipError_t build_noalloc_tables(lb_linear L, hipStream_t st) {
     N.nv = (int)H.vitems.size();
     N.nm = (int)H.mitems.size();
     N.nu = (int)H.uitems.size();
+    N.nuw = H.nuw;
   }
   if (img.empty()) return hipSuccess;
   img.resize(align256(img.size()));
@@ -529,7 +540,7 @@ inline int y_is_fp32(lb_dtype io) { return io == LB_BF16 ? 0 : 1; }
 // for the three launches.
 double decode_cost_us(const lb_linear* L, int count, int64_t T) {
   const int bucket = decode_bucket((int)std::min<int64_t>(T, kDecodeMaxTokens));
-  const int nmax = bucket > 8 ? 6 : 8;   // units a U wave keeps in registers (UShape::NMAX)
+  const int nmax = decode_u_fast_units(bucket);   // units a U wave keeps in registers
   double us = 0;
   for (int e = 0; e < count; ++e) {
     double vb = 0, ub = 0;
@@ -896,7 +907,7 @@ lb_status lb_linear_forward_noalloc(lb_linear L, const void* x, void* y, int64_t
   const DecodeTables D{reinterpret_cast<const DecEntry*>(L->na_tables + N.entries_off),
                        reinterpret_cast<const VItem*>(L->na_tables + N.v_off),
                        reinterpret_cast<const MItem*>(L->na_tables + N.m_off),
-                       reinterpret_cast<const UItem*>(L->na_tables + N.u_off), N.nv, N.nm, N.nu,
+                       reinterpret_cast<const UItem*>(L->na_tables + N.u_off), N.nv, N.nm, N.nu, N.nuw,
                        reinterpret_cast<float*>(L->na_scratch)};
   HIP_TRY(launch_decode_slices(D, nullptr, nullptr, x, y, tokens, y_is_fp32(io), st));
   return LB_OK;

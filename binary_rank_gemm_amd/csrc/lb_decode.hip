@@ -999,7 +999,7 @@ __device__ __attribute__((always_inline)) inline void u_plain(const DecArgs& a, 
 // persistent chained kernel's form: A operands and correction sums read with
 // hand-over loads, and only entries whose units fit the fast form (the plain
 // form is left out).
-template <int TM, bool YF, bool HL>
+template <int TM, bool YF, bool HL, int NMX = UShape<TM>::NMAX>
 __device__ __attribute__((always_inline)) inline void u_item(const DecArgs& a, const UItem& it, uint8_t* lds) {
   using S = UShape<TM>;
   constexpr int TB = S::TB;
@@ -1030,12 +1030,12 @@ __device__ __attribute__((always_inline)) inline void u_item(const DecArgs& a, c
   uint8_t* ring = lds + wave * kRingBytes;
   uint8_t* stg = lds + kWaves * kRingBytes + wave * S::STG;
   const int nu = Eg.ug.nu;
-  static_for<S::NMAX>([&](auto I) __attribute__((always_inline)) {
+  static_for<NMX>([&](auto I) __attribute__((always_inline)) {
     constexpr int k = decltype(I)::value + 1;
     if (nu == k) u_stream<TM, k, HL>(a, Eg, C, qa, qb, ring, stg);
   });
   if constexpr (!HL) {
-    if (nu > S::NMAX) u_plain<TM>(a, Eg, C, qa, qb);
+    if (nu > NMX) u_plain<TM>(a, Eg, C, qa, qb);
   }
 }
 
@@ -1043,6 +1043,16 @@ template <int TM, bool YF>
 __global__ void __launch_bounds__(kThreads, TM >= 16 ? 2 : 3) k_decode_u(DecArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   u_item<TM, YF, false>(a, cld(cp(a.uitems) + blockIdx.x), lds);
+}
+
+// The second U launch of a 16-token decode: entries of 7 or 8 units, in the
+// fast form with one workgroup per CU (their operands need the registers two
+// workgroups would share); four waves of nine 1 KB loads in flight per CU still
+// keep the stream going.
+template <int TM, bool YF>
+__global__ void __launch_bounds__(kThreads, 1) k_decode_u_wide(DecArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  u_item<TM, YF, false, kDecodeWideUnits>(a, cld(cp(a.uitems) + blockIdx.x), lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -1241,6 +1251,14 @@ static void launch_u(const DecArgs& a, int nitems, hipStream_t st) {
   }
 }
 
+hipError_t launch_decode_u_wide(const DecArgs& a, int nitems, hipStream_t st) {
+  if (nitems <= 0) return hipSuccess;
+  if (a.bucket != 16) return hipErrorInvalidValue;
+  if (a.yf32) hipLaunchKernelGGL((k_decode_u_wide<16, true>), dim3(nitems), dim3(kThreads), UShape<16>::lds, st, a);
+  else hipLaunchKernelGGL((k_decode_u_wide<16, false>), dim3(nitems), dim3(kThreads), UShape<16>::lds, st, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode_u(const DecArgs& a, int nitems, hipStream_t st) {
   if (nitems <= 0) return hipSuccess;
   if (a.yf32) launch_u<true>(a, nitems, st);
@@ -1252,8 +1270,11 @@ hipError_t launch_decode_u(const DecArgs& a, int nitems, hipStream_t st) {
 
 namespace lb {
 
+static_assert(UShape<16>::NMAX == decode_u_fast_units(16) && UShape<8>::NMAX == decode_u_fast_units(8),
+              "the planner's count of fast-form units");
+
 bool decode_chain_takes(const DecEntry& e, int bucket) {
-  return e.xdirect != 0 && e.ug.nu <= (bucket > 8 ? UShape<16>::NMAX : UShape<8>::NMAX);
+  return e.xdirect != 0 && e.ug.nu <= decode_u_fast_units(bucket);
 }
 
 int decode_chain_grid(int bucket, int device) {

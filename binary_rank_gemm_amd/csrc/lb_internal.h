@@ -152,6 +152,16 @@ __host__ __device__ inline constexpr int decode_u_qw_max(int bucket) {
 // take 2-4 % off the launches of 4, 8 and 16 tokens and add 2 % at one token.
 __host__ __device__ inline constexpr int decode_v_item_bytes(int bucket) { return bucket >= 4 ? 384 * 1024 : 192 * 1024; }
 constexpr int kDecodeUItemBytes = 192 * 1024;
+// U units (128 latents of both paths together) a U wave holds in registers in
+// the fast form: 8 up to 8 tokens, 6 at 16 tokens (two workgroups per CU).
+// At 16 tokens, entries of 7 or 8 units run in a second U launch whose
+// workgroups hold 8 (one workgroup per CU: the registers of 8 units' operands
+// for two token blocks); more units take the plain form.
+__host__ __device__ inline constexpr int decode_u_fast_units(int bucket) { return bucket > 8 ? 6 : 8; }
+constexpr int kDecodeWideUnits = 8;
+__host__ __device__ inline constexpr bool decode_u_wide(int bucket, int nu) {
+  return bucket > 8 && nu > decode_u_fast_units(bucket) && nu <= kDecodeWideUnits;
+}
 
 // ---------------------------------------------------------------------------
 // kernel launchers (defined in the .hip files)
@@ -200,6 +210,8 @@ hipError_t launch_exact(const PathDev* p, int np, int m, int n, const void* x, v
 hipError_t launch_decode_v(const DecArgs& a, int nitems, hipStream_t st);
 hipError_t launch_decode_mid(const DecArgs& a, int nitems, hipStream_t st);
 hipError_t launch_decode_u(const DecArgs& a, int nitems, hipStream_t st);
+// the second U launch of a 16-token decode: entries with decode_u_wide
+hipError_t launch_decode_u_wide(const DecArgs& a, int nitems, hipStream_t st);
 
 // Persistent chained decode: one launch runs the levels of a chained stack in
 // order, on the compute units of one XCD (hand-overs through its L2), each
