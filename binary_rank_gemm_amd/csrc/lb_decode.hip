@@ -319,7 +319,13 @@ struct VShape {
   static constexpr int CT = decode_v_tiles(TM);   // most column tiles of an item
   static constexpr int SMAX = (CT + 3) / 4;       // sign steps per chunk (4 tiles each)
   static constexpr int XS = (TM + 4) / 4;         // steps per chunk holding g and TM rows of x (256 B each)
-  static constexpr size_t lds = (size_t)kWaves * kRingBytes + (size_t)kWaves * TB * kABytes;
+  // ring slots per wave: 7 at one token, where four workgroups then fit a CU
+  // (36 KB of LDS and at most 128 VGPRs each), else kRing
+  static constexpr int RING = TM == 1 ? 7 : kRing;
+  static constexpr int RINGB = RING * 1024;
+  static constexpr int WPC = TM == 1 ? 4 : TM >= 16 ? 2 : 3;   // workgroups per CU
+  static constexpr size_t lds = (size_t)kWaves * RINGB + (size_t)kWaves * TB * kABytes;
+  static_assert(WPC * lds <= 160 * 1024, "workgroups per CU fit its LDS");
 };
 
 // Partial sums of one wave's chunks: acc (z_p before the correction term) and
@@ -389,14 +395,15 @@ __device__ __attribute__((always_inline)) inline void v_stream(const DecArgs& a,
     if (last_signs) dma16_once<TM>(last, ring + slot * 1024);
     else dma16<kHandAux<HL>>(last, ring + slot * 1024);
   };
+  constexpr int R = S::RING;
 #pragma unroll
-  for (int k = 0; k < kRing - 1; ++k) issue(k);
+  for (int k = 0; k < R - 1; ++k) issue(k);
   int s = 0;
   auto next_step = [&]() __attribute__((always_inline)) {
     lds_wait();                                // the slot reloaded next was read last step
-    issue((s + kRing - 1) % kRing);
-    vm_wait<kRing - 1>();
-    const uint8_t* slot = ring + (s % kRing) * 1024;
+    issue((s + R - 1) % R);
+    vm_wait<R - 1>();
+    const uint8_t* slot = ring + (s % R) * 1024;
     ++s;
     return slot;
   };
@@ -547,8 +554,8 @@ __device__ __attribute__((always_inline)) inline void v_item(const DecArgs& a, c
   const LB_GLOBAL uint8_t* gdec = reinterpret_cast<const LB_GLOBAL uint8_t*>(gp(Eg.gdec[p]));
   const void* xv = a.xs ? cp(a.xs)[it.entry] : a.x0;
   const LB_GLOBAL uint8_t* xb = reinterpret_cast<const LB_GLOBAL uint8_t*>(gp(xv)) + (int64_t)a.t0 * n * 2;
-  uint8_t* ring = lds + wave * kRingBytes;
-  uint8_t* abuf = lds + kWaves * kRingBytes + wave * TB * kABytes;
+  uint8_t* ring = lds + wave * S::RINGB;
+  uint8_t* abuf = lds + kWaves * S::RINGB + wave * TB * kABytes;
   // this wave's chunks: a contiguous quarter of the item's, the quarters as
   // even as whole groups of chunks allow (groups of two at one token)
   constexpr int GV = TM == 1 ? 2 : 1;
@@ -596,7 +603,7 @@ __device__ __attribute__((always_inline)) inline void v_item(const DecArgs& a, c
     }
   };
   __syncthreads();
-  if constexpr (kWaves * (CT * TM * 16 + TM) * 4 <= kRingBytes * kWaves) {
+  if constexpr (kWaves * (CT * TM * 16 + TM) * 4 <= S::RINGB * kWaves) {
     // each wave writes its own copy, then every thread adds the four in wave order
     float* red = reinterpret_cast<float*>(lds);    // [wave][tile][token][16]
     float* cred = red + kWaves * CT * TM * 16;     // [wave][token]
@@ -630,7 +637,7 @@ __device__ __attribute__((always_inline)) inline void v_item(const DecArgs& a, c
 }
 
 template <int TM>
-__global__ void __launch_bounds__(kThreads, TM >= 16 ? 2 : 3) k_decode_v(DecArgs a) {
+__global__ void __launch_bounds__(kThreads, VShape<TM>::WPC) k_decode_v(DecArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   v_item<TM, false>(a, cld(cp(a.vitems) + blockIdx.x), lds);
 }
