@@ -150,7 +150,11 @@ __host__ __device__ inline constexpr int decode_u_qw_max(int bucket) {
 // From 4 tokens on a V item's partial slot is large (20 KB at 16 tokens), so
 // fewer, larger items pay: measured on the Llama-2-70B stack, 384 KB items
 // take 2-4 % off the launches of 4, 8 and 16 tokens and add 2 % at one token.
-__host__ __device__ inline constexpr int decode_v_item_bytes(int bucket) { return bucket >= 4 ? 384 * 1024 : 192 * 1024; }
+// At one token, where four V workgroups fit a CU, 144 KB measured 0.5 % faster
+// than 192 (96, 128 and 256 KB slower).
+__host__ __device__ inline constexpr int decode_v_item_bytes(int bucket) {
+  return bucket >= 4 ? 384 * 1024 : bucket == 1 ? 144 * 1024 : 192 * 1024;
+}
 constexpr int kDecodeUItemBytes = 192 * 1024;
 // U units (128 latents of both paths together) a U wave holds in registers in
 // the fast form: 8 up to 8 tokens, 6 at 16 tokens (two workgroups per CU).
