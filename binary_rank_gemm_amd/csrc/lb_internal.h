@@ -155,7 +155,10 @@ __host__ __device__ inline constexpr int decode_u_qw_max(int bucket) {
 __host__ __device__ inline constexpr int decode_v_item_bytes(int bucket) {
   return bucket >= 4 ? 384 * 1024 : bucket == 1 ? 144 * 1024 : 192 * 1024;
 }
-constexpr int kDecodeUItemBytes = 192 * 1024;
+// U items of 288 KB (capped from 4 tokens by the quads a wave can stage):
+// with four V workgroups per CU at one token, 288 KB measured 1-2 % faster than
+// 192 at one and two tokens (144 and 384 KB slower).
+constexpr int kDecodeUItemBytes = 288 * 1024;
 // U units (128 latents of both paths together) a U wave holds in registers in
 // the fast form: 8 up to 8 tokens, 6 at 16 tokens (two workgroups per CU).
 // At 16 tokens, entries of 7 or 8 units run in a second U launch whose
