@@ -6,6 +6,7 @@
 #include <array>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <string>
@@ -202,6 +203,7 @@ struct lb_stack_s {
   int chain_enable = 0;                     // lb_stack_set_persistent's mode (0: level launches)
   int chain_active = 0;                     // the current plans run it
   int chain_grid = 0, chain_bucket = 0, chain_nlev = 0;
+  int chain_stall = 0;                      // LITTLEBIT_CHAIN_STALL at planning (abort-path tests)
   ChainLevel* chain_levels_d = nullptr;     // per level: its decode tables and buffers
   std::vector<DecodePlan> chain_plans;      // per level, planned for the kernel's participants
   Scratch chain_sync;                       // epoch, abort flag, barrier and mid counters
@@ -211,7 +213,7 @@ struct lb_stack_s {
     for (DecodePlan& P : chain_plans) P.release();
     chain_plans.clear();
     chain_active = 0;
-    chain_grid = chain_bucket = chain_nlev = 0;
+    chain_grid = chain_bucket = chain_nlev = chain_stall = 0;
   }
 };
 
@@ -997,7 +999,8 @@ lb_status stack_launch(lb_stack S, lb_regime rg, int64_t tokens, lb_dtype io, hi
   const int count = (int)S->linears.size();
   if (rg == LB_REGIME_DECODE && S->chain_active) {
     if (S->chain_enable == 1 && !capture) {
-      const ChainArgs c{S->chain_levels_d, reinterpret_cast<uint64_t*>(S->chain_sync.ptr), S->chain_nlev, 0};
+      const ChainArgs c{S->chain_levels_d, reinterpret_cast<uint64_t*>(S->chain_sync.ptr), S->chain_nlev,
+                        S->chain_stall};
       HIP_TRY(launch_decode_chain(c, S->chain_bucket, S->chain_grid, st));
       return LB_OK;
     }
@@ -1145,6 +1148,8 @@ lb_status chain_prepare(lb_stack S, int64_t tokens, lb_dtype io, hipStream_t st)
   S->chain_grid = grid;
   S->chain_bucket = bucket;
   S->chain_nlev = (int)lv.size();
+  const char* stall = std::getenv("LITTLEBIT_CHAIN_STALL");
+  S->chain_stall = stall && std::strcmp(stall, "1") == 0 ? 1 : 0;
   S->chain_active = 1;
   return LB_OK;
 }

@@ -1130,14 +1130,15 @@ __device__ inline bool chain_wait(uint64_t* sync, uint64_t* w, uint64_t target) 
 // Barrier number `target` of the P participants (counted over all launches
 // of the plan): every wave first waits for its own stores (in the L2 once
 // complete), then thread 0 adds to the barrier counter and waits for
-// P x target.  Returns false when the launch was aborted (every participant
-// then leaves).
-__device__ inline bool chain_barrier(uint64_t* sync, uint64_t target, uint64_t P, int* flag) {
+// P x target (+ extra, which only a test of the abort path sets: no
+// workgroup ever makes that arrival, so the wait times out).  Returns false
+// when the launch was aborted (every participant then leaves).
+__device__ inline bool chain_barrier(uint64_t* sync, uint64_t target, uint64_t P, uint64_t extra, int* flag) {
   vm_wait<0>();
   __syncthreads();
   if (threadIdx.x == 0) {
     dev_add(sync + kChainBar, 1);
-    *flag = chain_wait(sync, sync + kChainBar, target * P);
+    *flag = chain_wait(sync, sync + kChainBar, target * P + extra);
   }
   __syncthreads();
   return *flag != 0;
@@ -1186,12 +1187,12 @@ __global__ void __launch_bounds__(kThreads, TM >= 16 ? 1 : 2) k_decode_chain(Cha
       if (flag) mid_item<TM, true>(L.a, cld(cp(L.a.mitems) + it.mid), reinterpret_cast<float*>(lds));
       __syncthreads();                             // LDS is the next item's
     }
-    if (!chain_barrier(sync, ++bar, P, &flag)) return;
+    if (!chain_barrier(sync, ++bar, P, lev == 0 ? (uint64_t)c.stall : 0, &flag)) return;
     for (int i = rank; i < L.nu; i += (int)P) {
       u_item<TM, false, true>(L.a, cld(cp(L.a.uitems) + i), lds);
       __syncthreads();
     }
-    if (!chain_barrier(sync, ++bar, P, &flag)) return;
+    if (!chain_barrier(sync, ++bar, P, 0, &flag)) return;
   }
   if (rank == 0 && tid == 0) __hip_atomic_store(sync + kChainEpoch, epoch + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

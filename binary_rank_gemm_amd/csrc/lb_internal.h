@@ -241,7 +241,7 @@ struct ChainArgs {
   const ChainLevel* levels;
   uint64_t* sync;          // chain_sync_bytes, zero before the first launch of a plan
   int nlev;
-  int pad;
+  int stall;               // 1: the first barrier waits for one arrival more (abort-path tests)
 };
 // Entries the persistent kernel takes (x rows read with 16-byte loads, U units
 // within the fast form) at a token bucket.

@@ -248,10 +248,15 @@ lb_status lb_stack_set_persistent(lb_stack S, int32_t enable);
  * (*aborted, 0 or 1): a barrier that waits longer than one second (a
  * workgroup that never arrives), or a participating workgroup that finds
  * itself on another XCD than the dispatch order puts it on, makes every
- * participant leave; the outputs of that launch and of every later launch of
- * the plan are then not written, and the flag stays set until the stack plans
+ * participant leave; the outputs of that launch are then not written in
+ * full, those of every later launch of the plan not at all (its workgroups
+ * leave at once), and the flag stays set until the stack plans
  * again.  Reading *aborted synchronises the stream of the stack's last
- * forward.  Either pointer may be NULL. */
+ * forward.  Either pointer may be NULL.  To test this path, the environment
+ * variable LITTLEBIT_CHAIN_STALL=1 at planning makes the first barrier of
+ * every launch wait for one arrival more than take part, so each launch times
+ * out after one second and aborts; plan again without it (set enable to 0,
+ * then back) for normal launches. */
 lb_status lb_stack_persistent_status(lb_stack S, int32_t* active, int32_t* aborted);
 
 /* Frees the stack (not its linears).  Does not synchronise.  NULL accepted. */

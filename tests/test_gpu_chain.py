@@ -130,6 +130,49 @@ def test_persistent_chain_falls_back_when_an_entry_does_not_fit():
     S.close()
 
 
+def test_persistent_chain_abort_path(monkeypatch):
+    """Failure handling of the persistent launch, forced from the host: with
+    LITTLEBIT_CHAIN_STALL=1 at planning, the first barrier of every launch
+    waits for one arrival more than take part, so its bounded wait times out
+    (one second) and every participant leaves.  The stack then reports the
+    launch aborted, no output is written (the U items of the first level come
+    after that barrier), and a second launch of the plan leaves at once.
+    Planned again without the variable, the kernel runs normally: the bits of
+    its plans run as level launches."""
+    shapes = LAYER                                   # one layer: 4 levels
+    T = 1
+    paths = [synth.layer_tensors(43, i, 0, m, n, r) for i, (m, n, r) in enumerate(shapes)]
+    lins = [lb.Linear.from_numpy(m, n, p) for (m, n, _), p in zip(shapes, paths)]
+    x0 = x_tensor(synth.activations((43, 99, T), T, D))
+    ys = [torch.empty((T, m), dtype=torch.bfloat16, device="cuda") for m, _, _ in shapes]
+    xs = model_order_inputs(x0, ys, 1)
+    S1, S2 = stacks(lins)
+    kw = dict(regime=lb.REGIME_DECODE, use_graph=False)
+    monkeypatch.setenv("LITTLEBIT_CHAIN_STALL", "1")
+    log("persistent chain abort path: two stalled launches")
+    for call in range(2):
+        for y in ys:
+            y.fill_(7.0)
+        S1.forward(xs, ys, **kw)
+        torch.cuda.synchronize()
+        st = S1.persistent_status()
+        assert st["active"] and st["aborted"], (call, st)
+        for i, y in enumerate(ys):
+            assert bool((y == 7.0).all()), f"call {call}: entry {i} was written by an aborted launch"
+    monkeypatch.delenv("LITTLEBIT_CHAIN_STALL")
+    S1.set_persistent(0)
+    S1.set_persistent(1)                             # plans again at the next forward
+    ref = run(S2, xs, ys, **kw)
+    got = run(S1, xs, ys, **kw)
+    st = S1.persistent_status()
+    assert st["active"] and not st["aborted"], st
+    same_bits(ref, got, "after planning again")
+    for i, (m, n, _) in enumerate(shapes):
+        assert_bf16_close(to_f64(ys[i]), oracle.forward(to_f64(xs[i]), paths[i], m, n), f"link {i}")
+    S1.close()
+    S2.close()
+
+
 def ranks70(s):
     r = oracle.rank_for_bpw(s.m, s.n, Fraction(1, 10), s.rank_mult)
     return [r, r]
