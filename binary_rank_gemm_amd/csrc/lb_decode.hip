@@ -169,6 +169,19 @@ __device__ inline v8i expand_signs(uint32_t w, uint32_t one) {
 // two 16-byte reads of a wave each cover one contiguous 1 KB (no bank
 // conflicts); the e8m0 scales follow at byte 2048.
 __host__ __device__ inline int img_off(int row, int g, int e) { return (e >> 4) * 1024 + (row * 4 + g) * 16 + (e & 15); }
+// An image of AR rows (AR = 2: the hi and lo rows of one token): row r is
+// stored at r mod AR, so a lane of a row past AR reads a stored row (MFMA rows
+// are independent; those rows of the result are never read).  AR = 16 is the
+// full image above, with its scale bytes at 2048.
+template <int AR>
+__host__ __device__ inline int img_off_r(int row, int g, int e) {
+  return (e >> 4) * (AR * 64) + ((row & (AR - 1)) * 4 + g) * 16 + (e & 15);
+}
+template <int AR>
+__host__ __device__ inline constexpr int img_scales(int row, int g) { return AR * 128 + (row & (AR - 1)) * 4 + g; }
+template <int AR>
+__host__ __device__ inline constexpr int img_bytes() { return (AR * 132 + 15) / 16 * 16; }
+static_assert(img_bytes<16>() == kABytes, "the full image is kABytes");
 
 __device__ inline v4f mfma(const v8i& a, const v8i& b, v4f c, int scale_a) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, scale_a, 0, 127);
@@ -198,7 +211,7 @@ typedef float float2v __attribute__((ext_vector_type(2)));
 // Converts this lane's two values (already multiplied by the class factor) of
 // token slot tt into the A image `ab` at the lane's K position; the 16 lanes of
 // a DPP row hold one 32-element block.  Returns the lane's contribution to C.
-template <class Ptr>
+template <int AR = 16, class Ptr>
 __device__ inline float convert_pair(const ConvLane& L, float t0, float t1, int tt, Ptr ab) {
   float mx = row16_max_nonneg(fmaxf(fabsf(t0), fabsf(t1)));
   int ex;
@@ -215,14 +228,14 @@ __device__ inline float convert_pair(const ConvLane& L, float t0, float t1, int 
   const float2v Lq = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(lo, sl, false);
   const int mhi = 2 * tt, mlo = 2 * tt + 1;
   using U16 = typename std::conditional<std::is_same<Ptr, uint8_t*>::value, uint16_t, LB_GLOBAL uint16_t>::type;
-  *reinterpret_cast<U16*>(ab + img_off(mhi, L.gdst, L.edst)) = (uint16_t)hi;
-  *reinterpret_cast<U16*>(ab + img_off(mlo, L.gdst, L.edst)) = (uint16_t)lo;
+  *reinterpret_cast<U16*>(ab + img_off_r<AR>(mhi, L.gdst, L.edst)) = (uint16_t)hi;
+  *reinterpret_cast<U16*>(ab + img_off_r<AR>(mlo, L.gdst, L.edst)) = (uint16_t)lo;
   if (std::is_same<Ptr, uint8_t*>::value || L.sub == 0) {
     // into LDS every lane of the row writes its block's scale bytes (the same
     // value to the same byte): no branch, so the conversions of successive
     // tokens stay in one block that the compiler can interleave
-    ab[2048 + mhi * 4 + L.kb] = (uint8_t)(E + 127);
-    ab[2048 + mlo * 4 + L.kb] = (uint8_t)(E + 127 - 4);
+    ab[img_scales<AR>(mhi, L.kb)] = (uint8_t)(E + 127);
+    ab[img_scales<AR>(mlo, L.kb)] = (uint8_t)(E + 127 - 4);
   }
   // quantised value of t (A / class factor), summed over the three {0, beta} classes
   return ((H[0] + H[1]) + (Lq[0] + Lq[1])) * L.finv;
@@ -231,7 +244,7 @@ __device__ inline float convert_pair(const ConvLane& L, float t0, float t1, int 
 // Reads lane (mr, gr)'s A operand and scale from an A image (LDS or global).
 // Rows past the real tokens hold stale values: MFMA rows are independent and
 // those rows of the result are never read.
-template <bool HL = false, class Ptr>
+template <bool HL = false, int AR = 16, class Ptr>
 __device__ inline void load_a(Ptr ab, int mr, int gr, v8i& a, int& sc) {
   constexpr bool kLds = std::is_same<Ptr, const uint8_t*>::value || std::is_same<Ptr, uint8_t*>::value;
   if constexpr (HL && !kLds) {
@@ -243,10 +256,10 @@ __device__ inline void load_a(Ptr ab, int mr, int gr, v8i& a, int& sc) {
     sc = ld_h<true>(ab + 2048 + mr * 4 + gr);
   } else {
     using V4 = typename std::conditional<kLds, const v4i, const LB_GLOBAL v4i>::type;
-    const v4i lo = *reinterpret_cast<V4*>(ab + img_off(mr, gr, 0));
-    const v4i hi = *reinterpret_cast<V4*>(ab + img_off(mr, gr, 16));
+    const v4i lo = *reinterpret_cast<V4*>(ab + img_off_r<AR>(mr, gr, 0));
+    const v4i hi = *reinterpret_cast<V4*>(ab + img_off_r<AR>(mr, gr, 16));
     a = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    sc = ab[2048 + mr * 4 + gr];
+    sc = ab[img_scales<AR>(mr, gr)];
   }
 }
 
@@ -319,12 +332,16 @@ struct VShape {
   static constexpr int CT = decode_v_tiles(TM);   // most column tiles of an item
   static constexpr int SMAX = (CT + 3) / 4;       // sign steps per chunk (4 tiles each)
   static constexpr int XS = (TM + 4) / 4;         // steps per chunk holding g and TM rows of x (256 B each)
-  // ring slots per wave: 7 at one token, where four workgroups then fit a CU
-  // (36 KB of LDS and at most 128 VGPRs each), else kRing
-  static constexpr int RING = TM == 1 ? 7 : kRing;
+  // rows of a wave's A image: at one token only its hi and lo rows (272 bytes
+  // instead of 2112)
+  static constexpr int AR = TM == 1 ? 2 : 16;
+  static constexpr int AB = img_bytes<AR>();
+  // ring slots per wave: 9 at one token, where four workgroups then fit a CU
+  // (37 KB of LDS and at most 128 VGPRs each), else kRing
+  static constexpr int RING = TM == 1 ? 9 : kRing;
   static constexpr int RINGB = RING * 1024;
   static constexpr int WPC = TM == 1 ? 4 : TM >= 16 ? 2 : 3;   // workgroups per CU
-  static constexpr size_t lds = (size_t)kWaves * RINGB + (size_t)kWaves * TB * kABytes;
+  static constexpr size_t lds = (size_t)kWaves * RINGB + (size_t)kWaves * TB * AB;
   static_assert(WPC * lds <= 160 * 1024, "workgroups per CU fit its LDS");
 };
 
@@ -454,7 +471,7 @@ __device__ __attribute__((always_inline)) inline void v_stream(const DecArgs& a,
             // registers than two workgroups per CU leave: it keeps the test)
             if (t < TM && (TM <= 8 || t < T)) {
               const float x0 = bf16f((uint16_t)(xpair[g][t] & 0xffff)), x1 = bf16f((uint16_t)(xpair[g][t] >> 16));
-              cpart[t] += convert_pair(L, v0 ? x0 * g0 : 0.f, v1 ? x1 * g1 : 0.f, tt, abuf + tb * kABytes);
+              cpart[t] += convert_pair<S::AR>(L, v0 ? x0 * g0 : 0.f, v1 ? x1 * g1 : 0.f, tt, abuf + tb * S::AB);
             }
           }
         }
@@ -462,7 +479,7 @@ __device__ __attribute__((always_inline)) inline void v_stream(const DecArgs& a,
         v8i A[TB];
         int sc[TB];
 #pragma unroll
-        for (int tb = 0; tb < TB; ++tb) load_a(abuf + tb * kABytes, mr, gr, A[tb], sc[tb]);
+        for (int tb = 0; tb < TB; ++tb) load_a<false, S::AR>(abuf + tb * S::AB, mr, gr, A[tb], sc[tb]);
         wave_lds_fence();
 #pragma unroll
         for (int j = 0; j < S::SMAX; ++j) {
@@ -515,7 +532,7 @@ __device__ __attribute__((always_inline)) inline void v_plain(const DecArgs& a, 
         if (t < TM && t < T) {
           const float x0 = v0 ? bf16f(x[(int64_t)t * n + k0]) : 0.f;
           const float x1 = v1 ? bf16f(x[(int64_t)t * n + k0 + 1]) : 0.f;
-          cpart[t] += convert_pair(L, x0 * g0, x1 * g1, tt, abuf + tb * kABytes);
+          cpart[t] += convert_pair<S::AR>(L, x0 * g0, x1 * g1, tt, abuf + tb * S::AB);
         }
       }
     }
@@ -523,7 +540,7 @@ __device__ __attribute__((always_inline)) inline void v_plain(const DecArgs& a, 
     v8i A[TB];
     int sc[TB];
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb) load_a(abuf + tb * kABytes, mr, gr, A[tb], sc[tb]);
+    for (int tb = 0; tb < TB; ++tb) load_a<false, S::AR>(abuf + tb * S::AB, mr, gr, A[tb], sc[tb]);
     wave_lds_fence();
 #pragma unroll
     for (int i = 0; i < S::CT; ++i) {
@@ -555,7 +572,7 @@ __device__ __attribute__((always_inline)) inline void v_item(const DecArgs& a, c
   const void* xv = a.xs ? cp(a.xs)[it.entry] : a.x0;
   const LB_GLOBAL uint8_t* xb = reinterpret_cast<const LB_GLOBAL uint8_t*>(gp(xv)) + (int64_t)a.t0 * n * 2;
   uint8_t* ring = lds + wave * S::RINGB;
-  uint8_t* abuf = lds + kWaves * S::RINGB + wave * TB * kABytes;
+  uint8_t* abuf = lds + kWaves * S::RINGB + wave * TB * S::AB;
   // this wave's chunks: a contiguous quarter of the item's, the quarters as
   // even as whole groups of chunks allow (groups of two at one token)
   constexpr int GV = TM == 1 ? 2 : 1;
