@@ -332,13 +332,14 @@ struct VShape {
   static constexpr int CT = decode_v_tiles(TM);   // most column tiles of an item
   static constexpr int SMAX = (CT + 3) / 4;       // sign steps per chunk (4 tiles each)
   static constexpr int XS = (TM + 4) / 4;         // steps per chunk holding g and TM rows of x (256 B each)
-  // rows of a wave's A image: at one token only its hi and lo rows (272 bytes
-  // instead of 2112)
-  static constexpr int AR = TM == 1 ? 2 : 16;
+  // rows of a wave's A image: at one and two tokens only their hi and lo rows
+  // (272 and 528 bytes instead of 2112)
+  static constexpr int AR = TM <= 2 ? 2 * TM : 16;
   static constexpr int AB = img_bytes<AR>();
   // ring slots per wave: 9 at one token, where four workgroups then fit a CU
-  // (37 KB of LDS and at most 128 VGPRs each), else kRing
-  static constexpr int RING = TM == 1 ? 9 : kRing;
+  // (37 KB of LDS and at most 128 VGPRs each), 11 at two (the LDS the smaller
+  // image leaves; from 4 tokens a deeper ring measured no faster), else kRing
+  static constexpr int RING = TM == 1 ? 9 : TM == 2 ? 11 : kRing;
   static constexpr int RINGB = RING * 1024;
   static constexpr int WPC = TM == 1 ? 4 : TM >= 16 ? 2 : 3;   // workgroups per CU
   static constexpr size_t lds = (size_t)kWaves * RINGB + (size_t)kWaves * TB * AB;
