@@ -251,6 +251,7 @@ DECODE_SHAPES = [
     (640, 384, [1, 1], 16, 0.0),
     (513, 257, [33, 31], 17, 0.0),       # 17 tokens: two launches of the decode kernel
     (2000, 300, [600], 2, 0.0),          # single path, rank above one column group
+    (1536, 2048, [77, 51], 2, 0.01),     # two tokens with 16-byte x rows (the streamed V form's four-row A image)
     (456, 440, [400, 300], 13, 0.0),     # 7 units at 16-token launches: the wide U launch, ragged quads
     (520, 512, [500, 480], 16, 0.0),     # 8 units: the wide U launch
     (600, 560, [520, 480], 12, 0.0),     # 9 units: the plain U form
