@@ -682,8 +682,9 @@ __device__ __attribute__((always_inline)) inline void mid_item(const DecArgs& a,
   const int ufirst = p ? E.ug.nu0 : 0;
   const int nblk = 4 * ((r + kChunk - 1) / kChunk);
   // 16-lane rows of the workgroup (16 in the chained kernel's 256 threads;
-  // the mid launch has 64 from 4 tokens: with one memory round trip per
-  // position a row takes, more rows mean fewer round trips in a row)
+  // the mid launch has 32 at 4 and 8 tokens and 64 at 16: with one memory
+  // round trip per position a row takes, more rows mean fewer round trips in
+  // a row)
   const int tid = threadIdx.x, row = tid >> 4, sub = tid & 15, nrows = (int)(blockDim.x >> 4);
   for (int u = row; u < T * nblk; u += nrows) {
     const int t = u / nblk, blk = u % nblk, tb = t / 8, tt = t % 8;
@@ -735,9 +736,10 @@ __device__ __attribute__((always_inline)) inline void mid_item(const DecArgs& a,
 }
 
 // Threads of a mid workgroup: 256 up to 2 tokens (a path's positions fit
-// 16 rows), 1024 from 4 tokens.
+// 16 rows), 512 at 4 and 8 tokens (1024 left half the rows of the small k
+// and v paths idle: 8 tokens measured 0.6 % faster), 1024 at 16.
 template <int TM>
-constexpr int mid_threads() { return TM >= 4 ? 1024 : kThreads; }
+constexpr int mid_threads() { return TM >= 16 ? 1024 : TM >= 4 ? 512 : kThreads; }
 
 template <int TM>
 __global__ void __launch_bounds__(mid_threads<TM>()) k_decode_mid(DecArgs a) {
