@@ -338,8 +338,9 @@ struct VShape {
   static constexpr int AB = img_bytes<AR>();
   // ring slots per wave: 9 at one token, where four workgroups then fit a CU
   // (37 KB of LDS and at most 128 VGPRs each), 11 at two (the LDS the smaller
-  // image leaves; from 4 tokens a deeper ring measured no faster), else kRing
-  static constexpr int RING = TM == 1 ? 9 : TM == 2 ? 11 : kRing;
+  // image leaves) and at eight (three workgroups of 53 KB), else kRing (at 4
+  // tokens 11 or 12 measured no faster, at 16 tokens 14 slower)
+  static constexpr int RING = TM == 1 ? 9 : TM == 2 || TM == 8 ? 11 : kRing;
   static constexpr int RINGB = RING * 1024;
   static constexpr int WPC = TM == 1 ? 4 : TM >= 16 ? 2 : 3;   // workgroups per CU
   static constexpr size_t lds = (size_t)kWaves * RINGB + (size_t)kWaves * TB * AB;
